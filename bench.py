@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Throughput of the reranker hot path on one MI355X: scored query-passage pairs/s.
+
+A step is one pass of the whole hot path over one synthetic batch with every
+input already resident in HBM: pair layout, chunk pooling, the cross K/V of
+every layer, the merged-attention decoder stack and the yes/no score.  The
+default workload is the Small-shaped stack (32 queries x 100 passages, 26
+layers, H=1152, 4 query heads / 1 KV head, head dim 256, bf16 storage with fp32
+accumulation).  Every libkalm call of the timed steps is bracketed with HIP
+events on the launch stream, which gives each kernel's average duration and,
+with its algorithmic work, its roofline fraction.  The CPU oracle is timed on a
+bounded seeded sample of the same workload on the host cores.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import contextlib
+import json
+import math
+import os
+import sys
+import time
+from collections import defaultdict
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "scored query-passage pairs/s (1 GPU) + merged-attn MFMA util % / pool HBM GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="small_stack26_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
+    ap.add_argument("--no-pool-long", action="store_true", help="skip the pooling measurement at the 1024x2560 shape")
+    return ap.parse_args()
+
+
+class EventRec:
+    """Records a start/stop HIP event pair on the current stream around each call."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.ev = defaultdict(list)
+        self.on = True
+
+    @contextlib.contextmanager
+    def __call__(self, name):
+        if not self.on:
+            yield
+            return
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        yield
+        e.record()
+        self.ev[name].append((s, e))
+
+    def durations_ms(self):
+        self.torch.cuda.synchronize()
+        return {k: [s.elapsed_time(e) for s, e in v] for k, v in self.ev.items()}
+
+
+def work_model(inp, sh):
+    """Algorithmic work per launch of each kernel (flops or bytes)."""
+    D, T, H, nq, nkv, d = sh.n_docs, sh.T, sh.H, sh.nq, sh.nkv, sh.d
+    lq = np.asarray(inp["lq"], dtype=np.int64)
+    dl = np.asarray(inp["doc_len"], dtype=np.int64)
+    C = -(-dl // sh.chunk)                    # valid chunks per passage (right padding)
+    Cmax = -(-T // sh.chunk)
+    e = 2 if sh.dtype == "bf16" else 4
+    rows = int(D * lq.sum())
+    kv = nkv * d
+    # attention: useful causal-halved flops, sum over pairs
+    self_f = (lq * (lq + 1) // 2).sum() * D
+    cross_f = lq.sum() * C.sum()
+    attn_flops = 4 * nq * d * (self_f + cross_f)
+    attn_bytes = (2 * rows * nq * d + 2 * rows * kv + 2 * int(C.sum()) * kv) * e
+    return {
+        "merged_attn": dict(flops=float(attn_flops), bytes=float(attn_bytes)),
+        "qkv_linear": dict(flops=2.0 * rows * H * (nq * d + 2 * kv),
+                           bytes=float(rows * H * e + rows * (nq * d + 2 * kv) * e)),
+        "o_linear": dict(flops=2.0 * rows * nq * d * H,
+                         bytes=float(rows * nq * d * e + rows * H * 4 * 2 + rows * H * e)),
+        "cross_kv": dict(flops=2.0 * int(C.sum()) * H * 2 * kv, bytes=float(D * Cmax * (H + 2 * kv) * e)),
+        "chunk_pool": dict(flops=0.0, bytes=float(int(dl.sum()) * H * e + D * Cmax * H * e + D * T + D * Cmax + 4 * D)),
+        "gather_rows": dict(flops=0.0, bytes=float(rows * H * (4 + 4 + 2))),
+    }
+
+
+def cpu_baseline(inp, sh, budget_s):
+    import threadpoolctl
+    import oracle
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] or [1])
+    rng = np.random.default_rng(0)
+    order = rng.permutation(sh.pairs)
+    done = 0
+    t0 = time.perf_counter()
+    for p in order:
+        oracle.stack_scores(inp, pairs=[int(p)], mode="mirror")
+        done += 1
+        if time.perf_counter() - t0 >= budget_s and done >= 2:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "pairs/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} seeded-random pairs of the same workload, all {sh.n_layers} layers each, "
+                      f"pooling + cross K/V per pair, fp64 numpy (mirror mode), {el:.1f} s",
+            "blas": ";".join(sorted({f"{i.get('internal_api')}:{i.get('num_threads')}" for i in info}))}
+
+
+def pool_long(torch, ops, reps=20):
+    """Pooling at the 100 x 1024-token x 2560 shape (every chunk full)."""
+    D, T, H = 100, 1024, 2560
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    x = torch.randn(D, T, H, device="cuda", dtype=torch.bfloat16, generator=g)
+    m = torch.ones(D, T, dtype=torch.uint8, device="cuda")
+    C = T // 4
+    out = (torch.empty(D, C, H, dtype=torch.bfloat16, device="cuda"),
+           torch.empty(D, C, dtype=torch.uint8, device="cuda"), torch.empty(D, dtype=torch.int32, device="cuda"))
+    for _ in range(3):
+        ops.kalm_chunk_pool(x, m, 4, out=out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for s, e in ev:
+        s.record()
+        ops.kalm_chunk_pool(x, m, 4, out=out)
+        e.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    by = D * T * H * 2 + D * C * H * 2 + D * T + D * C + 4 * D
+    del x, out
+    return {"shape": "100 x 1024 tokens x 2560 bf16, chunk 4", "avg_us": ms * 1e3,
+            "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": by}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its own "
+              "passage shard independently); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from encoder_decoder_document_amd import ops, stack, synth
+
+    names = [s.name for s in synth.SHAPES]
+    if a.workload not in names:
+        sys.exit(f"unknown workload {a.workload}; one of {names}")
+    idx = names.index(a.workload)
+    sh = synth.SHAPES[idx]
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU (libkalm has no CPU fallback)")
+    if ops.device_check() != ops.KALM_OK:
+        sys.exit(ops.load().kalm_last_error().decode())
+    print(f"[bench] generating {sh.name}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(idx, nan_padding=False)
+    b = stack.upload(inp)
+    torch.cuda.synchronize()
+    print(f"[bench] uploaded: rows={b.rows} pairs={b.P}; warmup {a.warmup}", file=sys.stderr, flush=True)
+    rec = EventRec(torch)
+    rec.on = False
+    for _ in range(a.warmup):
+        stack.step(b, rec=rec)
+    torch.cuda.synchronize()
+    rec.on = True
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        stack.step(b, rec=rec)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_step = el / a.steps * 1e3
+    pairs_s = sh.pairs / (el / a.steps)
+    print(f"[bench] {a.steps} steps: {ms_step:.2f} ms/step, {pairs_s:.1f} pairs/s", file=sys.stderr, flush=True)
+
+    dur = rec.durations_ms()
+    work = work_model(inp, sh)
+    kernels = {}
+    for k, v in dur.items():
+        n_per = len(v) / a.steps
+        avg_us = float(np.mean(v)) * 1e3
+        ent = {"launches_per_step": n_per, "avg_us": avg_us, "total_ms_per_step": float(np.sum(v)) / a.steps}
+        if k in work:
+            w = work[k]
+            if w["flops"] > 0:
+                ent["tflops"] = w["flops"] / (avg_us * 1e-6) / 1e12
+                ent["mfma_frac"] = ent["tflops"] / (PEAK_BF16_TFLOPS if sh.dtype == "bf16" else PEAK_F32_TFLOPS)
+            ent["gbs"] = w["bytes"] / (avg_us * 1e-6) / 1e9
+            ent["hbm_frac"] = ent["gbs"] / PEAK_HBM_GBS
+        kernels[k] = ent
+    dom = max((k for k in kernels if k in work), key=lambda k: kernels[k]["total_ms_per_step"])
+    w = work[dom]
+    if w["flops"] > 0:
+        peak = PEAK_BF16_TFLOPS if sh.dtype == "bf16" else PEAK_F32_TFLOPS
+        roof = {"kernel": dom, "bound": "mfma", "achieved": kernels[dom]["tflops"], "peak": peak,
+                "unit": "TFLOP/s", "frac": kernels[dom]["tflops"] / peak, "traffic": None,
+                "algorithmic_per_launch": w["flops"]}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": kernels[dom]["gbs"] / PEAK_HBM_GBS, "traffic": None, "algorithmic_per_launch": w["bytes"]}
+    out = {
+        "metric": METRIC, "value": pairs_s, "unit": "pairs/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if sh.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) encoder states and first hidden states, N(0,0.02) weights)",
+        "config": {"workload": sh.name, "queries": sh.n_queries, "docs": sh.n_docs, "pairs": sh.pairs,
+                   "layers": sh.n_layers, "hidden": sh.H, "q_heads": sh.nq, "kv_heads": sh.nkv, "head_dim": sh.d,
+                   "decoder_len": list(sh.lq), "passage_len": list(sh.doc_len), "chunk": sh.chunk,
+                   "decoder_rows": b.rows, "parallelism": "single GPU"},
+        "roofline": roof,
+        "merged_attn": {k: kernels["merged_attn"].get(k) for k in ("avg_us", "tflops", "mfma_frac", "gbs", "hbm_frac")},
+        "kernels": kernels,
+    }
+    if not a.no_pool_long:
+        out["pool_long"] = pool_long(torch, ops)
+    del b
+    torch.cuda.empty_cache()
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, sh, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+// C ABI entry points of libkalm: host-side argument validation and dispatch.
+// Every check runs before anything is enqueued; there is no CPU fallback.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "kalm_common.h"
+
+namespace kalm {
+
+static thread_local char g_err[512];
+
+kalm_status set_error(kalm_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kalm_status check_device() {
+  static std::atomic<int> ok{0};  // 1 = a gfx950 device was found once
+  if (ok.load(std::memory_order_relaxed)) return KALM_OK;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return set_error(KALM_ERR_NO_DEVICE, "no HIP device visible (libkalm never falls back to the CPU)");
+  }
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return set_error(KALM_ERR_NO_DEVICE, "cannot query the current HIP device");
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return set_error(KALM_ERR_NO_DEVICE, "device %d is %s; libkalm is built for gfx950 only", dev,
+                     prop.gcnArchName);
+  ok.store(1, std::memory_order_relaxed);
+  return KALM_OK;
+}
+
+kalm_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(KALM_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return KALM_OK;
+}
+
+}  // namespace kalm
+
+#define ALIGNED16(p) ((((uintptr_t)(p)) & 15u) == 0)
+
+extern "C" {
+
+int32_t kalm_version(void) { return 100; }
+
+const char* kalm_last_error(void) { return kalm::g_err; }
+
+kalm_status kalm_device_check(void) { return kalm::check_device(); }
+
+kalm_status kalm_pair_layout(const int32_t* lq, int32_t n_queries, int32_t n_docs, int32_t* cu_q,
+                             int32_t* doc_of_pair, int32_t* final_row, int32_t* h0_row, int64_t rows,
+                             void* stream) {
+  kalm::g_err[0] = 0;
+  KALM_REQUIRE(n_queries >= 0 && n_docs >= 0, KALM_ERR_INVALID_ARG, "kalm_pair_layout: negative sizes");
+  KALM_REQUIRE((int64_t)n_queries * n_docs < (1LL << 31), KALM_ERR_UNSUPPORTED, "kalm_pair_layout: too many pairs");
+  KALM_REQUIRE(cu_q && (n_queries == 0 || (lq && doc_of_pair && final_row)), KALM_ERR_INVALID_ARG,
+               "kalm_pair_layout: null pointer");
+  KALM_REQUIRE(rows >= 0 && rows < (1LL << 31), KALM_ERR_INVALID_ARG, "kalm_pair_layout: rows out of range");
+  KALM_DEVICE_OR_RETURN();
+  kalm::launch_pair_layout(lq, n_queries, n_docs, cu_q, doc_of_pair, final_row, h0_row, rows, (hipStream_t)stream);
+  return kalm::check_launch("kalm_pair_layout");
+}
+
+kalm_status kalm_chunk_pool(const void* x, const uint8_t* token_mask, int32_t D, int32_t T, int32_t H,
+                            int32_t chunk, kalm_dtype dt, void* pooled, uint8_t* chunk_mask,
+                            int32_t* n_chunks, void* stream) {
+  kalm::g_err[0] = 0;
+  KALM_REQUIRE(dt == KALM_F32 || dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "kalm_chunk_pool: dtype %d", (int)dt);
+  KALM_REQUIRE(D >= 0 && T >= 1 && H >= 1, KALM_ERR_INVALID_ARG, "kalm_chunk_pool: bad sizes D=%d T=%d H=%d", D, T, H);
+  KALM_REQUIRE(chunk >= 1 && chunk <= 64, KALM_ERR_INVALID_ARG, "kalm_chunk_pool: chunk=%d not in 1..64", chunk);
+  KALM_REQUIRE(H % (dt == KALM_BF16 ? 8 : 4) == 0, KALM_ERR_UNSUPPORTED, "kalm_chunk_pool: H=%d not a multiple of the 16-byte vector", H);
+  KALM_REQUIRE(D == 0 || (x && token_mask && pooled && chunk_mask && n_chunks), KALM_ERR_INVALID_ARG,
+               "kalm_chunk_pool: null pointer");
+  KALM_REQUIRE(ALIGNED16(x) && ALIGNED16(pooled), KALM_ERR_INVALID_ARG, "kalm_chunk_pool: x/pooled not 16-byte aligned");
+  KALM_DEVICE_OR_RETURN();
+  if (D == 0) return KALM_OK;
+  const int Cmax = (T + chunk - 1) / chunk;
+  kalm::launch_chunk_pool(x, token_mask, D, T, H, chunk, Cmax, dt, pooled, chunk_mask, n_chunks, (hipStream_t)stream);
+  return kalm::check_launch("kalm_chunk_pool");
+}
+
+kalm_status kalm_linear(const void* X, const void* W, int32_t M, int32_t K, int32_t N, kalm_dtype dt,
+                        void* Y, kalm_dtype y_dt, int32_t accumulate, void* Y_bf16, void* stream) {
+  kalm::g_err[0] = 0;
+  KALM_REQUIRE(dt == KALM_F32 || dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "kalm_linear: dtype %d", (int)dt);
+  KALM_REQUIRE(y_dt == KALM_F32 || y_dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "kalm_linear: y dtype %d", (int)y_dt);
+  KALM_REQUIRE(M >= 0 && K >= 1 && N >= 1, KALM_ERR_INVALID_ARG, "kalm_linear: bad sizes M=%d K=%d N=%d", M, K, N);
+  KALM_REQUIRE(M == 0 || (X && W && Y), KALM_ERR_INVALID_ARG, "kalm_linear: null pointer");
+  KALM_REQUIRE(!accumulate || y_dt == KALM_F32, KALM_ERR_UNSUPPORTED, "kalm_linear: accumulate needs an F32 Y");
+  KALM_REQUIRE(!Y_bf16 || y_dt == KALM_F32, KALM_ERR_UNSUPPORTED, "kalm_linear: Y_bf16 copy needs an F32 Y");
+  KALM_REQUIRE(ALIGNED16(X) && ALIGNED16(W) && ALIGNED16(Y) && ALIGNED16(Y_bf16), KALM_ERR_INVALID_ARG,
+               "kalm_linear: pointers must be 16-byte aligned");
+  if (dt == KALM_BF16) {
+    KALM_REQUIRE(K % 8 == 0 && N % 8 == 0, KALM_ERR_UNSUPPORTED, "kalm_linear: bf16 needs K%%8==0 and N%%8==0 (K=%d N=%d)", K, N);
+  } else {
+    KALM_REQUIRE(y_dt == KALM_F32 && !Y_bf16, KALM_ERR_UNSUPPORTED, "kalm_linear: F32 inputs need an F32 Y and no bf16 copy");
+    KALM_REQUIRE(K % 4 == 0 && N % 4 == 0, KALM_ERR_UNSUPPORTED, "kalm_linear: f32 needs K%%4==0 and N%%4==0");
+  }
+  KALM_DEVICE_OR_RETURN();
+  if (M == 0) return KALM_OK;
+  if (dt == KALM_BF16)
+    kalm::launch_linear_bf16((const bf16_t*)X, (const bf16_t*)W, M, K, N, Y, y_dt == KALM_F32, accumulate != 0,
+                             (bf16_t*)Y_bf16, nullptr, (hipStream_t)stream);
+  else
+    kalm::launch_linear_f32((const float*)X, (const float*)W, M, K, N, (float*)Y, accumulate != 0, nullptr,
+                            (hipStream_t)stream);
+  return kalm::check_launch("kalm_linear");
+}
+
+kalm_status kalm_cross_kv(const void* pooled, const uint8_t* chunk_mask, int32_t D, int32_t Cmax, int32_t H,
+                          const void* Wkv, int32_t kv_dim, kalm_dtype dt, void* KVc, void* stream) {
+  kalm::g_err[0] = 0;
+  KALM_REQUIRE(dt == KALM_F32 || dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "kalm_cross_kv: dtype %d", (int)dt);
+  KALM_REQUIRE(D >= 0 && Cmax >= 1 && H >= 1 && kv_dim >= 1, KALM_ERR_INVALID_ARG, "kalm_cross_kv: bad sizes");
+  KALM_REQUIRE((int64_t)D * Cmax < (1LL << 31), KALM_ERR_UNSUPPORTED, "kalm_cross_kv: too many rows");
+  KALM_REQUIRE(D == 0 || (pooled && Wkv && KVc), KALM_ERR_INVALID_ARG, "kalm_cross_kv: null pointer");
+  KALM_REQUIRE(ALIGNED16(pooled) && ALIGNED16(Wkv) && ALIGNED16(KVc), KALM_ERR_INVALID_ARG,
+               "kalm_cross_kv: pointers must be 16-byte aligned");
+  KALM_REQUIRE(H % (dt == KALM_BF16 ? 8 : 4) == 0 && kv_dim % 4 == 0, KALM_ERR_UNSUPPORTED,
+               "kalm_cross_kv: H=%d / kv_dim=%d not aligned to the vector width", H, kv_dim);
+  KALM_DEVICE_OR_RETURN();
+  if (D == 0) return KALM_OK;
+  const int M = D * Cmax, N = 2 * kv_dim;
+  if (dt == KALM_BF16)
+    kalm::launch_linear_bf16((const bf16_t*)pooled, (const bf16_t*)Wkv, M, H, N, KVc, false, false, nullptr,
+                             chunk_mask, (hipStream_t)stream);
+  else
+    kalm::launch_linear_f32((const float*)pooled, (const float*)Wkv, M, H, N, (float*)KVc, false, chunk_mask,
+                            (hipStream_t)stream);
+  return kalm::check_launch("kalm_cross_kv");
+}
+
+kalm_status kalm_merged_attn(const void* Q, int64_t q_ld, const void* Ks, const void* Vs, int64_t kv_ld,
+                             const int32_t* cu_q, int32_t P, int64_t rows, int32_t max_lq, const void* Kc,
+                             const void* Vc, int64_t c_ld, const uint8_t* chunk_mask,
+                             const int32_t* doc_of_pair, int32_t D, int32_t Cmax, int32_t nq, int32_t nkv,
+                             int32_t d, float scale, kalm_dtype dt, void* O, int64_t o_ld, float* lse,
+                             void* stream) {
+  kalm::g_err[0] = 0;
+  KALM_REQUIRE(dt == KALM_F32 || dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "kalm_merged_attn: dtype %d", (int)dt);
+  KALM_REQUIRE(P >= 0 && rows >= 0 && max_lq >= 0 && D >= 0 && Cmax >= 0, KALM_ERR_INVALID_ARG,
+               "kalm_merged_attn: negative sizes");
+  KALM_REQUIRE(nq >= 1 && nkv >= 1 && nq % nkv == 0, KALM_ERR_INVALID_ARG, "kalm_merged_attn: nq=%d nkv=%d", nq, nkv);
+  KALM_REQUIRE(scale > 0.f, KALM_ERR_INVALID_ARG, "kalm_merged_attn: scale must be positive");
+  KALM_REQUIRE(P == 0 || (Q && Ks && Vs && cu_q && O && doc_of_pair), KALM_ERR_INVALID_ARG,
+               "kalm_merged_attn: null pointer");
+  KALM_REQUIRE(Cmax == 0 || D == 0 || (Kc && Vc && chunk_mask), KALM_ERR_INVALID_ARG,
+               "kalm_merged_attn: null cross pointer");
+  KALM_REQUIRE(q_ld >= (int64_t)nq * d && kv_ld >= (int64_t)nkv * d && o_ld >= (int64_t)nq * d &&
+                   (Cmax == 0 || c_ld >= (int64_t)nkv * d),
+               KALM_ERR_INVALID_ARG, "kalm_merged_attn: leading dimension smaller than the heads");
+  if (dt == KALM_BF16) {
+    KALM_REQUIRE(d == 256, KALM_ERR_UNSUPPORTED, "kalm_merged_attn: bf16 path needs head_dim 256 (got %d)", d);
+    const int G = nq / nkv;
+    KALM_REQUIRE(G == 1 || G == 2 || G % 4 == 0, KALM_ERR_UNSUPPORTED,
+                 "kalm_merged_attn: query heads per KV head must be 1, 2 or a multiple of 4 (got %d)", G);
+    KALM_REQUIRE(q_ld % 8 == 0 && kv_ld % 8 == 0 && o_ld % 8 == 0 && c_ld % 8 == 0, KALM_ERR_UNSUPPORTED,
+                 "kalm_merged_attn: bf16 leading dimensions must be multiples of 8");
+    KALM_REQUIRE(ALIGNED16(Q) && ALIGNED16(Ks) && ALIGNED16(Vs) && ALIGNED16(O) && ALIGNED16(Kc) && ALIGNED16(Vc),
+                 KALM_ERR_INVALID_ARG, "kalm_merged_attn: pointers must be 16-byte aligned");
+  } else {
+    KALM_REQUIRE(d >= 1 && d <= 256, KALM_ERR_UNSUPPORTED, "kalm_merged_attn: f32 path needs head_dim <= 256");
+  }
+  KALM_DEVICE_OR_RETURN();
+  if (P == 0 || rows == 0) return KALM_OK;
+  if (dt == KALM_BF16)
+    kalm::launch_merged_attn_bf16((const bf16_t*)Q, q_ld, (const bf16_t*)Ks, (const bf16_t*)Vs, kv_ld, cu_q, P,
+                                  rows, max_lq, (const bf16_t*)Kc, (const bf16_t*)Vc, c_ld, chunk_mask,
+                                  doc_of_pair, D, Cmax, nq, nkv, scale, (bf16_t*)O, o_ld, lse,
+                                  (hipStream_t)stream);
+  else
+    kalm::launch_merged_attn_f32((const float*)Q, q_ld, (const float*)Ks, (const float*)Vs, kv_ld, cu_q, P, rows,
+                                 max_lq, (const float*)Kc, (const float*)Vc, c_ld, chunk_mask, doc_of_pair, D,
+                                 Cmax, nq, nkv, d, scale, (float*)O, o_ld, lse, (hipStream_t)stream);
+  return kalm::check_launch("kalm_merged_attn");
+}
+
+kalm_status kalm_yesno_score(const void* h, kalm_dtype h_dt, int64_t h_ld, int64_t rows, const int32_t* final_row,
+                             int32_t P, int32_t H, const void* w_yesno, kalm_dtype w_dt, float* yes, float* no,
+                             float* margin, float* score, void* stream) {
+  kalm::g_err[0] = 0;
+  KALM_REQUIRE((h_dt == KALM_F32 || h_dt == KALM_BF16) && (w_dt == KALM_F32 || w_dt == KALM_BF16),
+               KALM_ERR_UNSUPPORTED, "kalm_yesno_score: dtype");
+  KALM_REQUIRE(P >= 0 && H >= 1 && h_ld >= H && rows >= 0, KALM_ERR_INVALID_ARG, "kalm_yesno_score: bad sizes");
+  KALM_REQUIRE(P == 0 || (h && final_row && w_yesno && yes && no && score), KALM_ERR_INVALID_ARG,
+               "kalm_yesno_score: null pointer");
+  KALM_DEVICE_OR_RETURN();
+  if (P == 0) return KALM_OK;
+  kalm::launch_yesno(h, h_dt == KALM_BF16, h_ld, rows, final_row, P, H, w_yesno, w_dt == KALM_BF16, yes, no, margin,
+                     score, (hipStream_t)stream);
+  return kalm::check_launch("kalm_yesno_score");
+}
+
+kalm_status kalm_gather_rows(const float* src, const int32_t* idx, int64_t M, int32_t H, int64_t n_src, float* dst,
+                             void* dst_bf16, void* stream) {
+  kalm::g_err[0] = 0;
+  KALM_REQUIRE(M >= 0 && H >= 1 && n_src >= 0, KALM_ERR_INVALID_ARG, "kalm_gather_rows: bad sizes");
+  KALM_REQUIRE(H % 4 == 0, KALM_ERR_UNSUPPORTED, "kalm_gather_rows: H %% 4 != 0");
+  KALM_REQUIRE(M == 0 || (src && idx && dst), KALM_ERR_INVALID_ARG, "kalm_gather_rows: null pointer");
+  KALM_REQUIRE(ALIGNED16(src) && ALIGNED16(dst) && ALIGNED16(dst_bf16), KALM_ERR_INVALID_ARG,
+               "kalm_gather_rows: pointers must be 16-byte aligned");
+  KALM_DEVICE_OR_RETURN();
+  if (M == 0) return KALM_OK;
+  kalm::launch_gather_rows(src, idx, M, H, n_src, dst, (bf16_t*)dst_bf16, (hipStream_t)stream);
+  return kalm::check_launch("kalm_gather_rows");
+}
+
+}  // extern "C"

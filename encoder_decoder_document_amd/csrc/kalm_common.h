@@ -1,0 +1,84 @@
+// Shared device helpers and host-side error plumbing of libkalm (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kalm.h"
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define KALM_WAVE 64
+
+// float -> bf16, round to nearest even (the hardware v_cvt_pk_bf16_f32 path on gfx950).
+__device__ __forceinline__ bf16_t to_bf16(float f) { return (bf16_t)f; }
+__device__ __forceinline__ float from_bf16(bf16_t b) { return (float)b; }
+
+// Pack two floats into one dword of two bf16 (lo = a, hi = b).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16_t x = to_bf16(a), y = to_bf16(b);
+  uint16_t xs = __builtin_bit_cast(uint16_t, x), ys = __builtin_bit_cast(uint16_t, y);
+  return (uint32_t)xs | ((uint32_t)ys << 16);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, KALM_WAVE);
+  return v;
+}
+
+// ---------------------------------------------------------------- host side
+namespace kalm {
+
+kalm_status set_error(kalm_status st, const char* fmt, ...);
+kalm_status check_device();
+kalm_status check_launch(const char* what);
+
+}  // namespace kalm
+
+#define KALM_REQUIRE(cond, status, ...)                     \
+  do {                                                      \
+    if (!(cond)) return ::kalm::set_error(status, __VA_ARGS__); \
+  } while (0)
+
+#define KALM_DEVICE_OR_RETURN()                        \
+  do {                                                 \
+    kalm_status _s = ::kalm::check_device();           \
+    if (_s != KALM_OK) return _s;                      \
+  } while (0)
+
+// Launchers implemented in the kernel translation units.
+namespace kalm {
+void launch_chunk_pool(const void* x, const uint8_t* mask, int D, int T, int H, int chunk, int Cmax,
+                       kalm_dtype dt, void* pooled, uint8_t* cmask, int32_t* n_chunks, hipStream_t s);
+void launch_pair_layout(const int32_t* lq, int nQ, int nD, int32_t* cu_q, int32_t* doc_of_pair,
+                        int32_t* final_row, int32_t* h0_row, int64_t rows, hipStream_t s);
+void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, void* Y, bool y_f32,
+                        bool accumulate, bf16_t* Y_bf16, const uint8_t* row_mask, hipStream_t s);
+void launch_linear_f32(const float* X, const float* W, int M, int K, int N, float* Y, bool accumulate,
+                       const uint8_t* row_mask, hipStream_t s);
+void launch_merged_attn_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, const bf16_t* Vs,
+                             int64_t kv_ld, const int32_t* cu_q, int P, int64_t rows, int max_lq,
+                             const bf16_t* Kc, const bf16_t* Vc, int64_t c_ld, const uint8_t* cmask,
+                             const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv, float scale,
+                             bf16_t* O, int64_t o_ld, float* lse, hipStream_t s);
+void launch_merged_attn_f32(const float* Q, int64_t q_ld, const float* Ks, const float* Vs,
+                            int64_t kv_ld, const int32_t* cu_q, int P, int64_t rows, int max_lq,
+                            const float* Kc, const float* Vc, int64_t c_ld, const uint8_t* cmask,
+                            const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv, int d,
+                            float scale, float* O, int64_t o_ld, float* lse, hipStream_t s);
+void launch_yesno(const void* h, bool h_bf16, int64_t h_ld, int64_t rows, const int32_t* final_row, int P,
+                  int H, const void* w, bool w_bf16, float* yes, float* no, float* margin, float* score,
+                  hipStream_t s);
+void launch_gather_rows(const float* src, const int32_t* idx, int64_t M, int H, int64_t n_src,
+                        float* dst, bf16_t* dst_bf16, hipStream_t s);
+}  // namespace kalm

@@ -1,0 +1,160 @@
+"""Device-resident batch and the end-to-end hot-path step.
+
+``upload`` copies a synthetic batch into HBM once (weights stacked the way the
+kernels read them) and allocates every buffer the step writes, so the step
+itself only enqueues libkalm calls on the current stream:
+
+  kalm_pair_layout -> kalm_chunk_pool -> kalm_cross_kv (one per layer, shared by
+  every query) -> kalm_gather_rows (each pair's residual stream starts from its
+  query's first hidden state) -> per layer: kalm_linear (fused Q/K/V), kalm_merged_attn,
+  kalm_linear (output projection added to the fp32 residual, bf16 copy for the
+  next layer) -> kalm_yesno_score.
+
+The decoder layer is the reading stated on the pages' behalf: the pages give
+only the layer counts ("KaLM-Reranker-V1-Nano -- MLX (Apple Silicon)", What
+this is) and the merged attention; no norm, RoPE or MLP is added.
+"""
+from __future__ import annotations
+
+import contextlib
+import dataclasses
+import math
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+from . import ops
+
+
+@dataclasses.dataclass
+class DeviceBatch:
+    shape: object
+    n_layers: int
+    dtype: torch.dtype
+    D: int
+    T: int
+    H: int
+    nq: int
+    nkv: int
+    d: int
+    chunk: int
+    Cmax: int
+    n_queries: int
+    P: int
+    rows: int
+    max_lq: int
+    # inputs
+    x: torch.Tensor
+    token_mask: torch.Tensor
+    lq: torch.Tensor
+    h0: torch.Tensor
+    Wqkv: List[torch.Tensor]
+    Wkvc: List[torch.Tensor]
+    Wo: List[torch.Tensor]
+    w_yesno: torch.Tensor
+    # buffers written by the step
+    buf: Dict[str, torch.Tensor]
+
+
+def upload(inputs: Dict[str, object], device="cuda", n_layers: Optional[int] = None) -> DeviceBatch:
+    sh = inputs["shape"]
+    dt = torch.bfloat16 if sh.dtype == "bf16" else torch.float32
+    layers = inputs["layers"] if n_layers is None else inputs["layers"][:n_layers]
+    L = len(layers)
+    D, T, H = sh.n_docs, sh.T, sh.H
+    chunk = sh.chunk
+    Cmax = -(-T // chunk)
+    lq = np.asarray(inputs["lq"], dtype=np.int32)
+    P = sh.n_queries * D
+    rows = int(D * lq.sum())
+    kv = sh.nkv * sh.d
+    nqkv = sh.nq * sh.d + 2 * kv
+
+    def dev(a, dtype=dt):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dtype)
+
+    Wqkv = [dev(np.concatenate([W["Wq"], W["Wk"], W["Wv"]], 0)) for W in layers]
+    Wkvc = [dev(np.concatenate([W["Wkc"], W["Wvc"]], 0)) for W in layers]
+    Wo = [dev(W["Wo"]) for W in layers]
+    buf = dict(
+        cu_q=torch.empty(P + 1, dtype=torch.int32, device=device),
+        doc_of_pair=torch.empty(P, dtype=torch.int32, device=device),
+        final_row=torch.empty(P, dtype=torch.int32, device=device),
+        h0_row=torch.empty(rows, dtype=torch.int32, device=device),
+        pooled=torch.empty(D, Cmax, H, dtype=dt, device=device),
+        chunk_mask=torch.empty(D, Cmax, dtype=torch.uint8, device=device),
+        n_chunks=torch.empty(D, dtype=torch.int32, device=device),
+        kvc=torch.empty(L, D, Cmax, 2 * kv, dtype=dt, device=device),
+        h=torch.empty(rows, H, dtype=torch.float32, device=device),
+        qkv=torch.empty(rows, nqkv, dtype=dt, device=device),
+        o=torch.empty(rows, sh.nq * sh.d, dtype=dt, device=device),
+    )
+    if dt == torch.bfloat16:
+        buf["hb"] = torch.empty(rows, H, dtype=torch.bfloat16, device=device)
+    return DeviceBatch(
+        shape=sh, n_layers=L, dtype=dt, D=D, T=T, H=H, nq=sh.nq, nkv=sh.nkv, d=sh.d, chunk=chunk, Cmax=Cmax,
+        n_queries=sh.n_queries, P=P, rows=rows, max_lq=int(lq.max()) if lq.size else 0,
+        x=dev(inputs["x"]), token_mask=dev(inputs["token_mask"], torch.uint8), lq=dev(lq, torch.int32),
+        h0=dev(inputs["h0"], torch.float32), Wqkv=Wqkv, Wkvc=Wkvc, Wo=Wo, w_yesno=dev(inputs["w_yesno"]), buf=buf)
+
+
+def _no_rec(_name):
+    return contextlib.nullcontext()
+
+
+def front(b: DeviceBatch, stream=None, rec=_no_rec):
+    """Rows a0-a2: pair layout, chunk pooling and the cross K/V of every layer.
+    ``rec(name)`` is an optional context-manager factory wrapped around each call
+    (the benchmark records HIP events with it)."""
+    B = b.buf
+    lay = dict(cu_q=B["cu_q"], doc_of_pair=B["doc_of_pair"], final_row=B["final_row"], h0_row=B["h0_row"])
+    _check = ops._check
+    lib = ops.load()
+    s = ops._stream(stream)
+    with rec("pair_layout"):
+        _check("kalm_pair_layout", lib.kalm_pair_layout(
+            ops._ptr(b.lq), b.n_queries, b.D, ops._ptr(lay["cu_q"]), ops._ptr(lay["doc_of_pair"]),
+            ops._ptr(lay["final_row"]), ops._ptr(lay["h0_row"]), b.rows, s))
+    with rec("chunk_pool"):
+        ops.kalm_chunk_pool(b.x, b.token_mask, b.chunk, out=(B["pooled"], B["chunk_mask"], B["n_chunks"]),
+                            stream=stream)
+    for l in range(b.n_layers):
+        with rec("cross_kv"):
+            ops.kalm_cross_kv(B["pooled"], B["chunk_mask"], b.Wkvc[l], out=B["kvc"][l], stream=stream)
+
+
+def decoder(b: DeviceBatch, stream=None, rec=_no_rec):
+    """Row a5 around a3: residual start, then every merged-attention layer."""
+    B = b.buf
+    bf = b.dtype == torch.bfloat16
+    qd, kv = b.nq * b.d, b.nkv * b.d
+    with rec("gather_rows"):
+        ops.kalm_gather_rows(b.h0, B["h0_row"], dst=B["h"], dst_bf16=B["hb"] if bf else None, stream=stream)
+    qkv = B["qkv"]
+    Q, Ks, Vs = qkv[:, :qd], qkv[:, qd:qd + kv], qkv[:, qd + kv:]
+    scale = 1.0 / math.sqrt(b.d)
+    for l in range(b.n_layers):
+        x_in = B["hb"] if bf else B["h"]
+        with rec("qkv_linear"):
+            ops.kalm_linear(x_in, b.Wqkv[l], Y=qkv, stream=stream)
+        kvc = B["kvc"][l].view(b.D * b.Cmax, 2 * kv)
+        with rec("merged_attn"):
+            ops.kalm_merged_attn(Q, Ks, Vs, B["cu_q"], b.max_lq, kvc[:, :kv], kvc[:, kv:], B["chunk_mask"],
+                                 B["doc_of_pair"], b.nq, b.nkv, b.d, scale=scale, out=B["o"], stream=stream)
+        with rec("o_linear"):
+            ops.kalm_linear(B["o"], b.Wo[l], Y=B["h"], accumulate=True, Y_bf16=B["hb"] if bf else None,
+                            stream=stream)
+
+
+def score(b: DeviceBatch, stream=None, rec=_no_rec):
+    """Row a4: yes/no readout at every pair's final row."""
+    with rec("yesno_score"):
+        return ops.kalm_yesno_score(b.buf["h"], b.buf["final_row"], b.w_yesno, stream=stream)
+
+
+def step(b: DeviceBatch, stream=None, rec=_no_rec):
+    """One pass of the whole hot path over the batch; returns (yes, no, margin, score)."""
+    front(b, stream, rec)
+    decoder(b, stream, rec)
+    return score(b, stream, rec)

@@ -42,8 +42,8 @@ class Shape:
     d: int                 # head dim
     n_layers: int
     dtype: str             # "f32" or "bf16"
-    doc_len: tuple         # ("tiny_nonmult4", lo, hi) | ("loguniform", lo, hi) | ("const", n, n)
-    lq: tuple              # ("const", n, n) | ("uniform", lo, hi)
+    doc_len: tuple         # ("tiny_nonmult4", lo, hi) | ("loguniform", lo, hi) | ("const", n, n) | ("list", [..], 0)
+    lq: tuple              # ("const", n, n) | ("uniform", lo, hi) | ("list", [..], 0)
     chunk: int = 4
 
     @property
@@ -63,10 +63,12 @@ SHAPES: List[Shape] = [
 def round_to_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 value (ties to even), returned as float32."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    out = r.astype(np.uint32).view(np.float32).copy()
+    u = a.view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u                      # wraps only for NaN bit patterns, restored below
+    r &= np.uint32(0xFFFF0000)
+    out = r.view(np.float32)
     nan = np.isnan(a)
     if nan.any():
         out[nan] = np.nan
@@ -89,6 +91,8 @@ def _doc_lengths(rng: np.random.Generator, spec: tuple, D: int) -> np.ndarray:
         return np.minimum(hi, np.floor(np.exp(u))).astype(np.int32)
     if kind == "const":
         return np.full(D, lo, dtype=np.int32)
+    if kind == "list":
+        return np.resize(np.asarray(lo, dtype=np.int32), D)
     raise ValueError(kind)
 
 
@@ -98,6 +102,8 @@ def _query_lengths(rng: np.random.Generator, spec: tuple, Q: int) -> np.ndarray:
         return np.full(Q, lo, dtype=np.int32)
     if kind == "uniform":
         return rng.integers(lo, hi + 1, size=Q).astype(np.int32)
+    if kind == "list":
+        return np.resize(np.asarray(lo, dtype=np.int32), Q)
     raise ValueError(kind)
 
 
@@ -152,3 +158,21 @@ def make_inputs(shape_index: int, seed: Optional[int] = None, nan_padding: bool 
     w_yesno = _normal(g_yn, (2, H), 0.02, bf16)
     return dict(shape=sh, seed=seed, doc_len=doc_len, token_mask=token_mask, x=x,
                 lq=lq, h0=h0, layers=layers, w_yesno=w_yesno)
+
+
+def normal(seed: int, shape, std: float = 1.0, bf16: bool = True) -> np.ndarray:
+    """Seeded N(0, std^2) array (float32; bf16-representable when ``bf16``)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _normal(rng, shape, std, bf16)
+
+
+def integers(seed: int, lo: int, hi: int, size) -> np.ndarray:
+    """Seeded uniform integers in [lo, hi] (int32)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(lo, hi + 1, size=size).astype(np.int32)
+
+
+def bernoulli_mask(seed: int, p: float, shape) -> np.ndarray:
+    """Seeded 0/1 uint8 mask with P(1) = p."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (rng.random(shape) < p).astype(np.uint8)

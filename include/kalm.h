@@ -1,0 +1,198 @@
+/*
+ * kalm.h -- C ABI of the KaLM-Reranker-V1 hot-path library (libkalm.so), gfx950.
+ *
+ * The library computes the data-parallel hot path of the "fast but not late
+ * interaction" reranker: chunk pooling of passage encoder states, the cross
+ * K/V projection of the pooled vectors, the merged self+cross attention of
+ * the decoder and the yes/no relevance score, plus the linear layers and row
+ * layout that chain them into a decoder stack.
+ *
+ * Page citations (by page title and section):
+ *   [MLX]  "KaLM-Reranker-V1-Nano -- MLX (Apple Silicon)": What this is, Speed.
+ *   [Q4KM] "KaLM-Reranker-V1-Small Q4_K_M GGUF": Score a pair, Runtime boundaries,
+ *          Troubleshooting.
+ *   [Q80]  "KaLM-Reranker-V1-Large Q8_0 GGUF": Frozen inference contract,
+ *          Score one query-passage pair, Runtime limitations.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or keeps them.  Layouts are row-major and contiguous unless a
+ *    leading dimension (ld, in elements) is given.  Data pointers must be 16-byte
+ *    aligned.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ *    stream).  The caller synchronises.
+ *  - Arguments are validated on the host before anything is launched; a bad
+ *    argument returns KALM_ERR_INVALID_ARG, an unsupported shape or dtype
+ *    KALM_ERR_UNSUPPORTED, a failed launch KALM_ERR_LAUNCH.  kalm_last_error()
+ *    then returns a thread-local message.
+ *  - There is no CPU fallback.  Without a usable GPU every call returns
+ *    KALM_ERR_NO_DEVICE (the same stance as the --require-gpu guard in [Q4KM]
+ *    Troubleshooting and [Q80] Score one query-passage pair).
+ *  - Every output element is written, padded positions included, so results are
+ *    deterministic run to run (no atomics in any reduction).
+ *  - Calls keep no state between them and may be made from several host threads.
+ */
+#ifndef KALM_H
+#define KALM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KALM_OK = 0,
+  KALM_ERR_INVALID_ARG = 1,
+  KALM_ERR_UNSUPPORTED = 2,
+  KALM_ERR_NO_DEVICE = 3,
+  KALM_ERR_LAUNCH = 4
+} kalm_status;
+
+typedef enum { KALM_F32 = 0, KALM_BF16 = 1 } kalm_dtype;
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t kalm_version(void);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* kalm_last_error(void);
+
+/* KALM_OK when a gfx950 device is visible, KALM_ERR_NO_DEVICE otherwise. */
+kalm_status kalm_device_check(void);
+
+/*
+ * a0 -- ragged batch layout.  Every query is paired with every one of n_docs
+ * passages ([MLX] Speed: one document set reranked against many queries);
+ * pair p joins query p / n_docs with doc p % n_docs; its decoder rows are packed
+ * after those of pair p-1, and its score is read at its last row ([MLX] What
+ * this is: the decoder's final position).
+ *
+ *   lq        [n_queries] int32   decoder length of each query, 1..max (device)
+ *   cu_q      [P+1] int32 out     row offsets, cu_q[0] = 0, P = n_queries*n_docs
+ *   doc_of_pair, final_row [P] int32 out
+ *   h0_row    [rows] int32 out, nullable: row of the query's first-layer hidden
+ *             state (queries packed in order) that pair row r starts from
+ *   rows      capacity of h0_row; must equal n_docs * sum(lq) when h0_row is given
+ */
+kalm_status kalm_pair_layout(const int32_t* lq, int32_t n_queries, int32_t n_docs,
+                             int32_t* cu_q, int32_t* doc_of_pair, int32_t* final_row,
+                             int32_t* h0_row, int64_t rows, void* stream);
+
+/*
+ * a1 -- chunk pooling ([Q80] Frozen inference contract: masked mean over
+ * consecutive groups of 4 encoder tokens under right padding; [MLX] What this
+ * is: chunk size 4, masked mean per chunk; [Q4KM] Runtime boundaries: encoder
+ * chunk size 4, at most 1024 tokens).
+ *
+ *   x           [D, T, H] dtype dt (F32 or BF16); padded tokens are never read
+ *   token_mask  [D, T] uint8, nonzero = valid token (any 0/1 pattern is allowed)
+ *   chunk       tokens per chunk, 1..64 (4 in the model)
+ *   pooled      [D, Cmax, H] dtype dt out, Cmax = ceil(T / chunk); chunk c of doc d
+ *               is the mean of the valid tokens among [c*chunk, (c+1)*chunk): fp32
+ *               sum, one IEEE division by the count, one round to dt; a chunk with
+ *               no valid token is written as 0
+ *   chunk_mask  [D, Cmax] uint8 out, 1 iff the chunk has a valid token
+ *   n_chunks    [D] int32 out, number of chunks with chunk_mask = 1
+ * Requires H % 8 == 0 (BF16) or H % 4 == 0 (F32), T >= 1.
+ */
+kalm_status kalm_chunk_pool(const void* x, const uint8_t* token_mask, int32_t D, int32_t T,
+                            int32_t H, int32_t chunk, kalm_dtype dt, void* pooled,
+                            uint8_t* chunk_mask, int32_t* n_chunks, void* stream);
+
+/*
+ * a2 -- cross K/V projection of the cached pooled passage vectors ([MLX] What
+ * this is: cross-attention KV computed over the cached passage encodings).
+ * One bias-free linear map with both projections stacked:
+ *   KVc[r, 0:kv_dim]        = pooled[r] . Wkv[0:kv_dim]^T          (keys)
+ *   KVc[r, kv_dim:2*kv_dim] = pooled[r] . Wkv[kv_dim:2*kv_dim]^T   (values)
+ *
+ *   pooled    [D*Cmax, H] dtype dt
+ *   chunk_mask [D*Cmax] uint8, nullable: rows whose mask byte is 0 are written as
+ *             0 without being computed (padded chunks of right-padded passages)
+ *   Wkv       [2*kv_dim, H] dtype dt ([out, in] layout)
+ *   KVc       [D*Cmax, 2*kv_dim] dtype dt out (fp32 accumulation, one rounding)
+ * Requires H % 8 == 0 and kv_dim % 4 == 0.
+ */
+kalm_status kalm_cross_kv(const void* pooled, const uint8_t* chunk_mask, int32_t D, int32_t Cmax,
+                          int32_t H, const void* Wkv, int32_t kv_dim, kalm_dtype dt, void* KVc,
+                          void* stream);
+
+/*
+ * a3 -- merged self+cross attention ([MLX] What this is: one scaled-dot-product
+ * attention whose KV is the decoder's self KV concatenated with the cross KV of
+ * the cached passage).  For pair p, query head h and pair-local row i:
+ *   o = softmax( [q.k_self_j * scale]_{j<=i}  U  [q.k_cross_c * scale]_{chunk_mask[doc,c]} )
+ *       . [v_self ; v_cross]
+ * in one softmax (single pass, online rescaling across the self/cross boundary).
+ * Query head h reads KV head h / (nq / nkv).
+ *
+ *   Q         [rows, *] dtype dt, row stride q_ld; head h at columns h*d .. h*d+d-1
+ *   Ks, Vs    [rows, *] dtype dt, row stride kv_ld; KV head g at columns g*d ..
+ *   cu_q      [P+1] int32 row offsets (non-decreasing, cu_q[P] <= rows)
+ *   max_lq    >= every pair's length cu_q[p+1]-cu_q[p]; rows of a pair beyond
+ *             max_lq are not computed (the caller's contract)
+ *   Kc, Vc    [D*Cmax, *] dtype dt, row stride c_ld; doc d's chunk c is row d*Cmax+c
+ *   chunk_mask[D, Cmax] uint8; doc_of_pair [P] int32 in [0, D) (a pair with an
+ *             out-of-range doc gets NaN outputs)
+ *   O         [rows, *] dtype dt out, row stride o_ld, same head columns as Q
+ *   lse       [rows, nq] float out, nullable: natural-log log-sum-exp of the
+ *             scaled logits of each row
+ * Requires nq % nkv == 0; BF16: d == 256 (the model's head dim); F32: d <= 256,
+ * d % 32 == 0; ld values multiples of 8.
+ */
+kalm_status kalm_merged_attn(const void* Q, int64_t q_ld, const void* Ks, const void* Vs,
+                             int64_t kv_ld, const int32_t* cu_q, int32_t P, int64_t rows,
+                             int32_t max_lq, const void* Kc, const void* Vc, int64_t c_ld,
+                             const uint8_t* chunk_mask, const int32_t* doc_of_pair, int32_t D,
+                             int32_t Cmax, int32_t nq, int32_t nkv, int32_t d, float scale,
+                             kalm_dtype dt, void* O, int64_t o_ld, float* lse, void* stream);
+
+/*
+ * a4 -- yes/no readout ([MLX] What this is: score = softmax([logit_yes,
+ * logit_no])[yes] at the decoder's final position; [Q4KM] Score a pair and [Q80]
+ * Frozen inference contract: margin = yes - no, score = sigmoid(margin)).
+ *
+ *   h          [rows, H] dtype h_dt (F32 or BF16), row stride h_ld
+ *   final_row  [P] int32 row of each pair's final position (outside [0, rows):
+ *              NaN outputs for that pair)
+ *   w_yesno    [2, H] dtype w_dt: row 0 the "yes" LM-head row, row 1 the "no" row
+ *   yes, no, score [P] float out; margin [P] float out, nullable
+ * score uses the overflow-free logistic form (equal to the two-way softmax).
+ */
+kalm_status kalm_yesno_score(const void* h, kalm_dtype h_dt, int64_t h_ld, int64_t rows,
+                             const int32_t* final_row, int32_t P, int32_t H, const void* w_yesno,
+                             kalm_dtype w_dt, float* yes, float* no, float* margin, float* score,
+                             void* stream);
+
+/*
+ * a5 -- linear layer of the decoder stack glue (the pages give the layer counts,
+ * [MLX] What this is: Nano 18 layers at H=640, Small 26 at H=1152; the layer
+ * internals besides the merged attention are a reading: projections in
+ * [out, in] layout with fp32 accumulation and an fp32 residual).
+ *   Y = X . W^T              (accumulate == 0)
+ *   Y = Y + X . W^T          (accumulate != 0; Y must be F32: the residual stream)
+ *   Y_bf16 = bf16(Y_final)   (optional second output, F32 Y only)
+ *
+ *   X  [M, K] dtype dt;  W [N, K] dtype dt;  Y [M, N] dtype y_dt
+ * dt == BF16: y_dt BF16 or F32, K % 8 == 0, N % 8 == 0.  dt == F32: y_dt F32,
+ * K % 4 == 0, N % 4 == 0.
+ */
+kalm_status kalm_linear(const void* X, const void* W, int32_t M, int32_t K, int32_t N,
+                        kalm_dtype dt, void* Y, kalm_dtype y_dt, int32_t accumulate, void* Y_bf16,
+                        void* stream);
+
+/*
+ * a5 -- row gather that starts the residual stream of every pair from its
+ * query's first-layer hidden state (all passages of a query share it).
+ *   dst[m] = src[idx[m]]   for m < M   (float rows of length H)
+ *   dst_bf16[m] = bf16(dst[m])   (nullable second output)
+ * idx values outside [0, n_src) give NaN rows.  Requires H % 4 == 0.
+ */
+kalm_status kalm_gather_rows(const float* src, const int32_t* idx, int64_t M, int32_t H,
+                             int64_t n_src, float* dst, void* dst_bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KALM_H */

@@ -1,0 +1,90 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute call is made).
+
+The built library must load and export every entry point that include/kalm.h
+declares; argument validation must reject bad calls before any launch; and
+without a GPU every call must report KALM_ERR_NO_DEVICE instead of falling back
+to the CPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kalm.h")
+LIB = os.path.join(ROOT, "encoder_decoder_document_amd", "libkalm.so")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(LIB), reason="libkalm.so not built (run __graft_entry__.build())")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kalm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_hot_path_calls():
+    syms = declared_symbols()
+    for s in ("kalm_chunk_pool", "kalm_cross_kv", "kalm_merged_attn", "kalm_yesno_score", "kalm_linear",
+              "kalm_pair_layout", "kalm_gather_rows", "kalm_last_error", "kalm_version", "kalm_device_check"):
+        assert s in syms
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    missing = [s for s in declared_symbols() if not hasattr(lib, s)]
+    assert not missing, f"not exported: {missing}"
+
+
+@needs_lib
+def test_binding_covers_every_declared_symbol():
+    from encoder_decoder_document_amd import ops
+    assert sorted(ops.EXPORTED) == declared_symbols()
+
+
+@needs_lib
+def test_invalid_arguments_rejected_before_launch():
+    from encoder_decoder_document_amd import ops
+    lib = ops.load()
+    assert lib.kalm_version() == 100
+    # chunk = 0
+    st = lib.kalm_chunk_pool(None, None, 1, 8, 64, 0, ops.KALM_BF16, None, None, None, None)
+    assert st == ops.KALM_ERR_INVALID_ARG and b"chunk" in lib.kalm_last_error()
+    # H not a multiple of the 16-byte vector
+    st = lib.kalm_chunk_pool(None, None, 1, 8, 12, 4, ops.KALM_BF16, None, None, None, None)
+    assert st == ops.KALM_ERR_UNSUPPORTED
+    # unsupported dtype
+    st = lib.kalm_linear(None, None, 4, 8, 8, 7, None, ops.KALM_F32, 0, None, None)
+    assert st == ops.KALM_ERR_UNSUPPORTED
+    # accumulate into a bf16 Y (fake, never dereferenced pointers: validation fails first)
+    st = lib.kalm_linear(16, 32, 4, 8, 8, ops.KALM_BF16, 48, ops.KALM_BF16, 1, None, None)
+    assert st == ops.KALM_ERR_UNSUPPORTED
+    # bf16 attention with a head dim other than 256
+    st = lib.kalm_merged_attn(None, 512, None, None, 128, None, 0, 0, 0, None, None, 128, None, None, 0, 0,
+                              4, 1, 128, 0.1, ops.KALM_BF16, None, 512, None, None)
+    assert st == ops.KALM_ERR_UNSUPPORTED
+    # nq not a multiple of nkv
+    st = lib.kalm_merged_attn(None, 1024, None, None, 768, None, 0, 0, 0, None, None, 768, None, None, 0, 0,
+                              4, 3, 256, 0.1, ops.KALM_BF16, None, 1024, None, None)
+    assert st == ops.KALM_ERR_INVALID_ARG
+    # misaligned pointer
+    st = lib.kalm_gather_rows(8, 16, 4, 8, 4, 16, None, None)
+    assert st == ops.KALM_ERR_INVALID_ARG
+
+
+@needs_lib
+def test_no_device_means_error_not_cpu_fallback():
+    import subprocess
+    import sys
+    code = (
+        "import ctypes,sys; lib=ctypes.CDLL(sys.argv[1]);"
+        "lib.kalm_device_check.restype=ctypes.c_int; lib.kalm_last_error.restype=ctypes.c_char_p;"
+        "s=lib.kalm_device_check(); print(s, lib.kalm_last_error().decode())"
+    )
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1")
+    out = subprocess.run([sys.executable, "-c", code, LIB], capture_output=True, text=True, env=env, timeout=120)
+    status = int(out.stdout.split()[0])
+    assert status == 3, out.stdout + out.stderr   # KALM_ERR_NO_DEVICE
+    assert "no HIP device" in out.stdout or "gfx950" in out.stdout

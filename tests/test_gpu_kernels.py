@@ -1,0 +1,282 @@
+"""GPU parity of each libkalm entry point against the CPU oracle.
+
+Every case feeds the same seeded synthetic inputs (encoder_decoder_document_amd.synth)
+to the HIP path through the C ABI and to the fp64 oracle, then compares
+element by element: integer outputs bit-exact, floating outputs within
+|g - r| <= 2e-2 + 1e-2 |r| (bf16 storage, fp32 accumulation) or 1e-4 + 1e-4 |r|
+(the fp32 path).  Sizes span several tiles and a ragged tail.
+"""
+import math
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from encoder_decoder_document_amd import ops, synth
+from parity_util import BF16_TOL, F32_TOL, assert_close, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+# ------------------------------------------------------------------ a0 layout
+@pytest.mark.parametrize("lq,D", [([16], 8), ([3, 1, 4, 1, 5], 7), ([64] * 3 + [512, 1, 77], 100)])
+def test_pair_layout_bit_exact(lq, D):
+    _announce(f"pair_layout lq={lq} D={D}")
+    lq = np.asarray(lq, np.int32)
+    rows = int(D * lq.sum())
+    got = ops.kalm_pair_layout(to_dev(lq, torch.int32), D, rows=rows)
+    torch.cuda.synchronize()
+    ref = oracle.pair_layout(lq, D)
+    for k in ("cu_q", "doc_of_pair", "final_row", "h0_row"):
+        assert np.array_equal(got[k].cpu().numpy(), ref[k]), k
+
+
+# ------------------------------------------------------------------ a1 pooling
+def _pool_case(seed, D, T, H, chunk, bf16, general_mask=False, lens=None):
+    x = synth.normal(seed, (D, T, H), 1.0, bf16)
+    if general_mask:
+        mask = synth.bernoulli_mask(seed + 1, 0.55, (D, T))
+        mask[0] = 0
+    else:
+        if lens is None:
+            lens = synth.integers(seed + 1, 0, T, D)
+        lens = np.asarray(lens)
+        mask = (np.arange(T)[None] < lens[:, None]).astype(np.uint8)
+    x[mask == 0] = np.nan  # padding must never be read
+    return x, mask
+
+
+@pytest.mark.parametrize("D,T,H,chunk,bf16,general", [
+    (13, 103, 640, 4, True, False),
+    (9, 1024, 1152, 4, True, False),
+    (8, 64, 64, 4, False, False),
+    (11, 97, 640, 1, True, True),
+    (7, 50, 256, 3, True, True),
+    (6, 200, 128, 8, False, True),
+    (5, 130, 640, 64, True, True),
+])
+def test_chunk_pool_parity(D, T, H, chunk, bf16, general):
+    _announce(f"chunk_pool D={D} T={T} H={H} chunk={chunk} bf16={bf16} general={general}")
+    lens = None
+    if not general:
+        lens = synth.integers(7 + D, 0, T, D)
+        lens[:4] = [0, 1, min(T, 5), T]
+    x, mask = _pool_case(100 + D, D, T, H, chunk, bf16, general, lens)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    pooled, cm, nc = ops.kalm_chunk_pool(to_dev(x, dt), to_dev(mask, torch.uint8), chunk)
+    torch.cuda.synchronize()
+    rp, rcm, rnc = oracle.chunk_pool(x, mask, chunk)
+    assert np.array_equal(cm.cpu().numpy(), rcm)
+    assert np.array_equal(nc.cpu().numpy(), rnc)
+    atol, rtol = BF16_TOL if bf16 else F32_TOL
+    assert_close(to_np(pooled), rp, atol, rtol, "pooled")
+    g = to_np(pooled)
+    assert not g[rcm == 0].any(), "empty chunks must be written as 0"
+
+
+def test_chunk_pool_constant_chunks_bit_exact():
+    _announce("chunk_pool constant chunks")
+    D, T, H = 6, 61, 640
+    const = synth.normal(5, (D, -(-T // 4), H), 1.0, True)
+    x = np.repeat(const, 4, axis=1)[:, :T].copy()
+    lens = np.array([61, 60, 59, 1, 0, 33], np.int32)
+    mask = (np.arange(T)[None] < lens[:, None]).astype(np.uint8)
+    x[mask == 0] = np.nan
+    pooled, cm, _ = ops.kalm_chunk_pool(to_dev(x, torch.bfloat16), to_dev(mask, torch.uint8), 4)
+    torch.cuda.synchronize()
+    g = pooled.float().cpu().numpy()
+    c = cm.cpu().numpy() == 1
+    assert np.array_equal(g[c], const[c])
+
+
+# ------------------------------------------------------------------ a2 cross K/V
+@pytest.mark.parametrize("D,C,H,kv,bf16", [(7, 37, 640, 256, True), (3, 256, 1152, 256, True),
+                                           (2, 256, 2560, 1024, True), (5, 29, 640, 72, True),
+                                           (8, 16, 64, 32, False)])
+def test_cross_kv_parity(D, C, H, kv, bf16):
+    _announce(f"cross_kv D={D} C={C} H={H} kv={kv} bf16={bf16}")
+    pooled = synth.normal(20 + D, (D, C, H), 1.0, bf16)
+    cm = synth.bernoulli_mask(21 + D, 0.7, (D, C))
+    cm[0] = 0
+    W = synth.normal(22 + D, (2 * kv, H), 0.02, bf16)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    got = to_np(ops.kalm_cross_kv(to_dev(pooled, dt), to_dev(cm, torch.uint8), to_dev(W, dt)))
+    torch.cuda.synchronize()
+    K, V = oracle.cross_kv(pooled, W[:kv], W[kv:])
+    ref = np.concatenate([K, V], -1) * (cm[..., None] != 0)
+    atol, rtol = BF16_TOL if bf16 else F32_TOL
+    assert_close(got, ref, atol, rtol, "KVc")
+    assert not got[cm == 0].any()
+
+
+# ------------------------------------------------------------------ a5 linear
+@pytest.mark.parametrize("M,K,N,mode", [(1000, 1152, 1536, "bf16"), (300, 1024, 1152, "acc"),
+                                        (77, 200, 136, "f32out"), (513, 640, 1536, "bf16"),
+                                        (130, 64, 96, "f32"), (33, 36, 20, "f32acc")])
+def test_linear_parity(M, K, N, mode):
+    _announce(f"linear M={M} K={K} N={N} mode={mode}")
+    bf = mode in ("bf16", "acc", "f32out")
+    X = synth.normal(30 + M, (M, K), 1.0, bf)
+    W = synth.normal(31 + M, (N, K), 0.02, bf)
+    dt = torch.bfloat16 if bf else torch.float32
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    if mode == "bf16":
+        got = to_np(ops.kalm_linear(to_dev(X, dt), to_dev(W, dt)))
+        assert_close(got, ref, *BF16_TOL, "Y bf16")
+    elif mode in ("acc", "f32acc"):
+        Y0 = synth.normal(32 + M, (M, N), 1.0, False)
+        Y = to_dev(Y0, torch.float32)
+        Yb = torch.empty(M, N, dtype=torch.bfloat16, device="cuda") if mode == "acc" else None
+        ops.kalm_linear(to_dev(X, dt), to_dev(W, dt), Y=Y, accumulate=True, Y_bf16=Yb)
+        torch.cuda.synchronize()
+        tol = (1e-4, 1e-4) if mode == "f32acc" else (1e-3, 1e-4)
+        assert_close(to_np(Y), Y0 + ref, *tol, "Y += XW^T")
+        if Yb is not None:
+            assert torch.equal(Yb.cpu(), Y.cpu().to(torch.bfloat16)), "bf16 copy is RNE of the fp32 result"
+    elif mode == "f32out":
+        got = to_np(ops.kalm_linear(to_dev(X, dt), to_dev(W, dt), y_dtype=torch.float32))
+        assert_close(got, ref, 1e-3, 1e-4, "Y f32")
+    else:
+        got = to_np(ops.kalm_linear(to_dev(X, dt), to_dev(W, dt)))
+        assert_close(got, ref, *F32_TOL, "Y f32 path")
+
+
+# ------------------------------------------------------------------ a3 merged attention
+def _attn_case(seed, lqs, docs_c, Cmax, nq, nkv, d, bf16, std=0.7, general=False):
+    P = len(lqs)
+    D = len(docs_c)
+    rows = int(sum(lqs))
+    Q = synth.normal(seed, (rows, nq * d), std, bf16)
+    Ks = synth.normal(seed + 1, (rows, nkv * d), std, bf16)
+    Vs = synth.normal(seed + 2, (rows, nkv * d), 1.0, bf16)
+    Kc = synth.normal(seed + 3, (D * Cmax, nkv * d), std, bf16)
+    Vc = synth.normal(seed + 4, (D * Cmax, nkv * d), 1.0, bf16)
+    if general:
+        cm = synth.bernoulli_mask(seed + 5, 0.5, (D, Cmax))
+    else:
+        cm = (np.arange(Cmax)[None] < np.asarray(docs_c)[:, None]).astype(np.uint8)
+    # masked chunks hold NaN: they must never be read
+    Kc.reshape(D, Cmax, -1)[cm == 0] = np.nan
+    Vc.reshape(D, Cmax, -1)[cm == 0] = np.nan
+    doc_of_pair = (np.arange(P) % D).astype(np.int32)
+    cu_q = np.concatenate([[0], np.cumsum(lqs)]).astype(np.int32)
+    return Q, Ks, Vs, Kc, Vc, cm, doc_of_pair, cu_q
+
+
+def _attn_ref(Q, Ks, Vs, Kc, Vc, cm, doc_of_pair, cu_q, nq, nkv, d):
+    rows = Q.shape[0]
+    O = np.zeros((rows, nq * d))
+    L = np.zeros((rows, nq))
+    Cmax = cm.shape[1]
+    for p in range(len(doc_of_pair)):
+        a, b = cu_q[p], cu_q[p + 1]
+        dd = doc_of_pair[p]
+        kc = Kc[dd * Cmax:(dd + 1) * Cmax].reshape(Cmax, nkv, d)
+        vc = Vc[dd * Cmax:(dd + 1) * Cmax].reshape(Cmax, nkv, d)
+        o, lse = oracle.merged_attn(Q[a:b].reshape(-1, nq, d), Ks[a:b].reshape(-1, nkv, d),
+                                    Vs[a:b].reshape(-1, nkv, d), kc, vc, cm[dd])
+        O[a:b] = o.reshape(b - a, nq * d)
+        L[a:b] = lse
+    return O, L
+
+
+@pytest.mark.parametrize("name,lqs,docs_c,Cmax,nq,nkv,std,general", [
+    ("g4_ragged", [1, 31, 32, 33, 100, 300], [0, 1, 31, 32, 33, 70], 70, 4, 1, 0.7, False),
+    ("g4_general_mask", [45, 129, 7], [0, 0, 0], 64, 4, 1, 0.7, True),
+    ("g2_gqa", [64, 65, 200, 3], [256, 100, 17, 0], 256, 8, 4, 0.7, False),
+    ("g1", [130, 5, 64], [10, 129, 0], 130, 2, 2, 0.7, False),
+    ("g8", [40, 97], [33, 64], 64, 8, 1, 0.7, False),
+    ("g4_sharp_logits", [150, 80], [90, 40], 96, 4, 1, 3.0, False),
+    ("g4_long", [512], [256], 256, 4, 1, 0.7, False),
+])
+def test_merged_attn_bf16_parity(name, lqs, docs_c, Cmax, nq, nkv, std, general):
+    _announce(f"merged_attn bf16 {name}")
+    d = 256
+    case = _attn_case(zlib.crc32(name.encode()) % 1000 + 50, lqs, docs_c, Cmax, nq, nkv, d, True, std, general)
+    Q, Ks, Vs, Kc, Vc, cm, dop, cu_q = case
+    rows = Q.shape[0]
+    lse = torch.empty(rows, nq, dtype=torch.float32, device="cuda")
+    bf = torch.bfloat16
+    O = ops.kalm_merged_attn(to_dev(Q, bf), to_dev(Ks, bf), to_dev(Vs, bf), to_dev(cu_q, torch.int32), max(lqs),
+                             to_dev(Kc, bf), to_dev(Vc, bf), to_dev(cm, torch.uint8), to_dev(dop, torch.int32),
+                             nq, nkv, d, lse=lse)
+    torch.cuda.synchronize()
+    rO, rL = _attn_ref(*case, nq, nkv, d)
+    assert_close(to_np(O), rO, *BF16_TOL, f"O ({name})")
+    assert_close(to_np(lse), rL, *BF16_TOL, f"lse ({name})")
+
+
+@pytest.mark.parametrize("name,lqs,docs_c,Cmax,nq,nkv,d", [
+    ("tiny", [16] * 8, [2, 16, 5, 9, 1, 16, 12, 7], 16, 2, 1, 32),
+    ("f32_gqa_ragged", [1, 9, 40], [0, 3, 20], 20, 4, 2, 64),
+])
+def test_merged_attn_f32_parity(name, lqs, docs_c, Cmax, nq, nkv, d):
+    _announce(f"merged_attn f32 {name}")
+    case = _attn_case(7, lqs, docs_c, Cmax, nq, nkv, d, False)
+    Q, Ks, Vs, Kc, Vc, cm, dop, cu_q = case
+    rows = Q.shape[0]
+    lse = torch.empty(rows, nq, dtype=torch.float32, device="cuda")
+    f = torch.float32
+    O = ops.kalm_merged_attn(to_dev(Q, f), to_dev(Ks, f), to_dev(Vs, f), to_dev(cu_q, torch.int32), max(lqs),
+                             to_dev(Kc, f), to_dev(Vc, f), to_dev(cm, torch.uint8), to_dev(dop, torch.int32),
+                             nq, nkv, d, lse=lse)
+    torch.cuda.synchronize()
+    rO, rL = _attn_ref(*case, nq, nkv, d)
+    assert_close(to_np(O), rO, *F32_TOL, "O f32")
+    assert_close(to_np(lse), rL, *F32_TOL, "lse f32")
+
+
+def test_merged_attn_bad_doc_gives_nan_rows():
+    _announce("merged_attn out-of-range doc")
+    case = _attn_case(9, [20, 20], [5, 5], 32, 4, 1, 256, True)
+    Q, Ks, Vs, Kc, Vc, cm, dop, cu_q = case
+    dop = np.array([0, 7], np.int32)  # doc 7 does not exist
+    bf = torch.bfloat16
+    O = ops.kalm_merged_attn(to_dev(Q, bf), to_dev(Ks, bf), to_dev(Vs, bf), to_dev(cu_q, torch.int32), 20,
+                             to_dev(Kc, bf), to_dev(Vc, bf), to_dev(cm, torch.uint8), to_dev(dop, torch.int32),
+                             4, 1, 256)
+    g = to_np(O)
+    assert np.isfinite(g[:20]).all() and np.isnan(g[20:]).all()
+
+
+# ------------------------------------------------------------------ a4 score
+@pytest.mark.parametrize("H,hb,wb", [(640, False, True), (1152, True, True), (64, False, False)])
+def test_yesno_score_parity(H, hb, wb):
+    _announce(f"yesno H={H}")
+    rows, P = 300, 57
+    h = synth.normal(40 + H, (rows, H), 1.0, hb)
+    h[:3] *= 32.0  # large margins (a power of two keeps bf16 values exact)
+    w = synth.normal(41 + H, (2, H), 0.02 if H > 64 else 1.0, wb)
+    fr = synth.integers(42, 0, rows - 1, P)
+    fr[:3] = [0, 1, 2]
+    y, n, m, s = ops.kalm_yesno_score(to_dev(h, torch.bfloat16 if hb else torch.float32), to_dev(fr, torch.int32),
+                                      to_dev(w, torch.bfloat16 if wb else torch.float32))
+    torch.cuda.synchronize()
+    ref = oracle.yesno_score(h[fr], w)
+    for got, k in ((y, "yes"), (n, "no"), (m, "margin")):
+        assert_close(to_np(got), ref[k], 1e-4, 1e-4, k)
+    assert_close(to_np(s), ref["score"], 1e-5, 1e-4, "score")
+
+
+# ------------------------------------------------------------------ a5 gather
+def test_gather_rows_exact():
+    _announce("gather_rows")
+    src = synth.normal(50, (37, 1152), 1.0, False)
+    idx = synth.integers(51, 0, 36, 500)
+    idx[7] = 37  # out of range -> NaN row
+    dst_b = torch.empty(500, 1152, dtype=torch.bfloat16, device="cuda")
+    dst = ops.kalm_gather_rows(to_dev(src, torch.float32), to_dev(idx, torch.int32), dst_bf16=dst_b)
+    torch.cuda.synchronize()
+    g = dst.cpu().numpy()
+    ok = np.arange(500) != 7
+    assert np.array_equal(g[ok], src[idx[ok]])
+    assert np.isnan(g[7]).all()
+    assert torch.equal(dst_b.cpu()[torch.from_numpy(ok)], torch.from_numpy(src[idx[ok]]).to(torch.bfloat16))
