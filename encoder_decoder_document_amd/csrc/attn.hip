@@ -38,16 +38,19 @@ constexpr int HD = 256;        // head dim of the bf16 path
 constexpr int BKV = 32;        // keys per tile
 constexpr int VT_LD = BKV + 8; // bf16 per transposed-V row in LDS (80 bytes)
 constexpr float LAZY = 8.0f;   // lazy-rescale threshold, log2 units
+constexpr int MAX_CTILES = 128;  // cross tiles per passage (Cmax <= 4096)
 
 __device__ __forceinline__ int key_of_slot(int v, int g) {  // key a lane's v-th logit belongs to
   return v < 8 ? 8 * g + v : 16 + 8 * g + (v - 8);
 }
-__device__ __forceinline__ int k_swz(int row) {  // LDS chunk swizzle of K row `row`
-  return ((row >> 1) & 4) | (row & 3);
-}
+// Physical 16-byte chunk of logical chunk c (0..31) in K row `key` (512-byte
+// rows).  A ds_read_b128 is served 16 lanes at a time over 64 banks (256 bytes);
+// lanes 0-15 read keys 0-15 (in the bit-2/3 swapped order) at one logical
+// chunk, so XOR with key & 15 spreads them over 16 distinct chunk columns.
+__device__ __forceinline__ int k_swz(int key, int c) { return c ^ (key & 15); }
 
 template <int NH>
-__global__ __launch_bounds__(256, 2) void merged_attn_bf16_kernel(
+__global__ __launch_bounds__(256, 1) void merged_attn_bf16_kernel(
     const bf16_t* __restrict__ Q, int64_t q_ld, const bf16_t* __restrict__ Ks,
     const bf16_t* __restrict__ Vs, int64_t kv_ld, const int32_t* __restrict__ cu_q, int P,
     int64_t rows, int nqb, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
@@ -56,9 +59,12 @@ __global__ __launch_bounds__(256, 2) void merged_attn_bf16_kernel(
     float* __restrict__ lse) {
   constexpr int WPH = 4 / NH;   // waves per head
   constexpr int RB = 32 * WPH;  // decoder rows per block
-  __shared__ __attribute__((aligned(16))) bf16_t k_lds[BKV * HD];
-  __shared__ __attribute__((aligned(16))) bf16_t vt_lds[HD * VT_LD];
-  __shared__ uint8_t cm_lds[BKV];
+  // two ring slots of (K tile [32 keys][256], swizzled) and (V^T tile [256][32+8])
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds[2][BKV * HD];
+  __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2][HD * VT_LD];
+  __shared__ __attribute__((aligned(1024))) bf16_t q_lds[4][32 * HD];  // each wave's 32 query rows (swizzled)
+  __shared__ uint32_t cm_bits[MAX_CTILES];  // valid-chunk bits of each cross tile
+  __shared__ int n_ctiles_s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, g = lane >> 5;
@@ -81,16 +87,45 @@ __global__ __launch_bounds__(256, 2) void merged_attn_bf16_kernel(
   const int doc = doc_of_pair[p];
   const bool bad_doc = doc < 0 || doc >= D;
 
-  const int h = kvh * G + hg * NH + wave / WPH;
-  const int i_loc = qb * RB + (wave % WPH) * 32 + r;  // this lane's decoder row (pair-local)
-  const int i_ld = min(i_loc, Lq - 1);
-  const int wave_last = min(qb * RB + (wave % WPH) * 32 + 31, Lq - 1);
+  // cross-tile validity bits; tiles past the last valid chunk are dropped
+  const int n_ct_all = bad_doc ? 0 : (Cmax + BKV - 1) / BKV;
+  if (tid < BKV) {
+    const uint8_t* cmd = cmask + (int64_t)(bad_doc ? 0 : doc) * Cmax;
+    for (int ct = 0; ct < n_ct_all; ++ct) {
+      const int c = ct * BKV + tid;
+      const bool v = c < Cmax && cmd[c] != 0;
+      const uint64_t bits = __ballot(v);
+      if (tid == 0) cm_bits[ct] = (uint32_t)bits;
+    }
+    if (tid == 0) {
+      int last = 0;
+      for (int ct = 0; ct < n_ct_all; ++ct)
+        if (cm_bits[ct]) last = ct + 1;
+      n_ctiles_s = last;
+    }
+  }
+  __syncthreads();
+  const int n_ct = n_ctiles_s;
 
-  bf16x8_t qf[HD / 16];
+  const int h = kvh * G + hg * NH + wave / WPH;
+  const int qr0 = qb * RB + (wave % WPH) * 32;  // first decoder row of this wave
+  const int i_loc = qr0 + r;                     // this lane's decoder row (pair-local)
+  const int i_ld = min(i_loc, Lq - 1);
+  const int wave_last = min(qr0 + 31, Lq - 1);
+
+  // this wave's 32 query rows -> LDS by DMA (16 instructions of 2 rows x 512 bytes);
+  // lane l writes physical chunk l & 31 of row 2j + (l >> 5); chunks XOR-swizzled
+  // with row & 15 like K, so the B-operand reads of 16 rows are conflict free
   {
-    const bf16_t* qp = Q + (row0 + i_ld) * q_ld + (int64_t)h * HD + 8 * g;
+    const uint64_t qbase = uniform64((uint64_t)(uintptr_t)(Q + row0 * q_ld + (int64_t)h * HD));
+    const uint32_t qlds = __builtin_amdgcn_readfirstlane(lds_addr(&q_lds[wave][0]));
+    const uint32_t q_ld2 = (uint32_t)q_ld * 2u;
 #pragma unroll
-    for (int s = 0; s < HD / 16; ++s) qf[s] = *(const bf16x8_t*)(qp + 16 * s);
+    for (int j = 0; j < 16; ++j) {
+      const int qrow = 2 * j + (lane >> 5);
+      const int src_row = min(qr0 + qrow, Lq - 1);
+      dma16(qbase, (uint32_t)src_row * q_ld2 + (uint32_t)(k_swz(qrow, lane & 31) * 16), qlds + j * 1024);
+    }
   }
 
   f32x16_t oacc[HD / 32];
@@ -100,60 +135,129 @@ __global__ __launch_bounds__(256, 2) void merged_attn_bf16_kernel(
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  // stage one 32-key tile of K (row-major, swizzled) and V (transposed) in LDS.
-  // Rows whose `ok` test fails are zero-filled and never read from memory.
-  auto stage = [&](const bf16_t* kbase, const bf16_t* vbase, int64_t ld, auto row_ok) {
-    // K: 1024 16-byte chunks, 4 per thread
+  const int n_self = min(Lq, qb * RB + RB);  // causal keys the block needs
+  const int n_st = (n_self + BKV - 1) / BKV;
+  const int n_tiles = n_st + n_ct;
+  // byte addresses of key 0 of this pair (self) / chunk 0 of this passage (cross), head kvh
+  const uint64_t ks_base = (uint64_t)(uintptr_t)(Ks + row0 * kv_ld + (int64_t)kvh * HD);
+  const uint64_t vs_base = (uint64_t)(uintptr_t)(Vs + row0 * kv_ld + (int64_t)kvh * HD);
+  const int64_t cdoc = (int64_t)(bad_doc ? 0 : doc) * Cmax * c_ld + (int64_t)kvh * HD;
+  const uint64_t kc_base = (uint64_t)(uintptr_t)(Kc + cdoc);
+  const uint64_t vc_base = (uint64_t)(uintptr_t)(Vc + cdoc);
+  const uint32_t klds0 = __builtin_amdgcn_readfirstlane(lds_addr(&k_lds[0][0]));
+  const uint32_t kv_ld2 = (uint32_t)kv_ld * 2u, c_ld2 = (uint32_t)c_ld * 2u;
+
+  // Per-lane pieces of the copy addresses, fixed for the whole block.
+  // K (LDS DMA): wave instruction j fills key rows kj, kj+1 (1 KB); lane l writes
+  // physical chunk l & 31 of key row kj + (l >> 5).
+  int kkey[4], klc16[4];
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int c = tid + 256 * pass;
-      const int key = c >> 5, dc = c & 31;
-      u32x4_t v = {0, 0, 0, 0};
-      if (row_ok(key)) v = *(const u32x4_t*)(kbase + key * ld + dc * 8);
-      *(u32x4_t*)(k_lds + key * HD + ((dc ^ k_swz(key)) << 3)) = v;
+  for (int j = 0; j < 4; ++j) {
+    kkey[j] = 2 * (wave * 4 + j) + (lane >> 5);
+    klc16[j] = k_swz(kkey[j], lane & 31) * 16;
+  }
+  const uint32_t kslab = __builtin_amdgcn_readfirstlane(wave * 4 * 1024);
+  // V (registers): thread holds keys 4*vkg .. 4*vkg+3, dims 8*vdc .. 8*vdc+7
+  const int vkg = tid & 7, vdc = tid >> 3;
+
+  auto tile_src = [&](int v, uint64_t& kb_addr, uint64_t& vb_addr, uint32_t& ld2, int& lim, int& kb) {
+    const bool self = v < n_st;
+    kb = self ? v * BKV : (v - n_st) * BKV;
+    ld2 = self ? kv_ld2 : c_ld2;
+    lim = self ? Lq : Cmax;  // key rows at or past it are clamped
+    kb_addr = (self ? ks_base : kc_base) + (uint64_t)kb * ld2;
+    vb_addr = (self ? vs_base : vc_base) + (uint64_t)kb * ld2;
+  };
+
+  u32x4_t vr[4];
+  // issue the copies of tile v: K straight to LDS slot v & 1, V into registers
+  auto fetch = [&](int v) {
+    uint64_t kba, vba;
+    uint32_t ld2;
+    int lim, kb;
+    tile_src(v, kba, vba, ld2, lim, kb);
+    const int nrow = lim - kb;  // rows of this tile that exist (>= 1)
+    const uint32_t slot = klds0 + (uint32_t)((v & 1) * BKV * HD * 2) + kslab;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = min(kkey[j], nrow - 1);
+      dma16(kba, (uint32_t)row * ld2 + klc16[j], slot + j * 1024);
     }
-    // V: thread holds 4 consecutive keys x 8 dims, writes 8 dims x 4 keys
-    const int kg = tid & 7, dc = tid >> 3;
-    u32x4_t vr[4];
+    const uint8_t* vb = (const uint8_t*)(uintptr_t)vba;
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      const int key = 4 * kg + pp;
-      vr[pp] = u32x4_t{0, 0, 0, 0};
-      if (row_ok(key)) vr[pp] = *(const u32x4_t*)(vbase + key * ld + dc * 8);
+      const int row = min(4 * vkg + pp, nrow - 1);
+      vr[pp] = *(const u32x4_t*)(vb + ((uint32_t)row * ld2 + vdc * 16));
     }
+  };
+  // zero the V rows of keys that do not exist or are masked, then write V^T
+  auto store_vt = [&](int v) {
+    const bool self = v < n_st;
+    const int kb = self ? v * BKV : (v - n_st) * BKV;
+    const uint32_t valid = self ? (Lq - kb >= BKV ? 0xffffffffu : ((1u << (Lq - kb)) - 1u)) : cm_bits[v - n_st];
+    if (valid != 0xffffffffu) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sh = (e & 1) * 16;
-      const uint32_t a0 = (vr[0][e >> 1] >> sh) & 0xffffu, a1 = (vr[1][e >> 1] >> sh) & 0xffffu;
-      const uint32_t a2 = (vr[2][e >> 1] >> sh) & 0xffffu, a3 = (vr[3][e >> 1] >> sh) & 0xffffu;
-      *(u32x2_t*)(vt_lds + (dc * 8 + e) * VT_LD + 4 * kg) = u32x2_t{a0 | (a1 << 16), a2 | (a3 << 16)};
+      for (int pp = 0; pp < 4; ++pp)
+        if (!((valid >> (4 * vkg + pp)) & 1u)) vr[pp] = u32x4_t{0, 0, 0, 0};
+    }
+    bf16_t* vt = &vt_lds[v & 1][0] + (vdc * 8) * VT_LD + 4 * vkg;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {  // dims 2m (low halves) and 2m+1 (high halves)
+      const uint32_t lo01 = __builtin_amdgcn_perm(vr[1][m], vr[0][m], 0x05040100u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(vr[3][m], vr[2][m], 0x05040100u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(vr[1][m], vr[0][m], 0x07060302u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(vr[3][m], vr[2][m], 0x07060302u);
+      *(u32x2_t*)(vt + (2 * m) * VT_LD) = u32x2_t{lo01, lo23};
+      *(u32x2_t*)(vt + (2 * m + 1) * VT_LD) = u32x2_t{hi01, hi23};
     }
   };
 
-  // consume the staged tile: kbase = index of the tile's first key
-  auto consume = [&](int kbase, bool is_self) {
+  const int krow = (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1);  // swap bits 2 and 3
+  const bf16_t* kfrag0 = &k_lds[0][0] + krow * HD;
+  const bf16_t* qfrag = &q_lds[wave][0] + r * HD;
+  const bf16_t* vfrag0 = &vt_lds[0][0] + r * VT_LD + 8 * g;
+  // consume tile v from ring slot v & 1
+  auto consume = [&](int v) {
+    const bool self = v < n_st;
+    const int kb = self ? v * BKV : (v - n_st) * BKV;
+    const bf16_t* kt = kfrag0 + (v & 1) * (BKV * HD);
+    const bf16_t* vt = vfrag0 + (v & 1) * (HD * VT_LD);
     f32x16_t sacc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
-    const int krow = (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1);  // swap bits 2 and 3
 #pragma unroll
     for (int s = 0; s < HD / 16; ++s) {
-      const int kc = 2 * s + g;
-      const bf16x8_t kf = *(const bf16x8_t*)(k_lds + krow * HD + ((kc ^ k_swz(krow)) << 3));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
+      const bf16x8_t kf = *(const bf16x8_t*)(kt + (k_swz(krow, 2 * s + g) << 3));
+      const bf16x8_t qf = *(const bf16x8_t*)(qfrag + (k_swz(r, 2 * s + g) << 3));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf, sacc, 0, 0, 0);
     }
-    float tmax = -INFINITY;
+    // masking only for the causal diagonal / ragged self tiles and partial cross tiles
+    const uint32_t bits = self ? 0u : cm_bits[v - n_st];
+    const bool full = self ? (kb + BKV - 1 <= qr0 && kb + BKV <= Lq) : (bits == 0xffffffffu);
+    if (!full) {
+      if (self) {
+        const int kmax = min(i_loc, Lq - 1) - kb - 8 * g;  // slot key offsets are 8g + const
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int kk = key_of_slot(v, g);
-      const bool ok = is_self ? (kbase + kk <= i_loc) && (kbase + kk < Lq) : (cm_lds[kk] != 0);
-      const float s = ok ? sacc[v] * scale_log2 : -INFINITY;
-      sacc[v] = s;
-      tmax = fmaxf(tmax, s);
+        for (int e = 0; e < 16; ++e) {
+          const int c = e < 8 ? e : e + 8;
+          if (c > kmax) sacc[e] = -INFINITY;
+        }
+      } else {
+        const uint32_t mb = bits >> (8 * g);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int c = e < 8 ? e : e + 8;
+          if (!((mb >> c) & 1u)) sacc[e] = -INFINITY;
+        }
+      }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const bool need = tmax > m_run + LAZY;
-    if (__ballot(need)) {
+    float tmax = sacc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, sacc[e]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;  // scale > 0 commutes with max
+    if (v == 0) {
+      m_run = tmax;  // first tile (causal tile 0: key 0 is visible to every row); accumulator still 0
+    } else if (__ballot(tmax > m_run + LAZY)) {
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -163,54 +267,39 @@ __global__ __launch_bounds__(256, 2) void merged_attn_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
     }
+    const float nm = -m_run;
     bf16x8_t pf0, pf1;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float pv = (sacc[v] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sacc[v] - m_run);
+    for (int e = 0; e < 16; ++e) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[e], scale_log2, nm));  // exp2(-inf) = 0
       l_run += pv;
-      if (v < 8) pf0[v] = to_bf16(pv);
-      else pf1[v - 8] = to_bf16(pv);
+      if (e < 8) pf0[e] = to_bf16(pv);
+      else pf1[e - 8] = to_bf16(pv);
     }
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db) {
-      const bf16_t* vrow = vt_lds + (db * 32 + r) * VT_LD + 8 * g;
-      const bf16x8_t vf0 = *(const bf16x8_t*)(vrow);
-      const bf16x8_t vf1 = *(const bf16x8_t*)(vrow + 16);
+      const bf16x8_t vf0 = *(const bf16x8_t*)(vt + db * 32 * VT_LD);
+      const bf16x8_t vf1 = *(const bf16x8_t*)(vt + db * 32 * VT_LD + 16);
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf0, pf0, oacc[db], 0, 0, 0);
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf1, pf1, oacc[db], 0, 0, 0);
     }
   };
 
-  // ---- self keys: causal, the block needs keys [0, min(Lq, last row + 1))
-  const int n_self = min(Lq, qb * RB + RB);
-  const bf16_t* ks_base = Ks + row0 * kv_ld + (int64_t)kvh * HD;
-  const bf16_t* vs_base = Vs + row0 * kv_ld + (int64_t)kvh * HD;
-  for (int kb = 0; kb < n_self; kb += BKV) {
-    __syncthreads();  // previous tile consumed
-    stage(ks_base + (int64_t)kb * kv_ld, vs_base + (int64_t)kb * kv_ld, kv_ld,
-          [&](int key) { return kb + key < Lq; });
-    __syncthreads();
-    if (kb <= wave_last) consume(kb, true);
-  }
-
-  // ---- cross keys: the pooled passage chunks with chunk_mask = 1
-  if (!bad_doc) {
-    const uint8_t* cmd = cmask + (int64_t)doc * Cmax;
-    const bf16_t* kc_base = Kc + (int64_t)doc * Cmax * c_ld + (int64_t)kvh * HD;
-    const bf16_t* vc_base = Vc + (int64_t)doc * Cmax * c_ld + (int64_t)kvh * HD;
-    for (int cb = 0; cb < Cmax; cb += BKV) {
-      int mine = 0;
-      if (tid < BKV) {
-        mine = (cb + tid < Cmax) ? (cmd[cb + tid] != 0) : 0;
-      }
-      __syncthreads();  // previous tile consumed before cm_lds is overwritten
-      if (tid < BKV) cm_lds[tid] = (uint8_t)mine;
-      if (!__syncthreads_or(mine)) continue;  // no valid chunk in this tile
-      stage(kc_base + (int64_t)cb * c_ld, vc_base + (int64_t)cb * c_ld, c_ld,
-            [&](int key) { return cm_lds[key] != 0; });
-      __syncthreads();
-      consume(cb, false);
+  // software pipeline: tile v+1's K copy and V loads are in flight while tile v
+  // is consumed; one barrier per tile publishes the next slot
+  fetch(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  store_vt(0);
+  __syncthreads();
+  for (int v = 0; v < n_tiles; ++v) {
+    const bool more = v + 1 < n_tiles;
+    if (more) fetch(v + 1);
+    if (v >= n_st || v * BKV <= wave_last) consume(v);  // a wave skips causal tiles entirely above its rows
+    if (more) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      store_vt(v + 1);
     }
+    __syncthreads();
   }
 
   // ---- normalise and store

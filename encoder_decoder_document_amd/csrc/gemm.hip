@@ -6,39 +6,106 @@
 // layout the gfx950 v_mfma_f32_32x32x16_bf16 fragments want: every lane reads 8
 // consecutive k values of one row.
 //
-// Block tile BM x BN x 64 with 256 threads (4 waves), each wave a
-// (BM/WAVES_M) x (BN/WAVES_N) sub-tile of 32x32 MFMA blocks.  The MFMA "A"
-// operand is the weight tile and the "B" operand the activation tile, so each
-// lane's accumulator holds 4 consecutive output columns of one output row and
-// the epilogue writes 8-byte (bf16) or 16-byte (fp32) vectors.  Global tiles
-// are register-staged and double-buffered in LDS; 16-byte k-chunks are stored
-// XOR-swizzled by (row & 7) so the fragment reads of 32 consecutive rows are
-// bank-conflict free.  Workgroups are remapped so that each XCD walks a
-// contiguous range of output tiles (the tiles sharing activation rows stay in
-// one L2).
+// Block tile BM x BN, k in steps of 32, 512 threads (8 waves, two per SIMD),
+// each wave a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  The MFMA "A" operand is
+// the weight tile and the "B" operand the activation tile, so each lane's
+// accumulator holds 4 consecutive output columns of one output row and the
+// epilogue writes 8-byte (bf16) or 16-byte (fp32) vectors.  Tiles move from
+// global memory straight into LDS with the gfx950 global_load_lds_dwordx4 copy
+// (no staging registers) through a 4-slot LDS ring: three k-tiles are in flight
+// while the fourth feeds the MFMAs, one barrier per k-tile.  16-byte k-chunks are stored XOR-swizzled
+// (see swz), chosen through the address each lane fetches, so the fragment
+// reads of 32 consecutive rows are bank-conflict free.  Workgroups are
+// remapped so that each XCD walks a contiguous range of output tiles (the
+// tiles sharing activation rows stay in one L2).
 #include "kalm_common.h"
 
 namespace {
 
 enum Epi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_ACC = 2 };
 
-constexpr int BK = 64;
+constexpr int BK = 32;      // k per pipeline stage: a 64-byte row of 4 16-byte chunks
+constexpr int STAGES = 4;   // LDS ring: up to 3 k-tiles in flight while one is consumed
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
+// Physical 16-byte chunk of logical chunk c (0..3) in tile row `row`.  The
+// gfx950 LDS serves a ds_read_b128 16 lanes at a time across 64 banks (256
+// bytes = 4 rows of 64 bytes), so rows r, r+4, r+8, r+12 (read together by
+// lanes 0-15) must use 4 distinct chunk columns: XOR with (row >> 2) & 3.
+__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 2) & 3); }
+
+// Wait until the copies of the oldest in-flight k-tile are done: at most
+// `later` k-tiles (CPS copies each) issued after it may still be outstanding.
+template <int CPS>
+__device__ __forceinline__ void wait_dma_ktile(int later) {
+  if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPS) : "memory");
+  else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPS) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Copy plan of one ROWS x 32 k-tile of a [rows_total, K] bf16 matrix into LDS
+// (row = 64 bytes; 16-byte chunk c of a row stored at swz(row, c)).  Each wave
+// instruction fills 16 tile rows (1 KB); lane l writes physical chunk l & 3 of
+// row l >> 2, so it fetches the logical chunk that belongs there -- the XOR
+// swizzle is applied through the global address.  Addresses are a scalar
+// 64-bit tile base plus a 32-bit per-lane byte offset; rows past the matrix
+// end are clamped to its last row (their products are discarded).
+template <int ROWS, int NWAVES>
+struct DmaPlan {
+  static constexpr int PER = ROWS / 16 / NWAVES;  // instructions per wave per stage
+  uint64_t base;                                  // byte address of the tile's first row (uniform)
+  uint32_t row_off[PER];                          // byte offset of this lane's source rows
+  uint32_t slab[PER];                             // LDS byte offset of each 1 KB slab (uniform)
+  int lc8[PER];                                   // k offset of this lane's chunk in a k-tile
+
+  __device__ __forceinline__ void init(const bf16_t* G, int rows_total, int K, int r0, int wave, int lane) {
+    const int rr = lane >> 2;
+    base = (uint64_t)(uintptr_t)(G + (int64_t)r0 * K);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int R0 = 16 * (wave * PER + j);
+      const int row = min(r0 + R0 + rr, rows_total - 1) - r0;
+      lc8[j] = swz(R0 + rr, lane & 3) * 8;  // the swizzle is an involution
+      row_off[j] = (uint32_t)row * (uint32_t)K * 2u;
+      slab[j] = (uint32_t)__builtin_amdgcn_readfirstlane(R0 * 64);
+    }
+  }
+  // k-tile starting at k0 into the tile at LDS byte address tile_lds
+  __device__ __forceinline__ void issue(uint32_t tile_lds, int k0, int K) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      int kk = k0 + lc8[j];
+      if (kk >= K) kk = 0;  // in-bounds dummy; zeroed in LDS by zero_k_tail
+      dma16(base, row_off[j] + (uint32_t)kk * 2u, tile_lds + slab[j]);
+    }
+  }
+};
+
+// Zero the 16-byte chunks of a staged tile that lie beyond K (last k-tile only).
+template <int ROWS>
+__device__ __forceinline__ void zero_k_tail(bf16_t* tile, int k0, int K, int tid, int nthreads) {
+  for (int e = tid; e < ROWS * 4; e += nthreads) {
+    const int row = e >> 2, pc = e & 3, lc = swz(row, pc);
+    if (k0 + lc * 8 >= K) *(u32x4_t*)(tile + row * BK + pc * 8) = u32x4_t{0, 0, 0, 0};
+  }
+}
+
+// 8 waves; the block tile BM x BN is split WM x WN ways.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, int M, int K, int N,
     void* __restrict__ Y, int epi, bf16_t* __restrict__ Ybf, const uint8_t* __restrict__ rmask) {
-  static_assert(WAVES_M * WAVES_N == 4, "4 waves");
-  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static_assert(WM * WN == 8, "8 waves");
+  constexpr int CPS = DmaPlan<BM, 8>::PER + DmaPlan<BN, 8>::PER;  // copies per thread per k-tile
+  static_assert(STAGES == 4, "wait_dma_ktile assumes at most two later k-tiles in flight");
+  constexpr int NT = 512;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int LA = BM / 32, LB = BN / 32;  // 16-byte loads per thread per k-tile
+  constexpr int STAGE_ELEMS = (BM + BN) * BK;
 
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * BK];
-  bf16_t* As = smem;                 // [2][BM][BK]
-  bf16_t* Bs = smem + 2 * BM * BK;   // [2][BN][BK]
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGES * STAGE_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int wm = wave % WM, wn = wave / WM;
 
   // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a
   // contiguous run of tiles, output columns fastest.
@@ -55,7 +122,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
   bool tile_live = true;
   if (rmask) {
     int any = 0;
-    for (int rr = tid; rr < BM; rr += 256)
+    for (int rr = tid; rr < BM; rr += NT)
       if (m0 + rr < M && rmask[m0 + rr]) any = 1;
     tile_live = __syncthreads_or(any) != 0;
   }
@@ -68,49 +135,35 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int lrow = tid >> 3, lkc = tid & 7;  // staging: row within 32-row slab, 16B k-chunk
-  u32x4_t ra[LA], rb[LB];
-  auto gload = [&](int k0) {
-    const int kk = k0 + lkc * 8;
-    const bool kin = kk < K;
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int gm = min(m0 + lrow + 32 * i, M - 1);
-      ra[i] = kin ? *(const u32x4_t*)(X + (int64_t)gm * K + kk) : u32x4_t{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int gn = min(n0 + lrow + 32 * i, N - 1);
-      rb[i] = kin ? *(const u32x4_t*)(W + (int64_t)gn * K + kk) : u32x4_t{0, 0, 0, 0};
-    }
-  };
-  auto sstore = [&](int buf) {
-    bf16_t* a = As + buf * BM * BK;
-    bf16_t* bb = Bs + buf * BN * BK;
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int row = lrow + 32 * i;
-      *(u32x4_t*)(a + row * BK + ((lkc ^ (row & 7)) << 3)) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int row = lrow + 32 * i;
-      *(u32x4_t*)(bb + row * BK + ((lkc ^ (row & 7)) << 3)) = rb[i];
-    }
+  const int nk = tile_live ? (K + BK - 1) / BK : 0;
+  const bool k_tail = (K % BK) != 0;
+  DmaPlan<BM, 8> planA;
+  DmaPlan<BN, 8> planB;
+  planA.init(X, M, K, m0, wave, lane);
+  planB.init(W, N, K, n0, wave, lane);
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  auto issue = [&](int kt) {  // k-tile kt into ring slot kt % STAGES
+    const uint32_t b = lds_base + (uint32_t)((kt % STAGES) * STAGE_ELEMS * 2);
+    planA.issue(b, kt * BK, K);
+    planB.issue(b + BM * BK * 2, kt * BK, K);
   };
 
-  const int nk = tile_live ? (K + BK - 1) / BK : 0;
   const int r = lane & 31, g = lane >> 5;
-  if (nk > 0) {
-    gload(0);
-    sstore(0);
-    __syncthreads();
-  }
+  for (int kt = 0; kt < STAGES - 1 && kt < nk; ++kt) issue(kt);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    const bf16_t* a = As + cur * BM * BK;
-    const bf16_t* bb = Bs + cur * BN * BK;
+    // this thread's copies of k-tile kt are done once at most those of the
+    // (up to two) later k-tiles already issued are outstanding
+    wait_dma_ktile<CPS>(min(nk - 1 - kt, STAGES - 2));
+    __syncthreads();  // k-tile kt visible to all waves; slot of k-tile kt-1 free
+    bf16_t* cur = smem + (kt % STAGES) * STAGE_ELEMS;
+    if (k_tail && kt == nk - 1) {
+      zero_k_tail<BM>(cur, kt * BK, K, tid, NT);
+      zero_k_tail<BN>(cur + BM * BK, kt * BK, K, tid, NT);
+      __syncthreads();
+    }
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    const bf16_t* a = cur;
+    const bf16_t* bb = cur + BM * BK;
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
       const int kc = 2 * s + g;
@@ -118,12 +171,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
         const int row = wm * WTM + j * 32 + r;
-        xf[j] = *(const bf16x8_t*)(a + row * BK + ((kc ^ (row & 7)) << 3));
+        xf[j] = *(const bf16x8_t*)(a + row * BK + (swz(row, kc) << 3));
       }
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
         const int row = wn * WTN + i * 32 + r;
-        wf[i] = *(const bf16x8_t*)(bb + row * BK + ((kc ^ (row & 7)) << 3));
+        wf[i] = *(const bf16x8_t*)(bb + row * BK + (swz(row, kc) << 3));
       }
 #pragma unroll
       for (int i = 0; i < FN; ++i)
@@ -131,8 +184,6 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
         for (int j = 0; j < FM; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
   }
 
   // epilogue: lane holds Y[m][n .. n+3] for m = .. + (lane & 31), n = .. + 8*q + 4*g
@@ -234,10 +285,16 @@ namespace kalm {
 void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, void* Y, bool y_f32,
                         bool accumulate, bf16_t* Y_bf16, const uint8_t* rmask, hipStream_t s) {
   const int epi = !y_f32 ? EPI_BF16 : (accumulate ? EPI_F32_ACC : EPI_F32);
-  constexpr int BM = 256, BN = 256;
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 2, 2>), dim3(tiles), dim3(256), 0, s, X, W, M, K, N, Y,
-                     epi, Y_bf16, rmask);
+  const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles >= 512) {
+    const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y, epi,
+                       Y_bf16, rmask);
+  } else {  // small problems: more, smaller tiles to fill the 256 CUs
+    const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y, epi,
+                       Y_bf16, rmask);
+  }
 }
 
 void launch_linear_f32(const float* X, const float* W, int M, int K, int N, float* Y, bool accumulate,

@@ -164,6 +164,9 @@ kalm_status kalm_merged_attn(const void* Q, int64_t q_ld, const void* Ks, const 
     const int G = nq / nkv;
     KALM_REQUIRE(G == 1 || G == 2 || G % 4 == 0, KALM_ERR_UNSUPPORTED,
                  "kalm_merged_attn: query heads per KV head must be 1, 2 or a multiple of 4 (got %d)", G);
+    KALM_REQUIRE(Cmax <= 4096, KALM_ERR_UNSUPPORTED, "kalm_merged_attn: bf16 path supports Cmax <= 4096 (got %d)", Cmax);
+    KALM_REQUIRE((int64_t)max_lq * kv_ld * 2 < (1LL << 31) && (int64_t)Cmax * c_ld * 2 < (1LL << 31),
+                 KALM_ERR_UNSUPPORTED, "kalm_merged_attn: per-pair K block exceeds 2 GiB");
     KALM_REQUIRE(q_ld % 8 == 0 && kv_ld % 8 == 0 && o_ld % 8 == 0 && c_ld % 8 == 0, KALM_ERR_UNSUPPORTED,
                  "kalm_merged_attn: bf16 leading dimensions must be multiples of 8");
     KALM_REQUIRE(ALIGNED16(Q) && ALIGNED16(Ks) && ALIGNED16(Vs) && ALIGNED16(O) && ALIGNED16(Kc) && ALIGNED16(Vc),

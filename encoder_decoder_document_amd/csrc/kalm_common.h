@@ -36,6 +36,37 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane i of the wave writes LDS bytes [16 i, 16 i + 16) after the wave-uniform
+// base held in M0.  Issued from asm: the compiler's wait-count pass treats every
+// LDS-DMA as aliasing every LDS access and would otherwise wait for each copy
+// before the next one is issued.  The instruction has no register results; the
+// kernel waits for its copies explicitly (vmcnt) before the barrier that
+// publishes a tile.
+// A wave-uniform 64-bit value the compiler cannot prove uniform, moved to SGPRs.
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void_t*)p;
+}
+__device__ __forceinline__ void dma16(uint64_t sbase, uint32_t voff, uint32_t lds_wave_base) {
+  uint32_t saved;  // M0 is a compiler-reserved register: restore it after the copy is issued
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_wave_base)
+      : "memory");
+}
+
 // ---------------------------------------------------------------- host side
 namespace kalm {
 
