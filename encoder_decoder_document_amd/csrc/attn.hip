@@ -8,75 +8,98 @@
 // (running max m, running sum l, fp32 accumulator) that is carried across the
 // self/cross boundary -- a single pass, no second reduction.
 //
-// Work unit (one 256-thread workgroup): one pair, one KV head and 128 "rows",
-// the query heads that share that KV head packed with 32-row blocks of decoder
-// rows (4 heads x 32 rows for 4:1 grouping, 2 x 64 for 2:1, 1 x 128 for 1:1),
-// so every K/V tile staged in LDS serves all heads of the group.  Each wave
-// owns 32 rows of one head and keeps its Q fragments (32 rows x 256) in
-// registers.
+// Work unit (one 512-thread workgroup, 8 waves): one pair, one KV head and
+// 8 slots of 32 decoder rows x one query head -- the query heads that share
+// the KV head packed with row blocks (4 heads x 64 rows for 4:1 grouping,
+// 2 x 128 for 2:1, 1 x 256 for 1:1) -- so every K/V tile staged in LDS serves
+// 256 query vectors.  That reuse sets the LDS-fill traffic per flop; each wave
+// keeps its Q fragments (32 rows x 256 dims) and fp32 O accumulator in
+// registers.  K and V tiles move global -> LDS with direct-to-LDS loads
+// through a 3-slot ring, two tiles in flight.
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16, 64-wide waves):
 //   S^T[key, row]  = K . Q^T     A = K tile rows from LDS, B = Q fragments
-//   O^T[dim, row] += V^T . P^T   A = V^T rows from LDS,    B = P from registers
+//   O^T[dim, row] += V^T . P^T   A = V^T from LDS (transposing reads), B = P
 // Computing the transposed products puts one decoder row in each lane
 // (lane & 31), so the softmax row max needs a single exchange with lane ^ 32,
 // the rescale is one scalar per lane, and the S accumulator can be fed
-// straight back as the B operand of the PV product: the K rows are loaded in
+// straight back as the B operand of the PV product: the K rows are read in
 // the order "swap bits 2 and 3 of the slot index", which makes the 16 logits a
-// lane holds exactly the 16 keys its PV fragments need.  V is transposed once
-// per tile while it is written to LDS (8-byte stores of 4 keys), so the PV
-// fragment reads are 16-byte vectors.  Rescaling of the accumulator is lazy:
-// the running max only moves when a tile's max exceeds it by more than 8
-// (log2 units), which keeps every exponent <= 2^8 and skips most rescales.
+// lane holds exactly the 16 keys its PV fragments need.  Rescaling of the
+// accumulator is lazy: the running max only moves when a tile's max exceeds
+// it by more than 8 (log2 units), which keeps every exponent <= 2^8 and skips
+// most rescales.
 #include <math.h>
 
 #include "kalm_common.h"
 
 namespace {
 
-constexpr int HD = 256;        // head dim of the bf16 path
-constexpr int BKV = 32;        // keys per tile
-constexpr int VT_LD = BKV + 8; // bf16 per transposed-V row in LDS (80 bytes)
-constexpr float LAZY = 8.0f;   // lazy-rescale threshold, log2 units
-constexpr int MAX_CTILES = 128;  // cross tiles per passage (Cmax <= 4096)
+constexpr int HD = 256;          // head dim of the bf16 path
+constexpr int BKV = 32;          // keys per tile
+constexpr int RING = 3;          // K/V tiles resident in LDS (two in flight)
+constexpr float LAZY = 8.0f;     // lazy-rescale threshold, log2 units
+constexpr int MAX_CTILES = 128;  // cross tiles per passage (Cmax <= 4096): two mask words per lane
 
-__device__ __forceinline__ int key_of_slot(int v, int g) {  // key a lane's v-th logit belongs to
-  return v < 8 ? 8 * g + v : 16 + 8 * g + (v - 8);
-}
-// Physical 16-byte chunk of logical chunk c (0..31) in K row `key` (512-byte
-// rows).  A ds_read_b128 is served 16 lanes at a time over 64 banks (256 bytes);
-// lanes 0-15 read keys 0-15 (in the bit-2/3 swapped order) at one logical
-// chunk, so XOR with key & 15 spreads them over 16 distinct chunk columns.
+// Physical 16-byte chunk of logical chunk c (0..31) in a K row (512 bytes).
+// The S product reads 16 keys at one logical chunk per 16-lane phase over 64
+// banks (256 bytes): XOR with key & 15 spreads them over 16 chunk columns.
 __device__ __forceinline__ int k_swz(int key, int c) { return c ^ (key & 15); }
+// Same for a V row.  V is read with ds_read_b64_tr_b16: 32 lanes take 8 bytes
+// from each of 4 consecutive keys at 4 consecutive chunks; XOR with 4*(key & 3)
+// puts the 4 keys on 16 distinct chunk columns.
+__device__ __forceinline__ int v_swz(int key, int c) { return c ^ ((key & 3) << 2); }
 
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// Transposing LDS read at a byte address (gfx950 ds_read_b64_tr_b16).  In
+// each 16-lane group, lane i receives halfword (i & 3) of the 8-byte pieces
+// addressed by lanes (i >> 2) + 4k, k = 0..3 (in that order).
+__device__ __forceinline__ u32x2_t lds_tr_at(uint32_t addr) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(size_t)addr);
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// 16-byte LDS read at a byte address.
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+__device__ __forceinline__ bf16x8_t lds_read16(uint32_t addr) { return *(const lds_bf16x8_t*)(size_t)addr; }
+
+// One workgroup = 8 waves = 8 slots of 32 decoder rows x one query head
+// (NH heads x WPH row blocks).  Every K/V tile staged in LDS is shared by the
+// 256 (row, head) query vectors of the block -- the reuse that keeps the
+// kernel off the L2 bandwidth limit.  Each wave keeps its Q fragments (32 rows
+// x 256 dims) and its fp32 O accumulator in registers.  K and V tiles move
+// global -> LDS by DMA through a 3-slot ring (two tiles in flight).
 template <int NH>
-__global__ __launch_bounds__(256, 1) void merged_attn_bf16_kernel(
+__global__ __launch_bounds__(512, 1) void merged_attn_bf16_kernel(
     const bf16_t* __restrict__ Q, int64_t q_ld, const bf16_t* __restrict__ Ks,
     const bf16_t* __restrict__ Vs, int64_t kv_ld, const int32_t* __restrict__ cu_q, int P,
     int64_t rows, int nqb, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     int64_t c_ld, const uint8_t* __restrict__ cmask, const int32_t* __restrict__ doc_of_pair,
     int D, int Cmax, int nq, int nkv, float scale_log2, bf16_t* __restrict__ O, int64_t o_ld,
     float* __restrict__ lse) {
-  constexpr int WPH = 4 / NH;   // waves per head
+  constexpr int WPH = 8 / NH;   // row blocks per head
   constexpr int RB = 32 * WPH;  // decoder rows per block
-  // two ring slots of (K tile [32 keys][256], swizzled) and (V^T tile [256][32+8])
-  __shared__ __attribute__((aligned(1024))) bf16_t k_lds[2][BKV * HD];
-  __shared__ __attribute__((aligned(16))) bf16_t vt_lds[2][HD * VT_LD];
-  __shared__ __attribute__((aligned(1024))) bf16_t q_lds[4][32 * HD];  // each wave's 32 query rows (swizzled)
-  __shared__ uint32_t cm_bits[MAX_CTILES];  // valid-chunk bits of each cross tile
-  __shared__ int n_ctiles_s;
+  __shared__ __attribute__((aligned(1024))) bf16_t k_lds[RING][BKV * HD];  // K tiles, k_swz
+  __shared__ __attribute__((aligned(1024))) bf16_t v_lds[RING][BKV * HD];  // V tiles, v_swz
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, g = lane >> 5;
   const int G = nq / nkv, HG = G / NH;
 
-  // heaviest row blocks first (later rows see more causal keys)
-  const int64_t per_level = (int64_t)P * nkv * HG;
+  // Work order for L2 reuse: pair-major, the pair's head groups and row
+  // blocks consecutive (they share the pair's self K/V and the passage's cross
+  // K/V), and each XCD (block b runs on XCD b % 8) walks a contiguous range.
+  const int64_t per_pair = (int64_t)nkv * HG * nqb;
+  const int64_t total = (int64_t)P * per_pair;
   const int64_t b = blockIdx.x;
-  const int qb = nqb - 1 - (int)(b / per_level);
-  const int64_t rem = b % per_level;
-  const int p = (int)(rem % P);
-  const int hgi = (int)(rem / P);
+  const int64_t xper = total / 8;
+  const int64_t t = (b < xper * 8) ? (b % 8) * xper + b / 8 : b;
+  const int p = (int)(t / per_pair);
+  const int64_t rem = t % per_pair;
+  const int qb = (int)(rem % nqb);
+  const int hgi = (int)(rem / nqb);
   const int kvh = hgi / HG, hg = hgi % HG;
 
   const int64_t row0 = cu_q[p];
@@ -87,25 +110,35 @@ __global__ __launch_bounds__(256, 1) void merged_attn_bf16_kernel(
   const int doc = doc_of_pair[p];
   const bool bad_doc = doc < 0 || doc >= D;
 
-  // cross-tile validity bits; tiles past the last valid chunk are dropped
+  // cross-tile validity words, kept in registers by every wave: lane l holds
+  // the words of tiles l and l + 64 (one ballot per 64 chunks); word t is
+  // read back with a scalar readlane
   const int n_ct_all = bad_doc ? 0 : (Cmax + BKV - 1) / BKV;
-  if (tid < BKV) {
+  uint32_t cmw0 = 0, cmw1 = 0;
+  {
     const uint8_t* cmd = cmask + (int64_t)(bad_doc ? 0 : doc) * Cmax;
-    for (int ct = 0; ct < n_ct_all; ++ct) {
-      const int c = ct * BKV + tid;
-      const bool v = c < Cmax && cmd[c] != 0;
-      const uint64_t bits = __ballot(v);
-      if (tid == 0) cm_bits[ct] = (uint32_t)bits;
-    }
-    if (tid == 0) {
-      int last = 0;
-      for (int ct = 0; ct < n_ct_all; ++ct)
-        if (cm_bits[ct]) last = ct + 1;
-      n_ctiles_s = last;
+    for (int base = 0; base < n_ct_all * BKV; base += 64) {
+      const int c = base + lane;
+      const uint64_t bits = __ballot(c < Cmax && cmd[c] != 0);
+      const int w = base >> 5;  // tile index of the low word
+      if (lane == (w & 63)) {
+        if (w < 64) cmw0 = (uint32_t)bits; else cmw1 = (uint32_t)bits;
+      }
+      if (lane == ((w + 1) & 63)) {
+        if (w + 1 < 64) cmw0 = (uint32_t)(bits >> 32); else cmw1 = (uint32_t)(bits >> 32);
+      }
     }
   }
-  __syncthreads();
-  const int n_ct = n_ctiles_s;
+  auto cm_word = [&](int t) -> uint32_t {  // t is wave-uniform
+    return t < 64 ? __builtin_amdgcn_readlane(cmw0, t) : __builtin_amdgcn_readlane(cmw1, t - 64);
+  };
+  const uint64_t nz0 = __ballot(cmw0 != 0), nz1 = __ballot(cmw1 != 0);
+  const int n_ct = nz1 ? 64 + 64 - __builtin_clzll(nz1) : (nz0 ? 64 - __builtin_clzll(nz0) : 0);
+  int donor = 0;  // a valid chunk: masked chunk rows are fetched from it
+  if (n_ct) {
+    const int t = nz0 ? __builtin_ctzll(nz0) : 64 + __builtin_ctzll(nz1);
+    donor = t * BKV + __builtin_ctz(cm_word(t));
+  }
 
   const int h = kvh * G + hg * NH + wave / WPH;
   const int qr0 = qb * RB + (wave % WPH) * 32;  // first decoder row of this wave
@@ -113,19 +146,12 @@ __global__ __launch_bounds__(256, 1) void merged_attn_bf16_kernel(
   const int i_ld = min(i_loc, Lq - 1);
   const int wave_last = min(qr0 + 31, Lq - 1);
 
-  // this wave's 32 query rows -> LDS by DMA (16 instructions of 2 rows x 512 bytes);
-  // lane l writes physical chunk l & 31 of row 2j + (l >> 5); chunks XOR-swizzled
-  // with row & 15 like K, so the B-operand reads of 16 rows are conflict free
+  // Q fragments (MFMA B operand of S^T = K Q^T): 16 k-steps of 16 dims
+  bf16x8_t qf[HD / 16];
   {
-    const uint64_t qbase = uniform64((uint64_t)(uintptr_t)(Q + row0 * q_ld + (int64_t)h * HD));
-    const uint32_t qlds = __builtin_amdgcn_readfirstlane(lds_addr(&q_lds[wave][0]));
-    const uint32_t q_ld2 = (uint32_t)q_ld * 2u;
+    const bf16_t* qp = Q + (row0 + i_ld) * q_ld + (int64_t)h * HD + 8 * g;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int qrow = 2 * j + (lane >> 5);
-      const int src_row = min(qr0 + qrow, Lq - 1);
-      dma16(qbase, (uint32_t)src_row * q_ld2 + (uint32_t)(k_swz(qrow, lane & 31) * 16), qlds + j * 1024);
-    }
+    for (int s = 0; s < HD / 16; ++s) qf[s] = *(const bf16x8_t*)(qp + 16 * s);
   }
 
   f32x16_t oacc[HD / 32];
@@ -145,94 +171,97 @@ __global__ __launch_bounds__(256, 1) void merged_attn_bf16_kernel(
   const uint64_t kc_base = (uint64_t)(uintptr_t)(Kc + cdoc);
   const uint64_t vc_base = (uint64_t)(uintptr_t)(Vc + cdoc);
   const uint32_t klds0 = __builtin_amdgcn_readfirstlane(lds_addr(&k_lds[0][0]));
+  const uint32_t vlds0 = __builtin_amdgcn_readfirstlane(lds_addr(&v_lds[0][0]));
   const uint32_t kv_ld2 = (uint32_t)kv_ld * 2u, c_ld2 = (uint32_t)c_ld * 2u;
 
-  // Per-lane pieces of the copy addresses, fixed for the whole block.
-  // K (LDS DMA): wave instruction j fills key rows kj, kj+1 (1 KB); lane l writes
-  // physical chunk l & 31 of key row kj + (l >> 5).
-  int kkey[4], klc16[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    kkey[j] = 2 * (wave * 4 + j) + (lane >> 5);
-    klc16[j] = k_swz(kkey[j], lane & 31) * 16;
-  }
-  const uint32_t kslab = __builtin_amdgcn_readfirstlane(wave * 4 * 1024);
-  // V (registers): thread holds keys 4*vkg .. 4*vkg+3, dims 8*vdc .. 8*vdc+7
-  const int vkg = tid & 7, vdc = tid >> 3;
+  // DMA plan: wave instruction j (of 2) fills key rows 2(2w+j), +1 (1 KB) of a
+  // tile; lane l writes physical chunk l & 31 of key row 2(2w+j) + (l >> 5)
+  const int dkey0 = 4 * wave + (lane >> 5);  // second row pair: dkey0 + 2
+  const int klc16_0 = k_swz(dkey0, lane & 31) * 16, klc16_1 = k_swz(dkey0 + 2, lane & 31) * 16;
+  const int vlc16_0 = v_swz(dkey0, lane & 31) * 16, vlc16_1 = v_swz(dkey0 + 2, lane & 31) * 16;
+  const uint32_t dslab = __builtin_amdgcn_readfirstlane(wave * 2 * 1024);
 
-  auto tile_src = [&](int v, uint64_t& kb_addr, uint64_t& vb_addr, uint32_t& ld2, int& lim, int& kb) {
-    const bool self = v < n_st;
-    kb = self ? v * BKV : (v - n_st) * BKV;
-    ld2 = self ? kv_ld2 : c_ld2;
-    lim = self ? Lq : Cmax;  // key rows at or past it are clamped
-    kb_addr = (self ? ks_base : kc_base) + (uint64_t)kb * ld2;
-    vb_addr = (self ? vs_base : vc_base) + (uint64_t)kb * ld2;
-  };
-
-  u32x4_t vr[4];
-  // issue the copies of tile v: K straight to LDS slot v & 1, V into registers
-  auto fetch = [&](int v) {
-    uint64_t kba, vba;
-    uint32_t ld2;
-    int lim, kb;
-    tile_src(v, kba, vba, ld2, lim, kb);
-    const int nrow = lim - kb;  // rows of this tile that exist (>= 1)
-    const uint32_t slot = klds0 + (uint32_t)((v & 1) * BKV * HD * 2) + kslab;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = min(kkey[j], nrow - 1);
-      dma16(kba, (uint32_t)row * ld2 + klc16[j], slot + j * 1024);
-    }
-    const uint8_t* vb = (const uint8_t*)(uintptr_t)vba;
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const int row = min(4 * vkg + pp, nrow - 1);
-      vr[pp] = *(const u32x4_t*)(vb + ((uint32_t)row * ld2 + vdc * 16));
-    }
-  };
-  // zero the V rows of keys that do not exist or are masked, then write V^T
-  auto store_vt = [&](int v) {
+  // copy tile v (K and V) into ring slot v % RING.  Key rows that do not
+  // exist (past the pair / the passage) or are masked are fetched from a
+  // valid row instead: their logits are masked to -inf, so p = 0 multiplies a
+  // finite value.
+  auto issue = [&](int v) {
     const bool self = v < n_st;
     const int kb = self ? v * BKV : (v - n_st) * BKV;
-    const uint32_t valid = self ? (Lq - kb >= BKV ? 0xffffffffu : ((1u << (Lq - kb)) - 1u)) : cm_bits[v - n_st];
-    if (valid != 0xffffffffu) {
+    const uint32_t ld2 = self ? kv_ld2 : c_ld2;
+    const uint64_t kba = self ? ks_base : kc_base;
+    const uint64_t vba = self ? vs_base : vc_base;
+    const uint32_t bits = self ? 0u : cm_word(v - n_st);
+    const uint32_t so = (uint32_t)((v % RING) * BKV * HD * 2) + dslab;
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp)
-        if (!((valid >> (4 * vkg + pp)) & 1u)) vr[pp] = u32x4_t{0, 0, 0, 0};
-    }
-    bf16_t* vt = &vt_lds[v & 1][0] + (vdc * 8) * VT_LD + 4 * vkg;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {  // dims 2m (low halves) and 2m+1 (high halves)
-      const uint32_t lo01 = __builtin_amdgcn_perm(vr[1][m], vr[0][m], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(vr[3][m], vr[2][m], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(vr[1][m], vr[0][m], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(vr[3][m], vr[2][m], 0x07060302u);
-      *(u32x2_t*)(vt + (2 * m) * VT_LD) = u32x2_t{lo01, lo23};
-      *(u32x2_t*)(vt + (2 * m + 1) * VT_LD) = u32x2_t{hi01, hi23};
+    for (int j = 0; j < 2; ++j) {
+      const int key = dkey0 + 2 * j;
+      int row;
+      if (self) row = min(kb + key, Lq - 1);
+      else row = ((bits >> key) & 1u) ? kb + key : donor;
+      const uint32_t ro = (uint32_t)row * ld2;
+      dma16(kba, ro + (j ? klc16_1 : klc16_0), klds0 + so + j * 1024);
+      dma16(vba, ro + (j ? vlc16_1 : vlc16_0), vlds0 + so + j * 1024);
     }
   };
 
-  const int krow = (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1);  // swap bits 2 and 3
-  const bf16_t* kfrag0 = &k_lds[0][0] + krow * HD;
-  const bf16_t* qfrag = &q_lds[wave][0] + r * HD;
-  const bf16_t* vfrag0 = &vt_lds[0][0] + r * VT_LD + 8 * g;
-  // consume tile v from ring slot v & 1
-  auto consume = [&](int v) {
+  // K fragment reads.  Lane (r, g) reads key row krow (r with bits 2 and 3
+  // swapped) at logical chunk 2s + g of k-step s; physical chunk (2s + g) ^
+  // (krow & 15) = 2s ^ (g ^ (krow & 15)), so the byte address of k-step s is
+  // kx ^ 32s with one per-lane base kx (the XOR only touches bits 4..8, below
+  // the 512-byte row and tile offsets).
+  const int krow = (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1);
+  const uint32_t kx = lds_addr(&k_lds[0][0]) + krow * (HD * 2) + ((g ^ (krow & 15)) << 4);
+  // V^T fragment reads (transposing, 8 bytes per lane): in 16-lane group
+  // G = lane >> 4, lane i addresses key 8 * (G >> 1) + (i >> 2) (+4 for the
+  // second read, +16 per k-step) at dims 16 * (G & 1) + 4 * (i & 3) of each
+  // 32-dim block db.  Physical chunk 4 (db ^ (key & 3)) + c0, so the byte
+  // address of block db is vx ^ 64 db.
+  const int vg = lane >> 4, vi = lane & 15;
+  const int vkey = 8 * (vg >> 1) + (vi >> 2);
+  const int vdim0 = 16 * (vg & 1) + 4 * (vi & 3);
+  const uint32_t vx = lds_addr(&v_lds[0][0]) + vkey * (HD * 2) + 64 * (vkey & 3) + 16 * (vdim0 >> 3) +
+                      2 * (vdim0 & 7);
+
+  for (int v = 0; v < RING - 1 && v < n_tiles; ++v) issue(v);
+  for (int v = 0; v < n_tiles; ++v) {
+    wait_dma_ktile<4>(min(n_tiles - 1 - v, RING - 2));
+    __syncthreads();  // tile v visible; the slot of tile v-1 is free
+    if (v + RING - 1 < n_tiles) issue(v + RING - 1);
     const bool self = v < n_st;
     const int kb = self ? v * BKV : (v - n_st) * BKV;
-    const bf16_t* kt = kfrag0 + (v & 1) * (BKV * HD);
-    const bf16_t* vt = vfrag0 + (v & 1) * (HD * VT_LD);
+    // nothing to do: no valid rows in this wave, or a causal tile entirely
+    // above its rows (the wave still joins every barrier and copy)
+    if (qr0 >= Lq || (self && kb > wave_last)) continue;
+    const uint32_t slot = (uint32_t)((v % RING) * (BKV * HD * 2));
+    uint32_t kt = kx + slot, vt = vx + slot;
+    // opaque per tile: keeps the compiler from hoisting 24 precomputed
+    // fragment addresses out of the loop (one XOR per read is cheaper than
+    // the registers they would hold)
+    asm volatile("" : "+v"(kt), "+v"(vt));
     f32x16_t sacc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+    // K fragments in groups of KG k-steps, the next group read while the
+    // current one multiplies (bounds the registers held by K fragments)
+    constexpr int KG = 2;
+    bf16x8_t kfa[KG], kfb[KG];
 #pragma unroll
-    for (int s = 0; s < HD / 16; ++s) {
-      const bf16x8_t kf = *(const bf16x8_t*)(kt + (k_swz(krow, 2 * s + g) << 3));
-      const bf16x8_t qf = *(const bf16x8_t*)(qfrag + (k_swz(r, 2 * s + g) << 3));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf, sacc, 0, 0, 0);
+    for (int j = 0; j < KG; ++j) kfa[j] = lds_read16(kt ^ (32u * j));
+#pragma unroll
+    for (int s0 = 0; s0 < HD / 16; s0 += KG) {
+      if (s0 + KG < HD / 16) {
+#pragma unroll
+        for (int j = 0; j < KG; ++j) kfb[j] = lds_read16(kt ^ (32u * (s0 + KG + j)));
+      }
+#pragma unroll
+      for (int j = 0; j < KG; ++j) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfa[j], qf[s0 + j], sacc, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < KG; ++j) kfa[j] = kfb[j];
+      __builtin_amdgcn_sched_barrier(0);
     }
     // masking only for the causal diagonal / ragged self tiles and partial cross tiles
-    const uint32_t bits = self ? 0u : cm_bits[v - n_st];
+    const uint32_t bits = self ? 0u : cm_word(v - n_st);
     const bool full = self ? (kb + BKV - 1 <= qr0 && kb + BKV <= Lq) : (bits == 0xffffffffu);
     if (!full) {
       if (self) {
@@ -255,11 +284,13 @@ __global__ __launch_bounds__(256, 1) void merged_attn_bf16_kernel(
 #pragma unroll
     for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, sacc[e]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;  // scale > 0 commutes with max
-    if (v == 0) {
-      m_run = tmax;  // first tile (causal tile 0: key 0 is visible to every row); accumulator still 0
-    } else if (__ballot(tmax > m_run + LAZY)) {
+    // lazy rescale: the running max moves only when some row's tile max
+    // exceeds it by more than LAZY (log2 units); the first tile (m_run = -inf,
+    // accumulator 0) always takes this branch with alpha = 0.  Tile 0 holds
+    // key 0, visible to every row, so tmax is finite there.
+    if (__ballot(tmax > m_run + LAZY)) {
       const float m_new = fmaxf(m_run, tmax);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // exp2(-inf) = 0
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -276,30 +307,27 @@ __global__ __launch_bounds__(256, 1) void merged_attn_bf16_kernel(
       if (e < 8) pf0[e] = to_bf16(pv);
       else pf1[e - 8] = to_bf16(pv);
     }
+    // V^T fragments of 32 dims: keys 8g..8g+7 (k-step 0) and 16+8g..16+8g+7
+    // (k-step 1), 4 keys per transposing read; block db+1 is read while block
+    // db multiplies
+    auto vread = [&](int db, u32x4_t& a0, u32x4_t& a1) {
+      const uint32_t base = vt ^ (64u * db);
+      const u32x2_t t0 = lds_tr_at(base), t1 = lds_tr_at(base + 4 * HD * 2);
+      const u32x2_t t2 = lds_tr_at(base + 16 * HD * 2), t3 = lds_tr_at(base + 20 * HD * 2);
+      a0 = u32x4_t{t0[0], t0[1], t1[0], t1[1]};
+      a1 = u32x4_t{t2[0], t2[1], t3[0], t3[1]};
+    };
+    u32x4_t va0, va1, vb0, vb1;
+    vread(0, va0, va1);
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db) {
-      const bf16x8_t vf0 = *(const bf16x8_t*)(vt + db * 32 * VT_LD);
-      const bf16x8_t vf1 = *(const bf16x8_t*)(vt + db * 32 * VT_LD + 16);
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf0, pf0, oacc[db], 0, 0, 0);
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf1, pf1, oacc[db], 0, 0, 0);
+      if (db + 1 < HD / 32) vread(db + 1, vb0, vb1);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va0), pf0, oacc[db], 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va1), pf1, oacc[db], 0, 0, 0);
+      va0 = vb0;
+      va1 = vb1;
+      __builtin_amdgcn_sched_barrier(0);
     }
-  };
-
-  // software pipeline: tile v+1's K copy and V loads are in flight while tile v
-  // is consumed; one barrier per tile publishes the next slot
-  fetch(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  store_vt(0);
-  __syncthreads();
-  for (int v = 0; v < n_tiles; ++v) {
-    const bool more = v + 1 < n_tiles;
-    if (more) fetch(v + 1);
-    if (v >= n_st || v * BKV <= wave_last) consume(v);  // a wave skips causal tiles entirely above its rows
-    if (more) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      store_vt(v + 1);
-    }
-    __syncthreads();
   }
 
   // ---- normalise and store
@@ -403,11 +431,11 @@ void launch_merged_attn_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, co
                              bf16_t* O, int64_t o_ld, float* lse, hipStream_t s) {
   const int G = nq / nkv;
   const int NH = G >= 4 ? 4 : G;  // heads per block (G is 1, 2 or a multiple of 4)
-  const int RB = 32 * (4 / NH);
+  const int RB = 32 * (8 / NH);
   const int nqb = (max_lq + RB - 1) / RB;
   const int64_t blocks = (int64_t)P * nkv * (G / NH) * nqb;
   const float sl2 = scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)blocks), block(256);
+  const dim3 grid((unsigned)blocks), block(512);
   if (blocks == 0) return;
   if (NH == 4)
     hipLaunchKernelGGL(merged_attn_bf16_kernel<4>, grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, P, rows, nqb,

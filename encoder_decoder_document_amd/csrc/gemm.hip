@@ -33,15 +33,6 @@ constexpr int STAGES = 4;   // LDS ring: up to 3 k-tiles in flight while one is 
 // lanes 0-15) must use 4 distinct chunk columns: XOR with (row >> 2) & 3.
 __device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 2) & 3); }
 
-// Wait until the copies of the oldest in-flight k-tile are done: at most
-// `later` k-tiles (CPS copies each) issued after it may still be outstanding.
-template <int CPS>
-__device__ __forceinline__ void wait_dma_ktile(int later) {
-  if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPS) : "memory");
-  else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPS) : "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
 // Copy plan of one ROWS x 32 k-tile of a [rows_total, K] bf16 matrix into LDS
 // (row = 64 bytes; 16-byte chunk c of a row stored at swz(row, c)).  Each wave
 // instruction fills 16 tile rows (1 KB); lane l writes physical chunk l & 3 of
@@ -89,15 +80,15 @@ __device__ __forceinline__ void zero_k_tail(bf16_t* tile, int k0, int K, int tid
   }
 }
 
-// 8 waves; the block tile BM x BN is split WM x WN ways.
+// WM x WN waves split the block tile BM x BN.
 template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, int M, int K, int N,
     void* __restrict__ Y, int epi, bf16_t* __restrict__ Ybf, const uint8_t* __restrict__ rmask) {
-  static_assert(WM * WN == 8, "8 waves");
-  constexpr int CPS = DmaPlan<BM, 8>::PER + DmaPlan<BN, 8>::PER;  // copies per thread per k-tile
+  constexpr int NW = WM * WN;
+  constexpr int CPS = DmaPlan<BM, NW>::PER + DmaPlan<BN, NW>::PER;  // copies per thread per k-tile
   static_assert(STAGES == 4, "wait_dma_ktile assumes at most two later k-tiles in flight");
-  constexpr int NT = 512;
+  constexpr int NT = NW * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int STAGE_ELEMS = (BM + BN) * BK;
@@ -137,8 +128,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(
 
   const int nk = tile_live ? (K + BK - 1) / BK : 0;
   const bool k_tail = (K % BK) != 0;
-  DmaPlan<BM, 8> planA;
-  DmaPlan<BN, 8> planB;
+  DmaPlan<BM, NW> planA;
+  DmaPlan<BN, NW> planB;
   planA.init(X, M, K, m0, wave, lane);
   planB.init(W, N, K, n0, wave, lane);
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
@@ -186,43 +177,42 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(
     }
   }
 
-  // epilogue: lane holds Y[m][n .. n+3] for m = .. + (lane & 31), n = .. + 8*q + 4*g
+  // Epilogue through LDS: each wave parks 32 rows x WTN columns of its fp32
+  // accumulator at a time (row stride padded by 16 bytes: conflict-free for
+  // both the column-wise writes and the row-wise reads), then streams them out
+  // row-wise so every global access covers whole 16-byte-aligned row segments
+  // (WTN * 4 bytes per row for fp32, WTN * 2 for bf16) instead of 32 short
+  // pieces per instruction.
+  constexpr int EP_LD = WTN + 4;  // fp32 per parked row
+  static_assert(NW * 32 * EP_LD * 4 <= STAGES * STAGE_ELEMS * 2, "epilogue staging fits the ring");
+  __syncthreads();  // every wave is done reading the ring
+  float* park = (float*)smem + wave * (32 * EP_LD);
+  constexpr int LPR = WTN / 4;          // lanes per row (16 bytes of fp32 each)
+  constexpr int RPI = 64 / LPR;         // rows per wave instruction
+  const int prow = lane / LPR, pcol = (lane % LPR) * 4;
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
-    const int m = m0 + wm * WTM + j * 32 + r;
-    if (m >= M) continue;
-    const bool row_ok = rmask ? rmask[m] != 0 : true;
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WTN + i * 32 + 8 * q + 4 * g;
-        if (n >= N) continue;
-        float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
-        float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-        if (!row_ok) v0 = v1 = v2 = v3 = 0.f;
+      for (int q = 0; q < 4; ++q)
+        *(f32x4_t*)(park + r * EP_LD + i * 32 + 8 * q + 4 * g) =
+            f32x4_t{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    const int n = n0 + wn * WTN + pcol;
+#pragma unroll
+    for (int rr = 0; rr < 32; rr += RPI) {
+      const int m = m0 + wm * WTM + j * 32 + rr + prow;
+      f32x4_t v = *(const f32x4_t*)(park + (rr + prow) * EP_LD + pcol);
+      if (m < M && n < N) {
+        if (rmask && !rmask[m]) v = f32x4_t{0.f, 0.f, 0.f, 0.f};
         const int64_t off = (int64_t)m * N + n;
         if (epi == EPI_BF16) {
-          u32x2_t o;
-          o[0] = pack_bf16x2(v0, v1);
-          o[1] = pack_bf16x2(v2, v3);
-          *(u32x2_t*)((bf16_t*)Y + off) = o;
+          *(u32x2_t*)((bf16_t*)Y + off) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         } else {
           float* yp = (float*)Y + off;
-          if (epi == EPI_F32_ACC) {
-            const f32x4_t old = *(const f32x4_t*)yp;
-            v0 += old[0];
-            v1 += old[1];
-            v2 += old[2];
-            v3 += old[3];
-          }
-          *(f32x4_t*)yp = f32x4_t{v0, v1, v2, v3};
-          if (Ybf) {
-            u32x2_t o;
-            o[0] = pack_bf16x2(v0, v1);
-            o[1] = pack_bf16x2(v2, v3);
-            *(u32x2_t*)(Ybf + off) = o;
-          }
+          if (epi == EPI_F32_ACC) v += *(const f32x4_t*)yp;
+          *(f32x4_t*)yp = v;
+          if (Ybf) *(u32x2_t*)(Ybf + off) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
       }
     }
@@ -282,14 +272,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 namespace kalm {
 
+#ifndef KALM_GEMM_VARIANT
+#define KALM_GEMM_VARIANT 0
+#endif
+
 void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, void* Y, bool y_f32,
                         bool accumulate, bf16_t* Y_bf16, const uint8_t* rmask, hipStream_t s) {
   const int epi = !y_f32 ? EPI_BF16 : (accumulate ? EPI_F32_ACC : EPI_F32);
   const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles >= 512) {
     const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y, epi,
-                       Y_bf16, rmask);
+    if (KALM_GEMM_VARIANT == 1)
+      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 2>), dim3(tiles), dim3(256), 0, s, X, W, M, K, N, Y, epi,
+                         Y_bf16, rmask);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y, epi,
+                         Y_bf16, rmask);
   } else {  // small problems: more, smaller tiles to fill the 256 CUs
     const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y, epi,

@@ -67,6 +67,15 @@ __device__ __forceinline__ void dma16(uint64_t sbase, uint32_t voff, uint32_t ld
       : "memory");
 }
 
+// Wait until the copies of the oldest in-flight k-tile are done: at most
+// `later` k-tiles (CPS copies each) issued after it may still be outstanding.
+template <int CPS>
+__device__ __forceinline__ void wait_dma_ktile(int later) {
+  if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPS) : "memory");
+  else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPS) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // ---------------------------------------------------------------- host side
 namespace kalm {
 
