@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     ap.add_argument("--no-pool-long", action="store_true", help="skip the pooling measurement at the 1024x2560 shape")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (calibrates the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -153,6 +155,15 @@ def main():
               "passage shard independently); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
+    if a.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read_per_launch": src.numel() * 4,
+                          "copy_probe_bytes_written_per_launch": dst.numel() * 4, "launches": 5}), flush=True)
+        return
     from encoder_decoder_document_amd import ops, stack, synth
 
     names = [s.name for s in synth.SHAPES]

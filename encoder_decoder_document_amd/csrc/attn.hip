@@ -8,15 +8,16 @@
 // (running max m, running sum l, fp32 accumulator) that is carried across the
 // self/cross boundary -- a single pass, no second reduction.
 //
-// Work unit (one 512-thread workgroup, 8 waves): one pair, one KV head and
-// 8 slots of 32 decoder rows x one query head -- the query heads that share
-// the KV head packed with row blocks (4 heads x 64 rows for 4:1 grouping,
-// 2 x 128 for 2:1, 1 x 256 for 1:1) -- so every K/V tile staged in LDS serves
-// 256 query vectors.  That reuse sets the LDS-fill traffic per flop; each wave
-// keeps its Q fragments (32 rows x 256 dims) and fp32 O accumulator in
-// registers.  K and V tiles move global -> LDS with direct-to-LDS loads
-// through a 3-slot ring, two tiles in flight.
-//
+// Work unit (one workgroup of NW = 4 waves by default, or 8): one pair, one
+// KV head and NW slots of 32 decoder rows x one query head -- the query heads
+// that share the KV head packed with row blocks (4 heads x 32 rows for 4:1
+// grouping with 4 waves) -- so every K/V tile staged in LDS serves 32 * NW
+// query vectors.  Each wave keeps its Q fragments (32 rows x 256 dims) and its
+// fp32 O accumulator in registers (about 250 VGPRs, two waves per SIMD).  K
+// and V tiles move global -> LDS with direct-to-LDS loads through a ring of 2
+// (4 waves, 64 KB: two workgroups per CU, whose phases interleave on the
+// SIMDs and hide each other's prologue and epilogue) or 3 (8 waves, 96 KB).
+
 // MFMA mapping (v_mfma_f32_32x32x16_bf16, 64-wide waves):
 //   S^T[key, row]  = K . Q^T     A = K tile rows from LDS, B = Q fragments
 //   O^T[dim, row] += V^T . P^T   A = V^T from LDS (transposing reads), B = P
@@ -37,8 +38,10 @@ namespace {
 
 constexpr int HD = 256;          // head dim of the bf16 path
 constexpr int BKV = 32;          // keys per tile
-constexpr int RING = 3;          // K/V tiles resident in LDS (two in flight)
 constexpr float LAZY = 8.0f;     // lazy-rescale threshold, log2 units
+#ifndef ATTN_WAVES
+#define ATTN_WAVES 4             // waves per workgroup (4 or 8)
+#endif
 constexpr int MAX_CTILES = 128;  // cross tiles per passage (Cmax <= 4096): two mask words per lane
 
 // Physical 16-byte chunk of logical chunk c (0..31) in a K row (512 bytes).
@@ -64,25 +67,33 @@ __device__ __forceinline__ u32x2_t lds_tr_at(uint32_t addr) {
 // 16-byte LDS read at a byte address.
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 __device__ __forceinline__ bf16x8_t lds_read16(uint32_t addr) { return *(const lds_bf16x8_t*)(size_t)addr; }
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
+__device__ __forceinline__ u32x4_t lds_read16u(uint32_t addr) { return *(const lds_u32x4_t*)(size_t)addr; }
+__device__ __forceinline__ void lds_write8(uint32_t addr, u32x2_t v) { *(lds_u32x2_t*)(size_t)addr = v; }
 
-// One workgroup = 8 waves = 8 slots of 32 decoder rows x one query head
-// (NH heads x WPH row blocks).  Every K/V tile staged in LDS is shared by the
-// 256 (row, head) query vectors of the block -- the reuse that keeps the
-// kernel off the L2 bandwidth limit.  Each wave keeps its Q fragments (32 rows
-// x 256 dims) and its fp32 O accumulator in registers.  K and V tiles move
-// global -> LDS by DMA through a 3-slot ring (two tiles in flight).
-template <int NH>
-__global__ __launch_bounds__(512, 1) void merged_attn_bf16_kernel(
+// One workgroup = NW waves = NW slots of 32 decoder rows x one query head
+// (NH heads x WPH row blocks); every K/V tile staged in LDS is shared by the
+// 32 * NW (row, head) query vectors of the block.
+template <int NH, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
     const bf16_t* __restrict__ Q, int64_t q_ld, const bf16_t* __restrict__ Ks,
     const bf16_t* __restrict__ Vs, int64_t kv_ld, const int32_t* __restrict__ cu_q, int P,
     int64_t rows, int nqb, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     int64_t c_ld, const uint8_t* __restrict__ cmask, const int32_t* __restrict__ doc_of_pair,
     int D, int Cmax, int nq, int nkv, float scale_log2, bf16_t* __restrict__ O, int64_t o_ld,
     float* __restrict__ lse) {
-  constexpr int WPH = 8 / NH;   // row blocks per head
-  constexpr int RB = 32 * WPH;  // decoder rows per block
-  __shared__ __attribute__((aligned(1024))) bf16_t k_lds[RING][BKV * HD];  // K tiles, k_swz
-  __shared__ __attribute__((aligned(1024))) bf16_t v_lds[RING][BKV * HD];  // V tiles, v_swz
+  constexpr int WPH = NW / NH;            // row blocks per head
+  constexpr int RB = 32 * WPH;            // decoder rows per block
+#ifdef ATTN_RING
+  constexpr int RING = ATTN_RING;
+#else
+  constexpr int RING = NW == 8 ? 3 : 2;   // K/V tiles resident in LDS
+#endif
+  constexpr int RPW = BKV / NW;           // key rows each wave copies per tile
+  constexpr int TILE_B = BKV * HD * 2;    // bytes of one K (or V) tile
+  // K tiles (k_swz) in slots 0..RING-1, then V tiles (v_swz)
+  __shared__ __attribute__((aligned(1024))) uint8_t kv_lds[2 * RING * TILE_B];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, g = lane >> 5;
@@ -170,16 +181,16 @@ __global__ __launch_bounds__(512, 1) void merged_attn_bf16_kernel(
   const int64_t cdoc = (int64_t)(bad_doc ? 0 : doc) * Cmax * c_ld + (int64_t)kvh * HD;
   const uint64_t kc_base = (uint64_t)(uintptr_t)(Kc + cdoc);
   const uint64_t vc_base = (uint64_t)(uintptr_t)(Vc + cdoc);
-  const uint32_t klds0 = __builtin_amdgcn_readfirstlane(lds_addr(&k_lds[0][0]));
-  const uint32_t vlds0 = __builtin_amdgcn_readfirstlane(lds_addr(&v_lds[0][0]));
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(kv_lds));
+  const uint32_t klds0 = lds0, vlds0 = lds0 + RING * TILE_B;
   const uint32_t kv_ld2 = (uint32_t)kv_ld * 2u, c_ld2 = (uint32_t)c_ld * 2u;
 
-  // DMA plan: wave instruction j (of 2) fills key rows 2(2w+j), +1 (1 KB) of a
-  // tile; lane l writes physical chunk l & 31 of key row 2(2w+j) + (l >> 5)
-  const int dkey0 = 4 * wave + (lane >> 5);  // second row pair: dkey0 + 2
-  const int klc16_0 = k_swz(dkey0, lane & 31) * 16, klc16_1 = k_swz(dkey0 + 2, lane & 31) * 16;
-  const int vlc16_0 = v_swz(dkey0, lane & 31) * 16, vlc16_1 = v_swz(dkey0 + 2, lane & 31) * 16;
-  const uint32_t dslab = __builtin_amdgcn_readfirstlane(wave * 2 * 1024);
+  // DMA plan: wave w copies key rows RPW*w .. RPW*w + RPW-1 of a tile, two
+  // rows (1 KB) per instruction; in instruction j lane l writes physical
+  // chunk l & 31 of key row RPW*w + 2j + (l >> 5), i.e. logical chunk
+  // (l & 31) ^ swizzle(key) of that row
+  const int dkey0 = RPW * wave + (lane >> 5);
+  const uint32_t dslab = __builtin_amdgcn_readfirstlane(wave * RPW * (HD * 2));
 
   // copy tile v (K and V) into ring slot v % RING.  Key rows that do not
   // exist (past the pair / the passage) or are masked are fetched from a
@@ -192,16 +203,19 @@ __global__ __launch_bounds__(512, 1) void merged_attn_bf16_kernel(
     const uint64_t kba = self ? ks_base : kc_base;
     const uint64_t vba = self ? vs_base : vc_base;
     const uint32_t bits = self ? 0u : cm_word(v - n_st);
-    const uint32_t so = (uint32_t)((v % RING) * BKV * HD * 2) + dslab;
+    const uint32_t so = (uint32_t)((v % RING) * TILE_B) + dslab;
+    int key0 = dkey0;
+    asm volatile("" : "+v"(key0));  // recompute the per-row offsets here instead of holding them
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int key = dkey0 + 2 * j;
+    for (int j = 0; j < RPW / 2; ++j) {
+      const int key = key0 + 2 * j;
       int row;
       if (self) row = min(kb + key, Lq - 1);
       else row = ((bits >> key) & 1u) ? kb + key : donor;
       const uint32_t ro = (uint32_t)row * ld2;
-      dma16(kba, ro + (j ? klc16_1 : klc16_0), klds0 + so + j * 1024);
-      dma16(vba, ro + (j ? vlc16_1 : vlc16_0), vlds0 + so + j * 1024);
+      const int c = __lane_id() & 31;
+      dma16(kba, ro + (uint32_t)(k_swz(key, c) << 4), klds0 + so + j * 1024);
+      dma16(vba, ro + (uint32_t)(v_swz(key, c) << 4), vlds0 + so + j * 1024);
     }
   };
 
@@ -211,7 +225,7 @@ __global__ __launch_bounds__(512, 1) void merged_attn_bf16_kernel(
   // kx ^ 32s with one per-lane base kx (the XOR only touches bits 4..8, below
   // the 512-byte row and tile offsets).
   const int krow = (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1);
-  const uint32_t kx = lds_addr(&k_lds[0][0]) + krow * (HD * 2) + ((g ^ (krow & 15)) << 4);
+  const uint32_t kx = klds0 + krow * (HD * 2) + ((g ^ (krow & 15)) << 4);
   // V^T fragment reads (transposing, 8 bytes per lane): in 16-lane group
   // G = lane >> 4, lane i addresses key 8 * (G >> 1) + (i >> 2) (+4 for the
   // second read, +16 per k-step) at dims 16 * (G & 1) + 4 * (i & 3) of each
@@ -220,12 +234,12 @@ __global__ __launch_bounds__(512, 1) void merged_attn_bf16_kernel(
   const int vg = lane >> 4, vi = lane & 15;
   const int vkey = 8 * (vg >> 1) + (vi >> 2);
   const int vdim0 = 16 * (vg & 1) + 4 * (vi & 3);
-  const uint32_t vx = lds_addr(&v_lds[0][0]) + vkey * (HD * 2) + 64 * (vkey & 3) + 16 * (vdim0 >> 3) +
+  const uint32_t vx = vlds0 + vkey * (HD * 2) + 64 * (vkey & 3) + 16 * (vdim0 >> 3) +
                       2 * (vdim0 & 7);
 
   for (int v = 0; v < RING - 1 && v < n_tiles; ++v) issue(v);
   for (int v = 0; v < n_tiles; ++v) {
-    wait_dma_ktile<4>(min(n_tiles - 1 - v, RING - 2));
+    wait_dma_ktile<RPW>(min(n_tiles - 1 - v, RING - 2));  // RPW copies per tile: RPW/2 for K, RPW/2 for V
     __syncthreads();  // tile v visible; the slot of tile v-1 is free
     if (v + RING - 1 < n_tiles) issue(v + RING - 1);
     const bool self = v < n_st;
@@ -233,7 +247,7 @@ __global__ __launch_bounds__(512, 1) void merged_attn_bf16_kernel(
     // nothing to do: no valid rows in this wave, or a causal tile entirely
     // above its rows (the wave still joins every barrier and copy)
     if (qr0 >= Lq || (self && kb > wave_last)) continue;
-    const uint32_t slot = (uint32_t)((v % RING) * (BKV * HD * 2));
+    const uint32_t slot = (uint32_t)((v % RING) * TILE_B);
     uint32_t kt = kx + slot, vt = vx + slot;
     // opaque per tile: keeps the compiler from hoisting 24 precomputed
     // fragment addresses out of the loop (one XOR per read is cheaper than
@@ -244,20 +258,21 @@ __global__ __launch_bounds__(512, 1) void merged_attn_bf16_kernel(
     for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
     // K fragments in groups of KG k-steps, the next group read while the
     // current one multiplies (bounds the registers held by K fragments)
-    constexpr int KG = 2;
-    bf16x8_t kfa[KG], kfb[KG];
+#ifndef ATTN_KG
+#define ATTN_KG 4
+#endif
+    constexpr int KG = ATTN_KG;
+    bf16x8_t kf[HD / 16];
 #pragma unroll
-    for (int j = 0; j < KG; ++j) kfa[j] = lds_read16(kt ^ (32u * j));
+    for (int j = 0; j < KG; ++j) kf[j] = lds_read16(kt ^ (32u * j));
 #pragma unroll
     for (int s0 = 0; s0 < HD / 16; s0 += KG) {
       if (s0 + KG < HD / 16) {
 #pragma unroll
-        for (int j = 0; j < KG; ++j) kfb[j] = lds_read16(kt ^ (32u * (s0 + KG + j)));
+        for (int j = 0; j < KG; ++j) kf[s0 + KG + j] = lds_read16(kt ^ (32u * (s0 + KG + j)));
       }
 #pragma unroll
-      for (int j = 0; j < KG; ++j) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfa[j], qf[s0 + j], sacc, 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < KG; ++j) kfa[j] = kfb[j];
+      for (int j = 0; j < KG; ++j) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s0 + j], qf[s0 + j], sacc, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     // masking only for the causal diagonal / ragged self tiles and partial cross tiles
@@ -317,38 +332,55 @@ __global__ __launch_bounds__(512, 1) void merged_attn_bf16_kernel(
       a0 = u32x4_t{t0[0], t0[1], t1[0], t1[1]};
       a1 = u32x4_t{t2[0], t2[1], t3[0], t3[1]};
     };
-    u32x4_t va0, va1, vb0, vb1;
-    vread(0, va0, va1);
+    u32x4_t vf[HD / 32][2];
+    vread(0, vf[0][0], vf[0][1]);
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db) {
-      if (db + 1 < HD / 32) vread(db + 1, vb0, vb1);
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va0), pf0, oacc[db], 0, 0, 0);
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va1), pf1, oacc[db], 0, 0, 0);
-      va0 = vb0;
-      va1 = vb1;
+      if (db + 1 < HD / 32) vread(db + 1, vf[db + 1][0], vf[db + 1][1]);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[db][0]), pf0, oacc[db], 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[db][1]), pf1, oacc[db], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // ---- normalise and store
+  // ---- normalise and store.  The accumulator holds, per lane (r, g), dims
+  // 32 db + 8 q + 4 g + (0..3) of row r; it is staged through LDS (now free)
+  // so that the global stores write whole rows, 16 bytes per lane.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (i_loc < Lq) {
-    const float inv = bad_doc ? __builtin_nanf("") : 1.f / l_tot;
-    bf16_t* op = O + (row0 + i_loc) * o_ld + (int64_t)h * HD + 4 * g;
+  const float inv = bad_doc ? __builtin_nanf("") : 1.f / l_tot;
+  __syncthreads();  // every wave is done with the K/V ring
+  constexpr int DPP = NW == 4 ? HD : HD / 2;  // dims per pass: a wave stages 32 x DPP bf16 (16 or 8 KB)
+  constexpr int CPR = DPP / 8;                // 16-byte chunks per staged row
+  constexpr int RPI = 64 / CPR;               // rows per read-back instruction
+  const uint32_t ebase = lds0 + wave * (32 * DPP * 2);
+  bf16_t* orow0 = O + (row0 + qr0) * o_ld + (int64_t)h * HD;
 #pragma unroll
-    for (int db = 0; db < HD / 32; ++db)
+  for (int pass = 0; pass < HD / DPP; ++pass) {
+#pragma unroll
+    for (int db = 0; db < DPP / 32; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x16_t& a = oacc[db];
+        const f32x16_t& a = oacc[pass * (DPP / 32) + db];
         u32x2_t o;
         o[0] = pack_bf16x2(a[4 * q4 + 0] * inv, a[4 * q4 + 1] * inv);
         o[1] = pack_bf16x2(a[4 * q4 + 2] * inv, a[4 * q4 + 3] * inv);
-        *(u32x2_t*)(op + db * 32 + 8 * q4) = o;
+        const int c = (4 * db + q4) ^ (r & (CPR - 1));
+        lds_write8(ebase + r * (DPP * 2) + c * 16 + 8 * g, o);
       }
-    if (lse && g == 0)
-      lse[(row0 + i_loc) * nq + h] =
-          bad_doc ? __builtin_nanf("") : (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int rr = RPI * i + lane / CPR, c = lane % CPR;
+      const u32x4_t val = lds_read16u(ebase + rr * (DPP * 2) + ((c ^ (rr & (CPR - 1))) << 4));
+      if (qr0 + rr < Lq) *(u32x4_t*)(orow0 + rr * o_ld + pass * DPP + 8 * c) = val;
+    }
+    __builtin_amdgcn_wave_barrier();
   }
+  if (lse && g == 0 && i_loc < Lq)
+    lse[(row0 + i_loc) * nq + h] =
+        bad_doc ? __builtin_nanf("") : (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f;
 }
 
 // fp32 path (the small fp32 workload): one wavefront per (pair, head, row),
@@ -429,23 +461,24 @@ void launch_merged_attn_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, co
                              const bf16_t* Kc, const bf16_t* Vc, int64_t c_ld, const uint8_t* cmask,
                              const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv, float scale,
                              bf16_t* O, int64_t o_ld, float* lse, hipStream_t s) {
+  constexpr int NW = ATTN_WAVES;
   const int G = nq / nkv;
   const int NH = G >= 4 ? 4 : G;  // heads per block (G is 1, 2 or a multiple of 4)
-  const int RB = 32 * (8 / NH);
+  const int RB = 32 * (NW / NH);
   const int nqb = (max_lq + RB - 1) / RB;
   const int64_t blocks = (int64_t)P * nkv * (G / NH) * nqb;
   const float sl2 = scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)blocks), block(512);
+  const dim3 grid((unsigned)blocks), block(NW * 64);
   if (blocks == 0) return;
   if (NH == 4)
-    hipLaunchKernelGGL(merged_attn_bf16_kernel<4>, grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, P, rows, nqb,
-                       Kc, Vc, c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, sl2, O, o_ld, lse);
+    hipLaunchKernelGGL((merged_attn_bf16_kernel<4, NW>), grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, P, rows,
+                       nqb, Kc, Vc, c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, sl2, O, o_ld, lse);
   else if (NH == 2)
-    hipLaunchKernelGGL(merged_attn_bf16_kernel<2>, grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, P, rows, nqb,
-                       Kc, Vc, c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, sl2, O, o_ld, lse);
+    hipLaunchKernelGGL((merged_attn_bf16_kernel<2, NW>), grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, P, rows,
+                       nqb, Kc, Vc, c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, sl2, O, o_ld, lse);
   else
-    hipLaunchKernelGGL(merged_attn_bf16_kernel<1>, grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, P, rows, nqb,
-                       Kc, Vc, c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, sl2, O, o_ld, lse);
+    hipLaunchKernelGGL((merged_attn_bf16_kernel<1, NW>), grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, P, rows,
+                       nqb, Kc, Vc, c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, sl2, O, o_ld, lse);
 }
 
 void launch_merged_attn_f32(const float* Q, int64_t q_ld, const float* Ks, const float* Vs,

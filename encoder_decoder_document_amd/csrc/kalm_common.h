@@ -71,7 +71,8 @@ __device__ __forceinline__ void dma16(uint64_t sbase, uint32_t voff, uint32_t ld
 // `later` k-tiles (CPS copies each) issued after it may still be outstanding.
 template <int CPS>
 __device__ __forceinline__ void wait_dma_ktile(int later) {
-  if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPS) : "memory");
+  if (later >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * CPS) : "memory");
+  else if (later == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPS) : "memory");
   else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPS) : "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
