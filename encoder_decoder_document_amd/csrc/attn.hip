@@ -42,7 +42,7 @@ constexpr float LAZY = 8.0f;     // lazy-rescale threshold, log2 units
 #ifndef ATTN_WAVES
 #define ATTN_WAVES 4             // waves per workgroup (4 or 8)
 #endif
-constexpr int MAX_CTILES = 128;  // cross tiles per passage (Cmax <= 4096): two mask words per lane
+
 
 // Physical 16-byte chunk of logical chunk c (0..31) in a K row (512 bytes).
 // The S product reads 16 keys at one logical chunk per 16-lane phase over 64

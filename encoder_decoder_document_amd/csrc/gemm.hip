@@ -6,14 +6,16 @@
 // layout the gfx950 v_mfma_f32_32x32x16_bf16 fragments want: every lane reads 8
 // consecutive k values of one row.
 //
-// Block tile BM x BN, k in steps of 32, 512 threads (8 waves, two per SIMD),
+// Block tile BM x BN, k in steps of BK (32 or 64), 512 threads (8 waves),
 // each wave a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  The MFMA "A" operand is
 // the weight tile and the "B" operand the activation tile, so each lane's
 // accumulator holds 4 consecutive output columns of one output row and the
 // epilogue writes 8-byte (bf16) or 16-byte (fp32) vectors.  Tiles move from
 // global memory straight into LDS with the gfx950 global_load_lds_dwordx4 copy
-// (no staging registers) through a 4-slot LDS ring: three k-tiles are in flight
-// while the fourth feeds the MFMAs, one barrier per k-tile.  16-byte k-chunks are stored XOR-swizzled
+// (no staging registers) through an LDS ring of STAGES k-tiles, one barrier
+// per k-tile.  With BK = 64 every copied row is one whole 128-byte line, which
+// halves the L1 -> L2 requests per byte (the k-loop is bound by the requests
+// in flight per CU, not by L2 bandwidth).  16-byte k-chunks are stored XOR-swizzled
 // (see swz), chosen through the address each lane fetches, so the fragment
 // reads of 32 consecutive rows are bank-conflict free.  Workgroups are
 // remapped so that each XCD walks a contiguous range of output tiles (the
@@ -24,40 +26,46 @@ namespace {
 
 enum Epi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_ACC = 2 };
 
-constexpr int BK = 32;      // k per pipeline stage: a 64-byte row of 4 16-byte chunks
-constexpr int STAGES = 4;   // LDS ring: up to 3 k-tiles in flight while one is consumed
+// Physical 16-byte chunk of logical chunk c in row `row` of a k-tile whose
+// rows are BK bf16 (64 or 128 bytes).  The gfx950 LDS serves a ds_read_b128
+// 16 lanes at a time across 64 banks (256 bytes); the fragment reads of 16
+// consecutive rows at one logical chunk must hit 16 distinct 16-byte bank
+// groups.  BK = 32: 4 rows share 256 bytes, XOR with (row >> 2) & 3; BK = 64:
+// 2 rows share 256 bytes, XOR with (row >> 1) & 7.
+template <int BK>
+__device__ __forceinline__ int swz(int row, int c) {
+  if constexpr (BK == 32) return c ^ ((row >> 2) & 3);
+  else return c ^ ((row >> 1) & 7);
+}
 
-// Physical 16-byte chunk of logical chunk c (0..3) in tile row `row`.  The
-// gfx950 LDS serves a ds_read_b128 16 lanes at a time across 64 banks (256
-// bytes = 4 rows of 64 bytes), so rows r, r+4, r+8, r+12 (read together by
-// lanes 0-15) must use 4 distinct chunk columns: XOR with (row >> 2) & 3.
-__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 2) & 3); }
-
-// Copy plan of one ROWS x 32 k-tile of a [rows_total, K] bf16 matrix into LDS
-// (row = 64 bytes; 16-byte chunk c of a row stored at swz(row, c)).  Each wave
-// instruction fills 16 tile rows (1 KB); lane l writes physical chunk l & 3 of
-// row l >> 2, so it fetches the logical chunk that belongs there -- the XOR
-// swizzle is applied through the global address.  Addresses are a scalar
+// Copy plan of one ROWS x BK k-tile of a [rows_total, K] bf16 matrix into LDS
+// (16-byte chunk c of a row stored at swz(row, c)).  Each wave instruction
+// fills 1 KB = 1024 / (2 BK) tile rows; lane l writes physical chunk l % CPR of
+// row l / CPR (CPR = chunks per row), so it fetches the logical chunk that
+// belongs there -- the XOR swizzle is applied through the global address, and
+// with BK = 64 every row is one whole 128-byte line.  Addresses are a scalar
 // 64-bit tile base plus a 32-bit per-lane byte offset; rows past the matrix
 // end are clamped to its last row (their products are discarded).
-template <int ROWS, int NWAVES>
+template <int ROWS, int NWAVES, int BK>
 struct DmaPlan {
-  static constexpr int PER = ROWS / 16 / NWAVES;  // instructions per wave per stage
-  uint64_t base;                                  // byte address of the tile's first row (uniform)
-  uint32_t row_off[PER];                          // byte offset of this lane's source rows
-  uint32_t slab[PER];                             // LDS byte offset of each 1 KB slab (uniform)
-  int lc8[PER];                                   // k offset of this lane's chunk in a k-tile
+  static constexpr int CPR = BK / 8;                    // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;                  // rows per instruction
+  static constexpr int PER = ROWS / RPI / NWAVES;       // instructions per wave per stage
+  uint64_t base;                                        // byte address of the tile's first row (uniform)
+  uint32_t row_off[PER];                                // byte offset of this lane's source rows
+  uint32_t slab[PER];                                   // LDS byte offset of each 1 KB slab (uniform)
+  int lc8[PER];                                         // k offset of this lane's chunk in a k-tile
 
   __device__ __forceinline__ void init(const bf16_t* G, int rows_total, int K, int r0, int wave, int lane) {
-    const int rr = lane >> 2;
+    const int rr = lane / CPR;
     base = (uint64_t)(uintptr_t)(G + (int64_t)r0 * K);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const int R0 = 16 * (wave * PER + j);
+      const int R0 = RPI * (wave * PER + j);
       const int row = min(r0 + R0 + rr, rows_total - 1) - r0;
-      lc8[j] = swz(R0 + rr, lane & 3) * 8;  // the swizzle is an involution
+      lc8[j] = swz<BK>(R0 + rr, lane % CPR) * 8;  // the swizzle is an involution
       row_off[j] = (uint32_t)row * (uint32_t)K * 2u;
-      slab[j] = (uint32_t)__builtin_amdgcn_readfirstlane(R0 * 64);
+      slab[j] = (uint32_t)__builtin_amdgcn_readfirstlane(R0 * BK * 2);
     }
   }
   // k-tile starting at k0 into the tile at LDS byte address tile_lds
@@ -72,22 +80,25 @@ struct DmaPlan {
 };
 
 // Zero the 16-byte chunks of a staged tile that lie beyond K (last k-tile only).
-template <int ROWS>
+template <int ROWS, int BK>
 __device__ __forceinline__ void zero_k_tail(bf16_t* tile, int k0, int K, int tid, int nthreads) {
-  for (int e = tid; e < ROWS * 4; e += nthreads) {
-    const int row = e >> 2, pc = e & 3, lc = swz(row, pc);
+  constexpr int CPR = BK / 8;
+  for (int e = tid; e < ROWS * CPR; e += nthreads) {
+    const int row = e / CPR, pc = e % CPR, lc = swz<BK>(row, pc);
     if (k0 + lc * 8 >= K) *(u32x4_t*)(tile + row * BK + pc * 8) = u32x4_t{0, 0, 0, 0};
   }
 }
 
-// WM x WN waves split the block tile BM x BN.
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(
+// WM x WN waves split the block tile BM x BN; k advances BK per stage and
+// STAGES k-tiles live in the LDS ring (STAGES - 1 in flight while one feeds
+// the MFMAs); OCC = waves per SIMD it is built for (bounds the registers).
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int OCC>
+__global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, int M, int K, int N,
     void* __restrict__ Y, int epi, bf16_t* __restrict__ Ybf, const uint8_t* __restrict__ rmask) {
   constexpr int NW = WM * WN;
-  constexpr int CPS = DmaPlan<BM, NW>::PER + DmaPlan<BN, NW>::PER;  // copies per thread per k-tile
-  static_assert(STAGES == 4, "wait_dma_ktile assumes at most two later k-tiles in flight");
+  constexpr int CPS = DmaPlan<BM, NW, BK>::PER + DmaPlan<BN, NW, BK>::PER;  // copies per thread per k-tile
+  static_assert(STAGES >= 2 && STAGES <= 5, "wait_dma_ktile handles at most three later k-tiles in flight");
   constexpr int NT = NW * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -128,8 +139,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(
 
   const int nk = tile_live ? (K + BK - 1) / BK : 0;
   const bool k_tail = (K % BK) != 0;
-  DmaPlan<BM, NW> planA;
-  DmaPlan<BN, NW> planB;
+  DmaPlan<BM, NW, BK> planA;
+  DmaPlan<BN, NW, BK> planB;
   planA.init(X, M, K, m0, wave, lane);
   planB.init(W, N, K, n0, wave, lane);
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
@@ -148,8 +159,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(
     __syncthreads();  // k-tile kt visible to all waves; slot of k-tile kt-1 free
     bf16_t* cur = smem + (kt % STAGES) * STAGE_ELEMS;
     if (k_tail && kt == nk - 1) {
-      zero_k_tail<BM>(cur, kt * BK, K, tid, NT);
-      zero_k_tail<BN>(cur + BM * BK, kt * BK, K, tid, NT);
+      zero_k_tail<BM, BK>(cur, kt * BK, K, tid, NT);
+      zero_k_tail<BN, BK>(cur + BM * BK, kt * BK, K, tid, NT);
       __syncthreads();
     }
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
@@ -162,12 +173,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
         const int row = wm * WTM + j * 32 + r;
-        xf[j] = *(const bf16x8_t*)(a + row * BK + (swz(row, kc) << 3));
+        xf[j] = *(const bf16x8_t*)(a + row * BK + (swz<BK>(row, kc) << 3));
       }
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
         const int row = wn * WTN + i * 32 + r;
-        wf[i] = *(const bf16x8_t*)(bb + row * BK + (swz(row, kc) << 3));
+        wf[i] = *(const bf16x8_t*)(bb + row * BK + (swz<BK>(row, kc) << 3));
       }
 #pragma unroll
       for (int i = 0; i < FN; ++i)
@@ -272,26 +283,25 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 namespace kalm {
 
-#ifndef KALM_GEMM_VARIANT
-#define KALM_GEMM_VARIANT 0
-#endif
-
 void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, void* Y, bool y_f32,
                         bool accumulate, bf16_t* Y_bf16, const uint8_t* rmask, hipStream_t s) {
   const int epi = !y_f32 ? EPI_BF16 : (accumulate ? EPI_F32_ACC : EPI_F32);
   const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles >= 512) {
+  if (big_tiles >= 512 && epi == EPI_F32_ACC) {
+    // residual update (reads and writes the fp32 stream): 128 x 128 tiles,
+    // two workgroups per CU, so one's epilogue traffic overlaps the other's k-loop
+    const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 64, 2, 4>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y,
+                       epi, Y_bf16, rmask);
+  } else if (big_tiles >= 512) {
+    // 256 x 256 tiles, k-tiles of 64 (every copied row a whole 128-byte line), two-slot ring
     const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    if (KALM_GEMM_VARIANT == 1)
-      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 2>), dim3(tiles), dim3(256), 0, s, X, W, M, K, N, Y, epi,
-                         Y_bf16, rmask);
-    else
-      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y, epi,
-                         Y_bf16, rmask);
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 64, 2, 1>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y,
+                       epi, Y_bf16, rmask);
   } else {  // small problems: more, smaller tiles to fill the 256 CUs
     const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y, epi,
-                       Y_bf16, rmask);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 32, 4, 1>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y,
+                       epi, Y_bf16, rmask);
   }
 }
 
