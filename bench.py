@@ -103,31 +103,50 @@ class EventRec:
 
 
 def work_model(inp, sh):
-    """Algorithmic work per launch of each kernel (flops or bytes)."""
+    """Algorithmic work per launch of each recorded call (flops and bytes).
+
+    Names follow the step: the full-size projections and attention of the
+    middle layers, the first layer (Q/K/V once per query row, attention over
+    shared rows) and the last layer (final rows only)."""
     D, T, H, nq, nkv, d = sh.n_docs, sh.T, sh.H, sh.nq, sh.nkv, sh.d
     lq = np.asarray(inp["lq"], dtype=np.int64)
     dl = np.asarray(inp["doc_len"], dtype=np.int64)
     C = -(-dl // sh.chunk)                    # valid chunks per passage (right padding)
     Cmax = -(-T // sh.chunk)
     e = 2 if sh.dtype == "bf16" else 4
-    rows = int(D * lq.sum())
-    kv = nkv * d
-    # attention: useful causal-halved flops, sum over pairs
-    self_f = (lq * (lq + 1) // 2).sum() * D
-    cross_f = lq.sum() * C.sum()
-    attn_flops = 4 * nq * d * (self_f + cross_f)
-    attn_bytes = (2 * rows * nq * d + 2 * rows * kv + 2 * int(C.sum()) * kv) * e
+    rows = int(D * lq.sum())                  # decoder rows of all pairs
+    U = int(lq.sum())                         # decoder rows of the queries themselves
+    P = sh.pairs
+    qd, kv = nq * d, nkv * d
+    nqkv = qd + 2 * kv
+    self_keys = int((lq * (lq + 1) // 2).sum()) * D     # causal (row, key) pairs over all pairs
+    cross_keys = int(lq.sum()) * int(C.sum())            # (row, chunk) pairs over all pairs
+    attn_flops = 4 * nq * d * (self_keys + cross_keys)
+    self_bytes = 2 * rows * kv * e                       # self K and V, once
+    cross_bytes = 2 * int(C.sum()) * kv * e
+    last_flops = 4 * nq * d * (int(lq.sum()) * D + len(lq) * int(C.sum()))  # final row: Lq self + C cross keys
+
+    def linear(M, K, N, out_bytes):
+        return dict(flops=2.0 * M * K * N, bytes=float(M * K * e + N * K * e + out_bytes))
+
     return {
-        "merged_attn": dict(flops=float(attn_flops), bytes=float(attn_bytes)),
-        "qkv_linear": dict(flops=2.0 * rows * H * (nq * d + 2 * kv),
-                           bytes=float(rows * H * e + rows * (nq * d + 2 * kv) * e)),
-        "o_linear": dict(flops=2.0 * rows * nq * d * H,
-                         bytes=float(rows * nq * d * e + rows * H * 4 * 2 + rows * H * e)),
+        "merged_attn": dict(flops=float(attn_flops), bytes=float(2 * rows * qd * e + self_bytes + cross_bytes)),
+        "merged_attn_first": dict(flops=float(attn_flops),
+                                  bytes=float(U * qd * e + rows * qd * e + 2 * U * kv * e + cross_bytes)),
+        "merged_attn_last": dict(flops=float(last_flops), bytes=float(2 * P * qd * e + self_bytes + cross_bytes)),
+        "qkv_linear": linear(rows, H, nqkv, rows * nqkv * e),
+        "qkv_linear_first": linear(U, H, nqkv, U * nqkv * e),
+        "kv_linear_last": linear(rows, H, 2 * kv, rows * 2 * kv * e),
+        "q_linear_last": linear(P, H, qd, P * qd * e),
+        # residual update: read and write the fp32 stream, write its bf16 copy
+        "o_linear": linear(rows, qd, H, rows * H * (4 + 4 + (2 if e == 2 else 0))),
+        "o_linear_last": linear(P, qd, H, P * H * 8),
         "cross_kv": dict(flops=2.0 * int(C.sum()) * H * 2 * kv, bytes=float(D * Cmax * (H + 2 * kv) * e)),
         "chunk_pool": dict(flops=0.0, bytes=float(int(dl.sum()) * H * e + D * Cmax * H * e + D * T + D * Cmax + 4 * D)),
-        # source rows are the queries' first hidden states (read once), every
-        # decoder row is written in fp32 and bf16
-        "gather_rows": dict(flops=0.0, bytes=float(int(lq.sum()) * H * 4 + rows * H * (4 + 2))),
+        # residual start: the queries' first hidden states read once, every pair row written fp32 + bf16
+        "gather_rows": dict(flops=0.0, bytes=float(U * H * 4 + rows * H * (4 + (2 if e == 2 else 0)))),
+        "gather_query_rows": dict(flops=0.0, bytes=float(U * H * (4 + 4 + 2))),
+        "gather_final_rows": dict(flops=0.0, bytes=float(P * H * (4 + 4 + 2))),
     }
 
 

@@ -72,17 +72,50 @@ typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
 __device__ __forceinline__ u32x4_t lds_read16u(uint32_t addr) { return *(const lds_u32x4_t*)(size_t)addr; }
 __device__ __forceinline__ void lds_write8(uint32_t addr, u32x2_t v) { *(lds_u32x2_t*)(size_t)addr = v; }
 
+// Row spaces of one pair.  The pair's self keys are Lq = cu_q[p+1] - cu_q[p]
+// decoder positions; the query rows handled are positions pos0 .. pos0+nrow-1.
+//   mode 0 (all rows):   Q, self K/V and O rows start at cu_q[p];
+//   mode 1 (final row):  one query row per pair, position Lq-1; Q and O row p
+//                        (self K/V rows still start at cu_q[p]);
+//   mode 2 (shared):     Q and self K/V are the rows of the pair's query
+//                        (p / D), shared by all its D passages, at cu_q[qD]/D;
+//                        O rows start at cu_q[p].
+// A pair whose rows fall outside the given row counts is skipped (no access).
+struct PairRows {
+  int64_t kv0, q0, o0;
+  int Lq, nrow, pos0;
+  bool ok;
+};
+__device__ __forceinline__ PairRows pair_rows(const int32_t* __restrict__ cu_q, int p, int D, int mode,
+                                              int64_t q_rows, int64_t kv_rows, int64_t o_rows) {
+  PairRows pr;
+  const int64_t c0 = cu_q[p];
+  pr.Lq = (int)((int64_t)cu_q[p + 1] - c0);
+  pr.kv0 = pr.q0 = pr.o0 = c0;
+  if (mode == 2) {
+    const int64_t qs = (int64_t)cu_q[(int64_t)(p / D) * D] / D;
+    pr.kv0 = pr.q0 = qs;
+  } else if (mode == 1) {
+    pr.q0 = pr.o0 = p;
+  }
+  pr.nrow = mode == 1 ? (pr.Lq > 0 ? 1 : 0) : pr.Lq;
+  pr.pos0 = mode == 1 ? pr.Lq - 1 : 0;
+  pr.ok = c0 >= 0 && pr.Lq >= 0 && pr.kv0 >= 0 && pr.kv0 + pr.Lq <= kv_rows && pr.q0 >= 0 &&
+          pr.q0 + pr.nrow <= q_rows && pr.o0 >= 0 && pr.o0 + pr.nrow <= o_rows;
+  return pr;
+}
+
 // One workgroup = NW waves = NW slots of 32 decoder rows x one query head
 // (NH heads x WPH row blocks); every K/V tile staged in LDS is shared by the
 // 32 * NW (row, head) query vectors of the block.
-template <int NH, int NW>
+template <int NH, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
     const bf16_t* __restrict__ Q, int64_t q_ld, const bf16_t* __restrict__ Ks,
     const bf16_t* __restrict__ Vs, int64_t kv_ld, const int32_t* __restrict__ cu_q, int P,
-    int64_t rows, int nqb, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
-    int64_t c_ld, const uint8_t* __restrict__ cmask, const int32_t* __restrict__ doc_of_pair,
-    int D, int Cmax, int nq, int nkv, float scale_log2, bf16_t* __restrict__ O, int64_t o_ld,
-    float* __restrict__ lse) {
+    int64_t q_rows, int64_t kv_rows, int64_t o_rows, int nqb, const bf16_t* __restrict__ Kc,
+    const bf16_t* __restrict__ Vc, int64_t c_ld, const uint8_t* __restrict__ cmask,
+    const int32_t* __restrict__ doc_of_pair, int D, int Cmax, int nq, int nkv, float scale_log2,
+    bf16_t* __restrict__ O, int64_t o_ld, float* __restrict__ lse) {
   constexpr int WPH = NW / NH;            // row blocks per head
   constexpr int RB = 32 * WPH;            // decoder rows per block
 #ifdef ATTN_RING
@@ -113,11 +146,9 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
   const int hgi = (int)(rem / nqb);
   const int kvh = hgi / HG, hg = hgi % HG;
 
-  const int64_t row0 = cu_q[p];
-  int Lq = cu_q[p + 1] - (int)row0;
-  if (row0 < 0 || row0 >= rows || Lq < 0) Lq = 0;
-  else if (row0 + Lq > rows) Lq = (int)(rows - row0);
-  if (qb * RB >= Lq) return;
+  const PairRows pr = pair_rows(cu_q, p, D, MODE, q_rows, kv_rows, o_rows);
+  if (!pr.ok || qb * RB >= pr.nrow) return;
+  const int Lq = pr.Lq, nrow = pr.nrow, pos0 = pr.pos0;
   const int doc = doc_of_pair[p];
   const bool bad_doc = doc < 0 || doc >= D;
 
@@ -152,15 +183,16 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
   }
 
   const int h = kvh * G + hg * NH + wave / WPH;
-  const int qr0 = qb * RB + (wave % WPH) * 32;  // first decoder row of this wave
-  const int i_loc = qr0 + r;                     // this lane's decoder row (pair-local)
-  const int i_ld = min(i_loc, Lq - 1);
-  const int wave_last = min(qr0 + 31, Lq - 1);
+  const int qr0 = qb * RB + (wave % WPH) * 32;  // first handled query row of this wave
+  const int j_loc = qr0 + r;                     // this lane's handled row
+  const int j_ld = min(j_loc, nrow - 1);
+  const int pos = pos0 + j_ld;                   // its self position: sees self keys 0..pos
+  const int wave_first = pos0 + qr0, wave_last = pos0 + min(qr0 + 31, nrow - 1);
 
   // Q fragments (MFMA B operand of S^T = K Q^T): 16 k-steps of 16 dims
   bf16x8_t qf[HD / 16];
   {
-    const bf16_t* qp = Q + (row0 + i_ld) * q_ld + (int64_t)h * HD + 8 * g;
+    const bf16_t* qp = Q + (pr.q0 + j_ld) * q_ld + (int64_t)h * HD + 8 * g;
 #pragma unroll
     for (int s = 0; s < HD / 16; ++s) qf[s] = *(const bf16x8_t*)(qp + 16 * s);
   }
@@ -172,12 +204,12 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int n_self = min(Lq, qb * RB + RB);  // causal keys the block needs
+  const int n_self = min(Lq, pos0 + min(nrow, qb * RB + RB));  // causal keys the block needs
   const int n_st = (n_self + BKV - 1) / BKV;
   const int n_tiles = n_st + n_ct;
   // byte addresses of key 0 of this pair (self) / chunk 0 of this passage (cross), head kvh
-  const uint64_t ks_base = (uint64_t)(uintptr_t)(Ks + row0 * kv_ld + (int64_t)kvh * HD);
-  const uint64_t vs_base = (uint64_t)(uintptr_t)(Vs + row0 * kv_ld + (int64_t)kvh * HD);
+  const uint64_t ks_base = (uint64_t)(uintptr_t)(Ks + pr.kv0 * kv_ld + (int64_t)kvh * HD);
+  const uint64_t vs_base = (uint64_t)(uintptr_t)(Vs + pr.kv0 * kv_ld + (int64_t)kvh * HD);
   const int64_t cdoc = (int64_t)(bad_doc ? 0 : doc) * Cmax * c_ld + (int64_t)kvh * HD;
   const uint64_t kc_base = (uint64_t)(uintptr_t)(Kc + cdoc);
   const uint64_t vc_base = (uint64_t)(uintptr_t)(Vc + cdoc);
@@ -246,7 +278,7 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
     const int kb = self ? v * BKV : (v - n_st) * BKV;
     // nothing to do: no valid rows in this wave, or a causal tile entirely
     // above its rows (the wave still joins every barrier and copy)
-    if (qr0 >= Lq || (self && kb > wave_last)) continue;
+    if (qr0 >= nrow || (self && kb > wave_last)) continue;
     const uint32_t slot = (uint32_t)((v % RING) * TILE_B);
     uint32_t kt = kx + slot, vt = vx + slot;
     // opaque per tile: keeps the compiler from hoisting 24 precomputed
@@ -277,10 +309,10 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
     }
     // masking only for the causal diagonal / ragged self tiles and partial cross tiles
     const uint32_t bits = self ? 0u : cm_word(v - n_st);
-    const bool full = self ? (kb + BKV - 1 <= qr0 && kb + BKV <= Lq) : (bits == 0xffffffffu);
+    const bool full = self ? (kb + BKV - 1 <= wave_first && kb + BKV <= Lq) : (bits == 0xffffffffu);
     if (!full) {
       if (self) {
-        const int kmax = min(i_loc, Lq - 1) - kb - 8 * g;  // slot key offsets are 8g + const
+        const int kmax = pos - kb - 8 * g;  // slot key offsets are 8g + const
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int c = e < 8 ? e : e + 8;
@@ -353,7 +385,7 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
   constexpr int CPR = DPP / 8;                // 16-byte chunks per staged row
   constexpr int RPI = 64 / CPR;               // rows per read-back instruction
   const uint32_t ebase = lds0 + wave * (32 * DPP * 2);
-  bf16_t* orow0 = O + (row0 + qr0) * o_ld + (int64_t)h * HD;
+  bf16_t* orow0 = O + (pr.o0 + qr0) * o_ld + (int64_t)h * HD;
 #pragma unroll
   for (int pass = 0; pass < HD / DPP; ++pass) {
 #pragma unroll
@@ -374,12 +406,12 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
     for (int i = 0; i < 32 / RPI; ++i) {
       const int rr = RPI * i + lane / CPR, c = lane % CPR;
       const u32x4_t val = lds_read16u(ebase + rr * (DPP * 2) + ((c ^ (rr & (CPR - 1))) << 4));
-      if (qr0 + rr < Lq) *(u32x4_t*)(orow0 + rr * o_ld + pass * DPP + 8 * c) = val;
+      if (qr0 + rr < nrow) *(u32x4_t*)(orow0 + rr * o_ld + pass * DPP + 8 * c) = val;
     }
     __builtin_amdgcn_wave_barrier();
   }
-  if (lse && g == 0 && i_loc < Lq)
-    lse[(row0 + i_loc) * nq + h] =
+  if (lse && g == 0 && j_loc < nrow)
+    lse[(pr.o0 + j_loc) * nq + h] =
         bad_doc ? __builtin_nanf("") : (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f;
 }
 
@@ -388,8 +420,8 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
 // causal self keys and then the valid cross keys.
 __global__ __launch_bounds__(256) void merged_attn_f32_kernel(
     const float* __restrict__ Q, int64_t q_ld, const float* __restrict__ Ks,
-    const float* __restrict__ Vs, int64_t kv_ld, const int32_t* __restrict__ cu_q, int64_t rows,
-    const float* __restrict__ Kc, const float* __restrict__ Vc, int64_t c_ld,
+    const float* __restrict__ Vs, int64_t kv_ld, const int32_t* __restrict__ cu_q, int64_t q_rows,
+    int64_t kv_rows, int64_t o_rows, int mode, const float* __restrict__ Kc, const float* __restrict__ Vc, int64_t c_ld,
     const uint8_t* __restrict__ cmask, const int32_t* __restrict__ doc_of_pair, int D, int Cmax,
     int nq, int nkv, int d, float scale, float* __restrict__ O, int64_t o_ld,
     float* __restrict__ lse, int nrb) {
@@ -398,11 +430,9 @@ __global__ __launch_bounds__(256) void merged_attn_f32_kernel(
   const int i = (int)(blk % nrb) * 4 + (threadIdx.x >> 6);
   const int h = (int)((blk / nrb) % nq);
   const int p = (int)(blk / ((int64_t)nrb * nq));
-  const int64_t row0 = cu_q[p];
-  int Lq = cu_q[p + 1] - (int)row0;
-  if (row0 < 0 || row0 >= rows || Lq < 0) Lq = 0;
-  else if (row0 + Lq > rows) Lq = (int)(rows - row0);
-  if (i >= Lq) return;
+  const PairRows pr = pair_rows(cu_q, p, D, mode, q_rows, kv_rows, o_rows);
+  if (!pr.ok || i >= pr.nrow) return;
+  const int pos = pr.pos0 + i;  // self position of this query row
   const int kvh = h / (nq / nkv);
   const int doc = doc_of_pair[p];
   const bool bad_doc = doc < 0 || doc >= D;
@@ -412,7 +442,7 @@ __global__ __launch_bounds__(256) void merged_attn_f32_kernel(
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
     const int e = lane + 64 * j;
-    q[j] = (j < nj && e < d) ? Q[(row0 + i) * q_ld + (int64_t)h * d + e] : 0.f;
+    q[j] = (j < nj && e < d) ? Q[(pr.q0 + i) * q_ld + (int64_t)h * d + e] : 0.f;
     acc[j] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
@@ -436,8 +466,8 @@ __global__ __launch_bounds__(256) void merged_attn_f32_kernel(
     }
     m = m_new;
   };
-  for (int jk = 0; jk <= i; ++jk)
-    visit(Ks + (row0 + jk) * kv_ld + (int64_t)kvh * d, Vs + (row0 + jk) * kv_ld + (int64_t)kvh * d);
+  for (int jk = 0; jk <= pos; ++jk)
+    visit(Ks + (pr.kv0 + jk) * kv_ld + (int64_t)kvh * d, Vs + (pr.kv0 + jk) * kv_ld + (int64_t)kvh * d);
   if (!bad_doc)
     for (int c = 0; c < Cmax; ++c)
       if (cmask[(int64_t)doc * Cmax + c])
@@ -447,9 +477,9 @@ __global__ __launch_bounds__(256) void merged_attn_f32_kernel(
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
     const int e = lane + 64 * j;
-    if (j < nj && e < d) O[(row0 + i) * o_ld + (int64_t)h * d + e] = acc[j] * inv;
+    if (j < nj && e < d) O[(pr.o0 + i) * o_ld + (int64_t)h * d + e] = acc[j] * inv;
   }
-  if (lse && lane == 0) lse[(row0 + i) * nq + h] = bad_doc ? __builtin_nanf("") : m + logf(l);
+  if (lse && lane == 0) lse[(pr.o0 + i) * nq + h] = bad_doc ? __builtin_nanf("") : m + logf(l);
 }
 
 }  // namespace
@@ -457,40 +487,47 @@ __global__ __launch_bounds__(256) void merged_attn_f32_kernel(
 namespace kalm {
 
 void launch_merged_attn_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, const bf16_t* Vs,
-                             int64_t kv_ld, const int32_t* cu_q, int P, int64_t rows, int max_lq,
-                             const bf16_t* Kc, const bf16_t* Vc, int64_t c_ld, const uint8_t* cmask,
-                             const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv, float scale,
-                             bf16_t* O, int64_t o_ld, float* lse, hipStream_t s) {
+                             int64_t kv_ld, const int32_t* cu_q, int P, int64_t q_rows, int64_t kv_rows,
+                             int64_t o_rows, int mode, int max_lq, const bf16_t* Kc, const bf16_t* Vc,
+                             int64_t c_ld, const uint8_t* cmask, const int32_t* doc_of_pair, int D, int Cmax,
+                             int nq, int nkv, float scale, bf16_t* O, int64_t o_ld, float* lse, hipStream_t s) {
   constexpr int NW = ATTN_WAVES;
   const int G = nq / nkv;
   const int NH = G >= 4 ? 4 : G;  // heads per block (G is 1, 2 or a multiple of 4)
   const int RB = 32 * (NW / NH);
-  const int nqb = (max_lq + RB - 1) / RB;
+  const int max_rows = mode == 1 ? 1 : max_lq;  // query rows per pair
+  const int nqb = (max_rows + RB - 1) / RB;
   const int64_t blocks = (int64_t)P * nkv * (G / NH) * nqb;
   const float sl2 = scale * 1.4426950408889634f;
   const dim3 grid((unsigned)blocks), block(NW * 64);
   if (blocks == 0) return;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, P, q_rows, kv_rows, o_rows, nqb, Kc, Vc,
+                       c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, sl2, O, o_ld, lse);
+  };
+  // one instantiation per (heads per block, row mode)
   if (NH == 4)
-    hipLaunchKernelGGL((merged_attn_bf16_kernel<4, NW>), grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, P, rows,
-                       nqb, Kc, Vc, c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, sl2, O, o_ld, lse);
+    mode == 0 ? go(merged_attn_bf16_kernel<4, NW, 0>) : mode == 1 ? go(merged_attn_bf16_kernel<4, NW, 1>)
+                                                      : go(merged_attn_bf16_kernel<4, NW, 2>);
   else if (NH == 2)
-    hipLaunchKernelGGL((merged_attn_bf16_kernel<2, NW>), grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, P, rows,
-                       nqb, Kc, Vc, c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, sl2, O, o_ld, lse);
+    mode == 0 ? go(merged_attn_bf16_kernel<2, NW, 0>) : mode == 1 ? go(merged_attn_bf16_kernel<2, NW, 1>)
+                                                      : go(merged_attn_bf16_kernel<2, NW, 2>);
   else
-    hipLaunchKernelGGL((merged_attn_bf16_kernel<1, NW>), grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, P, rows,
-                       nqb, Kc, Vc, c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, sl2, O, o_ld, lse);
+    mode == 0 ? go(merged_attn_bf16_kernel<1, NW, 0>) : mode == 1 ? go(merged_attn_bf16_kernel<1, NW, 1>)
+                                                      : go(merged_attn_bf16_kernel<1, NW, 2>);
 }
 
 void launch_merged_attn_f32(const float* Q, int64_t q_ld, const float* Ks, const float* Vs,
-                            int64_t kv_ld, const int32_t* cu_q, int P, int64_t rows, int max_lq,
-                            const float* Kc, const float* Vc, int64_t c_ld, const uint8_t* cmask,
-                            const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv, int d,
-                            float scale, float* O, int64_t o_ld, float* lse, hipStream_t s) {
-  if (P == 0 || max_lq == 0) return;
-  const int nrb = (max_lq + 3) / 4;  // 4 rows (one per wave) per block
+                            int64_t kv_ld, const int32_t* cu_q, int P, int64_t q_rows, int64_t kv_rows,
+                            int64_t o_rows, int mode, int max_lq, const float* Kc, const float* Vc, int64_t c_ld,
+                            const uint8_t* cmask, const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv,
+                            int d, float scale, float* O, int64_t o_ld, float* lse, hipStream_t s) {
+  const int max_rows = mode == 1 ? 1 : max_lq;
+  if (P == 0 || max_rows == 0) return;
+  const int nrb = (max_rows + 3) / 4;  // 4 rows (one per wave) per block
   const dim3 grid((unsigned)((int64_t)nrb * nq * P)), block(256);
-  hipLaunchKernelGGL(merged_attn_f32_kernel, grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, rows, Kc, Vc,
-                     c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, d, scale, O, o_ld, lse, nrb);
+  hipLaunchKernelGGL(merged_attn_f32_kernel, grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, q_rows, kv_rows,
+                     o_rows, mode, Kc, Vc, c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, d, scale, O, o_ld, lse, nrb);
 }
 
 }  // namespace kalm

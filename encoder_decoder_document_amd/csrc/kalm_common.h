@@ -108,15 +108,15 @@ void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, v
 void launch_linear_f32(const float* X, const float* W, int M, int K, int N, float* Y, bool accumulate,
                        const uint8_t* row_mask, hipStream_t s);
 void launch_merged_attn_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, const bf16_t* Vs,
-                             int64_t kv_ld, const int32_t* cu_q, int P, int64_t rows, int max_lq,
-                             const bf16_t* Kc, const bf16_t* Vc, int64_t c_ld, const uint8_t* cmask,
-                             const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv, float scale,
-                             bf16_t* O, int64_t o_ld, float* lse, hipStream_t s);
+                             int64_t kv_ld, const int32_t* cu_q, int P, int64_t q_rows, int64_t kv_rows,
+                             int64_t o_rows, int mode, int max_lq, const bf16_t* Kc, const bf16_t* Vc,
+                             int64_t c_ld, const uint8_t* cmask, const int32_t* doc_of_pair, int D, int Cmax,
+                             int nq, int nkv, float scale, bf16_t* O, int64_t o_ld, float* lse, hipStream_t s);
 void launch_merged_attn_f32(const float* Q, int64_t q_ld, const float* Ks, const float* Vs,
-                            int64_t kv_ld, const int32_t* cu_q, int P, int64_t rows, int max_lq,
-                            const float* Kc, const float* Vc, int64_t c_ld, const uint8_t* cmask,
-                            const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv, int d,
-                            float scale, float* O, int64_t o_ld, float* lse, hipStream_t s);
+                            int64_t kv_ld, const int32_t* cu_q, int P, int64_t q_rows, int64_t kv_rows,
+                            int64_t o_rows, int mode, int max_lq, const float* Kc, const float* Vc, int64_t c_ld,
+                            const uint8_t* cmask, const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv,
+                            int d, float scale, float* O, int64_t o_ld, float* lse, hipStream_t s);
 void launch_yesno(const void* h, bool h_bf16, int64_t h_ld, int64_t rows, const int32_t* final_row, int P,
                   int H, const void* w, bool w_bf16, float* yes, float* no, float* margin, float* score,
                   hipStream_t s);

@@ -36,6 +36,9 @@ _SIGS = {
     "kalm_cross_kv": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _c_p, _i32, _i32, _c_p, _c_p]),
     "kalm_merged_attn": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i32, _i64, _i32, _c_p, _c_p, _i64,
                                 _c_p, _c_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_p, _i64, _c_p, _c_p]),
+    "kalm_merged_attn_rows": (_i32, [_c_p, _i64, _i64, _c_p, _c_p, _i64, _i64, _c_p, _i32, _i32, _c_p, _c_p, _i64,
+                                     _c_p, _c_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_p, _i64, _i64, _c_p,
+                                     _i32, _c_p]),
     "kalm_yesno_score": (_i32, [_c_p, _i32, _i64, _i64, _c_p, _i32, _i32, _c_p, _i32, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "kalm_linear": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _i32, _c_p, _i32, _i32, _c_p, _c_p]),
     "kalm_gather_rows": (_i32, [_c_p, _c_p, _i64, _i32, _i64, _c_p, _c_p, _c_p]),
@@ -180,6 +183,31 @@ def kalm_merged_attn(Q: torch.Tensor, Ks: torch.Tensor, Vs: torch.Tensor, cu_q: 
         _ptr(Q), Q.stride(0), _ptr(Ks), _ptr(Vs), Ks.stride(0), _ptr(cu_q), P, rows, max_lq,
         _ptr(Kc), _ptr(Vc), Kc.stride(0), _ptr(chunk_mask), _ptr(doc_of_pair), D, Cmax, nq, nkv, d,
         float(scale), _dt(Q), _ptr(out), out.stride(0), _ptr(lse), _stream(stream)))
+    return out
+
+
+ROWS_ALL, ROWS_FINAL, ROWS_SHARED = 0, 1, 2
+
+
+def kalm_merged_attn_rows(Q: torch.Tensor, Ks: torch.Tensor, Vs: torch.Tensor, cu_q: torch.Tensor, max_lq: int,
+                          Kc: torch.Tensor, Vc: torch.Tensor, chunk_mask: torch.Tensor, doc_of_pair: torch.Tensor,
+                          nq: int, nkv: int, d: int, row_mode: int, o_rows: int, scale: Optional[float] = None,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
+    """Merged attention over a choice of query rows (row_mode ROWS_ALL / ROWS_FINAL / ROWS_SHARED):
+    Q [q_rows, >=nq*d], Ks/Vs [kv_rows, >=nkv*d] -> O [o_rows, nq*d]."""
+    for t in (Q, Ks, Vs, Kc, Vc):
+        if t.stride(-1) != 1:
+            raise ValueError("unit column stride required")
+    P = cu_q.numel() - 1
+    D, Cmax = chunk_mask.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(o_rows, nq * d, dtype=Q.dtype, device=Q.device)
+    _check("kalm_merged_attn_rows", load().kalm_merged_attn_rows(
+        _ptr(Q), Q.stride(0), Q.shape[0], _ptr(Ks), _ptr(Vs), Ks.stride(0), Ks.shape[0], _ptr(cu_q), P, max_lq,
+        _ptr(Kc), _ptr(Vc), Kc.stride(0), _ptr(chunk_mask), _ptr(doc_of_pair), D, Cmax, nq, nkv, d,
+        float(scale), _dt(Q), _ptr(out), out.stride(0), o_rows, _ptr(lse), int(row_mode), _stream(stream)))
     return out
 
 

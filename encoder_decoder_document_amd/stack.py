@@ -10,6 +10,16 @@ itself only enqueues libkalm calls on the current stream:
   kalm_linear (output projection added to the fp32 residual, bf16 copy for the
   next layer) -> kalm_yesno_score.
 
+With ``prune`` (the default) two layers do less work for the same result:
+  * layer 1: every passage of a query still holds the query's own first hidden
+    states, so Q/K/V are projected once per query row (not once per pair row)
+    and the attention reads them shared (kalm_merged_attn_rows, shared rows);
+  * the last layer (stacks of two or more layers): the score reads only each
+    pair's final position ("KaLM-Reranker-V1-Nano -- MLX (Apple Silicon)",
+    What this is), so self K/V are projected for every row but Q, attention,
+    the output projection and the residual update only for the final rows
+    (kalm_merged_attn_rows, final row).
+
 The decoder layer is the reading stated on the pages' behalf: the pages give
 only the layer counts ("KaLM-Reranker-V1-Nano -- MLX (Apple Silicon)", What
 this is) and the merged attention; no norm, RoPE or MLP is added.
@@ -92,6 +102,19 @@ def upload(inputs: Dict[str, object], device="cuda", n_layers: Optional[int] = N
     )
     if dt == torch.bfloat16:
         buf["hb"] = torch.empty(rows, H, dtype=torch.bfloat16, device=device)
+    U = int(lq.sum())  # decoder rows of the queries themselves
+    buf.update(
+        u_idx=torch.arange(U, dtype=torch.int32, device=device),
+        p_idx=torch.arange(P, dtype=torch.int32, device=device),
+        h0_copy=torch.empty(U, H, dtype=torch.float32, device=device),
+        qkv_u=torch.empty(U, nqkv, dtype=dt, device=device),
+        hf=torch.empty(P, H, dtype=torch.float32, device=device),
+        qf=torch.empty(P, sh.nq * sh.d, dtype=dt, device=device),
+        of=torch.empty(P, sh.nq * sh.d, dtype=dt, device=device),
+    )
+    if dt == torch.bfloat16:
+        buf["h0b"] = torch.empty(U, H, dtype=torch.bfloat16, device=device)
+        buf["hfb"] = torch.empty(P, H, dtype=torch.bfloat16, device=device)
     return DeviceBatch(
         shape=sh, n_layers=L, dtype=dt, D=D, T=T, H=H, nq=sh.nq, nkv=sh.nkv, d=sh.d, chunk=chunk, Cmax=Cmax,
         n_queries=sh.n_queries, P=P, rows=rows, max_lq=int(lq.max()) if lq.size else 0,
@@ -124,7 +147,12 @@ def front(b: DeviceBatch, stream=None, rec=_no_rec):
             ops.kalm_cross_kv(B["pooled"], B["chunk_mask"], b.Wkvc[l], out=B["kvc"][l], stream=stream)
 
 
-def decoder(b: DeviceBatch, stream=None, rec=_no_rec):
+def pruned(b: DeviceBatch, prune: bool = True) -> bool:
+    """Whether the last layer runs on final rows only (needs two or more layers)."""
+    return prune and b.n_layers >= 2
+
+
+def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True):
     """Row a5 around a3: residual start, then every merged-attention layer."""
     B = b.buf
     bf = b.dtype == torch.bfloat16
@@ -134,27 +162,61 @@ def decoder(b: DeviceBatch, stream=None, rec=_no_rec):
     qkv = B["qkv"]
     Q, Ks, Vs = qkv[:, :qd], qkv[:, qd:qd + kv], qkv[:, qd + kv:]
     scale = 1.0 / math.sqrt(b.d)
+    last_pruned = pruned(b, prune)
     for l in range(b.n_layers):
-        x_in = B["hb"] if bf else B["h"]
-        with rec("qkv_linear"):
-            ops.kalm_linear(x_in, b.Wqkv[l], Y=qkv, stream=stream)
         kvc = B["kvc"][l].view(b.D * b.Cmax, 2 * kv)
-        with rec("merged_attn"):
-            ops.kalm_merged_attn(Q, Ks, Vs, B["cu_q"], b.max_lq, kvc[:, :kv], kvc[:, kv:], B["chunk_mask"],
-                                 B["doc_of_pair"], b.nq, b.nkv, b.d, scale=scale, out=B["o"], stream=stream)
+        x_in = B["hb"] if bf else B["h"]
+        if prune and l == 0:
+            # the queries' own rows: one Q/K/V projection per query row, shared by its passages
+            if bf:
+                with rec("gather_query_rows"):
+                    ops.kalm_gather_rows(b.h0, B["u_idx"], dst=B["h0_copy"], dst_bf16=B["h0b"], stream=stream)
+            u = B["qkv_u"]
+            with rec("qkv_linear_first"):
+                ops.kalm_linear(B["h0b"] if bf else b.h0, b.Wqkv[0], Y=u, stream=stream)
+            with rec("merged_attn_first"):
+                ops.kalm_merged_attn_rows(u[:, :qd], u[:, qd:qd + kv], u[:, qd + kv:], B["cu_q"], b.max_lq,
+                                          kvc[:, :kv], kvc[:, kv:], B["chunk_mask"], B["doc_of_pair"], b.nq,
+                                          b.nkv, b.d, ops.ROWS_SHARED, b.rows, scale=scale, out=B["o"],
+                                          stream=stream)
+        elif last_pruned and l == b.n_layers - 1:
+            # final rows only: self K/V of every row, Q / attention / projection of the final rows
+            kvs = qkv.view(-1)[: b.rows * 2 * kv].view(b.rows, 2 * kv)
+            with rec("kv_linear_last"):
+                ops.kalm_linear(x_in, b.Wqkv[l][qd:], Y=kvs, stream=stream)
+            with rec("gather_final_rows"):
+                ops.kalm_gather_rows(B["h"], B["final_row"], dst=B["hf"], dst_bf16=B["hfb"] if bf else None,
+                                     stream=stream)
+            with rec("q_linear_last"):
+                ops.kalm_linear(B["hfb"] if bf else B["hf"], b.Wqkv[l][:qd], Y=B["qf"], stream=stream)
+            with rec("merged_attn_last"):
+                ops.kalm_merged_attn_rows(B["qf"], kvs[:, :kv], kvs[:, kv:], B["cu_q"], b.max_lq, kvc[:, :kv],
+                                          kvc[:, kv:], B["chunk_mask"], B["doc_of_pair"], b.nq, b.nkv, b.d,
+                                          ops.ROWS_FINAL, b.P, scale=scale, out=B["of"], stream=stream)
+            with rec("o_linear_last"):
+                ops.kalm_linear(B["of"], b.Wo[l], Y=B["hf"], accumulate=True, stream=stream)
+            continue
+        else:
+            with rec("qkv_linear"):
+                ops.kalm_linear(x_in, b.Wqkv[l], Y=qkv, stream=stream)
+            with rec("merged_attn"):
+                ops.kalm_merged_attn(Q, Ks, Vs, B["cu_q"], b.max_lq, kvc[:, :kv], kvc[:, kv:], B["chunk_mask"],
+                                     B["doc_of_pair"], b.nq, b.nkv, b.d, scale=scale, out=B["o"], stream=stream)
         with rec("o_linear"):
             ops.kalm_linear(B["o"], b.Wo[l], Y=B["h"], accumulate=True, Y_bf16=B["hb"] if bf else None,
                             stream=stream)
 
 
-def score(b: DeviceBatch, stream=None, rec=_no_rec):
+def score(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True):
     """Row a4: yes/no readout at every pair's final row."""
     with rec("yesno_score"):
+        if pruned(b, prune):
+            return ops.kalm_yesno_score(b.buf["hf"], b.buf["p_idx"], b.w_yesno, stream=stream)
         return ops.kalm_yesno_score(b.buf["h"], b.buf["final_row"], b.w_yesno, stream=stream)
 
 
-def step(b: DeviceBatch, stream=None, rec=_no_rec):
+def step(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True):
     """One pass of the whole hot path over the batch; returns (yes, no, margin, score)."""
     front(b, stream, rec)
-    decoder(b, stream, rec)
-    return score(b, stream, rec)
+    decoder(b, stream, rec, prune)
+    return score(b, stream, rec, prune)

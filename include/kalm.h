@@ -128,7 +128,8 @@ kalm_status kalm_cross_kv(const void* pooled, const uint8_t* chunk_mask, int32_t
  *
  *   Q         [rows, *] dtype dt, row stride q_ld; head h at columns h*d .. h*d+d-1
  *   Ks, Vs    [rows, *] dtype dt, row stride kv_ld; KV head g at columns g*d ..
- *   cu_q      [P+1] int32 row offsets (non-decreasing, cu_q[P] <= rows)
+ *   cu_q      [P+1] int32 row offsets (non-decreasing, cu_q[P] <= rows; a pair
+ *             whose rows fall outside [0, rows) is skipped, its outputs not written)
  *   max_lq    >= every pair's length cu_q[p+1]-cu_q[p]; rows of a pair beyond
  *             max_lq are not computed (the caller's contract)
  *   Kc, Vc    [D*Cmax, *] dtype dt, row stride c_ld; doc d's chunk c is row d*Cmax+c
@@ -146,6 +147,36 @@ kalm_status kalm_merged_attn(const void* Q, int64_t q_ld, const void* Ks, const 
                              const uint8_t* chunk_mask, const int32_t* doc_of_pair, int32_t D,
                              int32_t Cmax, int32_t nq, int32_t nkv, int32_t d, float scale,
                              kalm_dtype dt, void* O, int64_t o_ld, float* lse, void* stream);
+
+/*
+ * a3 with a choice of query rows (the same operation as kalm_merged_attn).
+ * The pair's self keys are its Lq = cu_q[p+1] - cu_q[p] decoder positions;
+ * row_mode selects which query rows are computed and where the rows live:
+ *   0  every position of every pair; Q, Ks/Vs and O rows of pair p start at
+ *      cu_q[p] (exactly kalm_merged_attn; q_rows = kv_rows = o_rows = rows).
+ *   1  only the final position Lq-1 of each pair (it sees all Lq self keys):
+ *      Q row p and O/lse row p; Ks/Vs rows start at cu_q[p].  The score is read
+ *      at the decoder's final position only ([MLX] What this is), so the last
+ *      layer needs no other row.
+ *   2  rows shared by the D passages of a query: with the kalm_pair_layout
+ *      layout (pair p = query p / D, passage p % D), Q and Ks/Vs rows are the
+ *      query's rows in a per-query packing, starting at cu_q[(p/D)*D] / D;
+ *      O/lse rows start at cu_q[p].  While every passage of a query still
+ *      holds the query's own hidden states (the decoder models the query,
+ *      [MLX] What this is; one passage set reranked against many queries,
+ *      [MLX] Speed), their Q/K/V projections are one set of rows.
+ *   q_rows, kv_rows, o_rows  rows in Q, in Ks/Vs and in O (and lse); a pair
+ *      whose rows fall outside them is skipped (its outputs are not written).
+ * Other arguments as kalm_merged_attn; row_mode outside 0..2 is
+ * KALM_ERR_INVALID_ARG.
+ */
+kalm_status kalm_merged_attn_rows(const void* Q, int64_t q_ld, int64_t q_rows, const void* Ks,
+                                  const void* Vs, int64_t kv_ld, int64_t kv_rows, const int32_t* cu_q,
+                                  int32_t P, int32_t max_lq, const void* Kc, const void* Vc,
+                                  int64_t c_ld, const uint8_t* chunk_mask, const int32_t* doc_of_pair,
+                                  int32_t D, int32_t Cmax, int32_t nq, int32_t nkv, int32_t d,
+                                  float scale, kalm_dtype dt, void* O, int64_t o_ld, int64_t o_rows,
+                                  float* lse, int32_t row_mode, void* stream);
 
 /*
  * a4 -- yes/no readout ([MLX] What this is: score = softmax([logit_yes,

@@ -234,6 +234,60 @@ def test_merged_attn_f32_parity(name, lqs, docs_c, Cmax, nq, nkv, d):
     assert_close(to_np(lse), rL, *F32_TOL, "lse f32")
 
 
+@pytest.mark.parametrize("bf16", [True, False])
+def test_merged_attn_final_row_mode(bf16):
+    """row_mode 1: only each pair's final position, Q/O one row per pair."""
+    _announce(f"merged_attn final-row mode bf16={bf16}")
+    d = 256 if bf16 else 64
+    lqs = [1, 33, 64, 100, 7]
+    case = _attn_case(11, lqs, [0, 31, 70, 5, 64], 70, 4, 1, d, bf16)
+    Q, Ks, Vs, Kc, Vc, cm, dop, cu_q = case
+    P = len(lqs)
+    fin = cu_q[1:] - 1
+    dt = torch.bfloat16 if bf16 else torch.float32
+    lse = torch.full((P, 4), -7.0, dtype=torch.float32, device="cuda")
+    O = ops.kalm_merged_attn_rows(to_dev(Q[fin], dt), to_dev(Ks, dt), to_dev(Vs, dt), to_dev(cu_q, torch.int32),
+                                  max(lqs), to_dev(Kc, dt), to_dev(Vc, dt), to_dev(cm, torch.uint8),
+                                  to_dev(dop, torch.int32), 4, 1, d, ops.ROWS_FINAL, P, lse=lse)
+    torch.cuda.synchronize()
+    rO, rL = _attn_ref(*case, 4, 1, d)
+    tol = BF16_TOL if bf16 else F32_TOL
+    assert_close(to_np(O), rO[fin], *tol, "O final rows")
+    assert_close(to_np(lse), rL[fin], *tol, "lse final rows")
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_merged_attn_shared_rows_mode(bf16):
+    """row_mode 2: Q/K/V rows of each query shared by its D passages (pair
+    p = query p // D, passage p % D); O in the pair layout."""
+    _announce(f"merged_attn shared-rows mode bf16={bf16}")
+    d = 256 if bf16 else 32
+    nq, nkv, D, Cmax = 4, 1, 4, 40
+    lq = np.array([5, 37, 70], np.int64)
+    docs_c = [0, 3, 32, 33]
+    U = int(lq.sum())
+    Qu = synth.normal(21, (U, nq * d), 0.7, bf16)
+    Ku = synth.normal(22, (U, nkv * d), 0.7, bf16)
+    Vu = synth.normal(23, (U, nkv * d), 1.0, bf16)
+    Kc = synth.normal(24, (D * Cmax, nkv * d), 0.7, bf16)
+    Vc = synth.normal(25, (D * Cmax, nkv * d), 1.0, bf16)
+    cm = (np.arange(Cmax)[None] < np.asarray(docs_c)[:, None]).astype(np.uint8)
+    starts = np.concatenate([[0], np.cumsum(lq)])
+    # pair layout: query q's D pairs back to back, each a copy of the query's rows
+    idx = np.concatenate([np.arange(starts[q], starts[q + 1]) for q in range(len(lq)) for _ in range(D)])
+    lens = np.repeat(lq, D)
+    cu_q = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    dop = (np.arange(len(lens)) % D).astype(np.int32)
+    rows = int(cu_q[-1])
+    dt = torch.bfloat16 if bf16 else torch.float32
+    O = ops.kalm_merged_attn_rows(to_dev(Qu, dt), to_dev(Ku, dt), to_dev(Vu, dt), to_dev(cu_q, torch.int32),
+                                  int(lq.max()), to_dev(Kc, dt), to_dev(Vc, dt), to_dev(cm, torch.uint8),
+                                  to_dev(dop, torch.int32), nq, nkv, d, ops.ROWS_SHARED, rows)
+    torch.cuda.synchronize()
+    rO, _ = _attn_ref(Qu[idx], Ku[idx], Vu[idx], Kc, Vc, cm, dop, cu_q, nq, nkv, d)
+    assert_close(to_np(O), rO, *(BF16_TOL if bf16 else F32_TOL), "O shared rows")
+
+
 def test_merged_attn_bad_doc_gives_nan_rows():
     _announce("merged_attn out-of-range doc")
     case = _attn_case(9, [20, 20], [5, 5], 32, 4, 1, 256, True)

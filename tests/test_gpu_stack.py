@@ -83,3 +83,21 @@ def test_stack_edge_empty_and_one_token_passages():
     inp = synth.make_inputs(0, seed=77, shape=sh)
     b, got = _run(inp)
     _check(inp, b, got, list(range(sh.pairs)))
+
+
+def test_stack_pruned_path_equals_full_path():
+    # the shared first layer and the final-row last layer change how much is
+    # computed, not the result: scores of both paths agree, and with the oracle
+    idx = 2
+    sh = synth.SHAPES[idx]
+    print(f"[case] stack {sh.name} 3 layers, pruned vs full", flush=True)
+    inp = synth.make_inputs(idx, nan_padding=True, n_layers=3)
+    b = stack.upload(inp)
+    full = to_np(stack.step(b, prune=False)[3])
+    pruned = to_np(stack.step(b, prune=True)[3])
+    torch.cuda.synchronize()
+    assert_close(pruned, full, 1e-3, 0.0, "pruned vs full score")
+    pairs = _sample_pairs(inp, 8)
+    ref = oracle.stack_scores(inp, pairs=pairs, mode="mirror")
+    assert_close(pruned[np.asarray(pairs)], ref["score"], SCORE_ATOL, 0.0, "pruned score vs oracle")
+
