@@ -69,6 +69,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="small_stack26_bf16")
+    ap.add_argument("--chunk", type=int, default=None,
+                    help="pooling granularity in tokens (Matryoshka variants); default: the workload's (4)")
+    ap.add_argument("--no-prune", action="store_true",
+                    help="compute every row of the first and last layers (no shared / final-row shortcut)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     ap.add_argument("--no-pool-long", action="store_true", help="skip the pooling measurement at the 1024x2560 shape")
@@ -219,24 +223,27 @@ def main():
         sys.exit(f"unknown workload {a.workload}; one of {names}")
     idx = names.index(a.workload)
     sh = synth.SHAPES[idx]
+    if a.chunk is not None:
+        import dataclasses
+        sh = dataclasses.replace(sh, chunk=a.chunk)
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU (libkalm has no CPU fallback)")
     if ops.device_check() != ops.KALM_OK:
         sys.exit(ops.load().kalm_last_error().decode())
     print(f"[bench] generating {sh.name}", file=sys.stderr, flush=True)
-    inp = synth.make_inputs(idx, nan_padding=False)
+    inp = synth.make_inputs(idx, nan_padding=False, shape=sh)
     b = stack.upload(inp)
     torch.cuda.synchronize()
     print(f"[bench] uploaded: rows={b.rows} pairs={b.P}; warmup {a.warmup}", file=sys.stderr, flush=True)
     rec = EventRec(torch)
     rec.on = False
     for _ in range(a.warmup):
-        stack.step(b, rec=rec)
+        stack.step(b, rec=rec, prune=not a.no_prune)
     torch.cuda.synchronize()
     rec.on = True
     t0 = time.perf_counter()
     for i in range(a.steps):
-        stack.step(b, rec=rec)
+        stack.step(b, rec=rec, prune=not a.no_prune)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_step = el / a.steps * 1e3
@@ -278,7 +285,8 @@ def main():
         "config": {"workload": sh.name, "queries": sh.n_queries, "docs": sh.n_docs, "pairs": sh.pairs,
                    "layers": sh.n_layers, "hidden": sh.H, "q_heads": sh.nq, "kv_heads": sh.nkv, "head_dim": sh.d,
                    "decoder_len": list(sh.lq), "passage_len": list(sh.doc_len), "chunk": sh.chunk,
-                   "decoder_rows": b.rows, "parallelism": "single GPU"},
+                   "decoder_rows": b.rows, "pruned_first_last_layer": not a.no_prune,
+                   "parallelism": "single GPU"},
         "roofline": roof,
         "merged_attn": {k: kernels["merged_attn"].get(k) for k in ("avg_us", "tflops", "mfma_frac", "gbs", "hbm_frac")},
         "kernels": kernels,

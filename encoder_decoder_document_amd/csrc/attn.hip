@@ -39,6 +39,18 @@ namespace {
 constexpr int HD = 256;          // head dim of the bf16 path
 constexpr int BKV = 32;          // keys per tile
 constexpr float LAZY = 8.0f;     // lazy-rescale threshold, log2 units
+// Streaming (non-temporal) hints for the Q loads and O stores: measured
+// slower here (2.50 vs 2.20 ms at the Small shape), so off by default.
+#ifndef ATTN_STREAM
+#define ATTN_STREAM 0
+#endif
+#if ATTN_STREAM
+#define ATTN_LD_Q(p) __builtin_nontemporal_load(p)
+#define ATTN_ST_O(v, p) __builtin_nontemporal_store(v, p)
+#else
+#define ATTN_LD_Q(p) (*(p))
+#define ATTN_ST_O(v, p) (*(p) = (v))
+#endif
 #ifndef ATTN_WAVES
 #define ATTN_WAVES 4             // waves per workgroup (4 or 8)
 #endif
@@ -118,15 +130,19 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
     bf16_t* __restrict__ O, int64_t o_ld, float* __restrict__ lse) {
   constexpr int WPH = NW / NH;            // row blocks per head
   constexpr int RB = 32 * WPH;            // decoder rows per block
-#ifdef ATTN_RING
-  constexpr int RING = ATTN_RING;
+  // K and V rings: 2 deep with 4 waves (two workgroups per CU, 64 KB each),
+  // 3 deep with 8 waves.  A 3-deep K ring beside a 2-deep V ring (80 KB) was
+  // measured slower at the Small shape (2.40 vs 2.25 ms).
+#ifdef ATTN_KRING
+  constexpr int KR = ATTN_KRING, VR = ATTN_VRING;
 #else
-  constexpr int RING = NW == 8 ? 3 : 2;   // K/V tiles resident in LDS
+  constexpr int KR = NW == 8 ? 3 : 2, VR = KR;
 #endif
+  static_assert(KR == VR || KR == VR + 1, "K ring as deep as the V ring or one deeper");
   constexpr int RPW = BKV / NW;           // key rows each wave copies per tile
   constexpr int TILE_B = BKV * HD * 2;    // bytes of one K (or V) tile
-  // K tiles (k_swz) in slots 0..RING-1, then V tiles (v_swz)
-  __shared__ __attribute__((aligned(1024))) uint8_t kv_lds[2 * RING * TILE_B];
+  // K tiles (k_swz) in slots 0..KR-1, then V tiles (v_swz) in VR slots
+  __shared__ __attribute__((aligned(1024))) uint8_t kv_lds[(KR + VR) * TILE_B];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, g = lane >> 5;
@@ -194,7 +210,7 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
   {
     const bf16_t* qp = Q + (pr.q0 + j_ld) * q_ld + (int64_t)h * HD + 8 * g;
 #pragma unroll
-    for (int s = 0; s < HD / 16; ++s) qf[s] = *(const bf16x8_t*)(qp + 16 * s);
+    for (int s = 0; s < HD / 16; ++s) qf[s] = ATTN_LD_Q((const bf16x8_t*)(qp + 16 * s));
   }
 
   f32x16_t oacc[HD / 32];
@@ -214,7 +230,7 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
   const uint64_t kc_base = (uint64_t)(uintptr_t)(Kc + cdoc);
   const uint64_t vc_base = (uint64_t)(uintptr_t)(Vc + cdoc);
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(kv_lds));
-  const uint32_t klds0 = lds0, vlds0 = lds0 + RING * TILE_B;
+  const uint32_t klds0 = lds0, vlds0 = lds0 + KR * TILE_B;
   const uint32_t kv_ld2 = (uint32_t)kv_ld * 2u, c_ld2 = (uint32_t)c_ld * 2u;
 
   // DMA plan: wave w copies key rows RPW*w .. RPW*w + RPW-1 of a tile, two
@@ -224,18 +240,17 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
   const int dkey0 = RPW * wave + (lane >> 5);
   const uint32_t dslab = __builtin_amdgcn_readfirstlane(wave * RPW * (HD * 2));
 
-  // copy tile v (K and V) into ring slot v % RING.  Key rows that do not
-  // exist (past the pair / the passage) or are masked are fetched from a
-  // valid row instead: their logits are masked to -inf, so p = 0 multiplies a
-  // finite value.
-  auto issue = [&](int v) {
+  // copy the K (or V) rows of tile v into ring slot v % KR (v % VR).  Key rows
+  // that do not exist (past the pair / the passage) or are masked are fetched
+  // from a valid row instead: their logits are masked to -inf, so p = 0
+  // multiplies a finite value.
+  auto issue = [&](int v, bool is_k) {
     const bool self = v < n_st;
     const int kb = self ? v * BKV : (v - n_st) * BKV;
     const uint32_t ld2 = self ? kv_ld2 : c_ld2;
-    const uint64_t kba = self ? ks_base : kc_base;
-    const uint64_t vba = self ? vs_base : vc_base;
+    const uint64_t base = is_k ? (self ? ks_base : kc_base) : (self ? vs_base : vc_base);
     const uint32_t bits = self ? 0u : cm_word(v - n_st);
-    const uint32_t so = (uint32_t)((v % RING) * TILE_B) + dslab;
+    const uint32_t so = (is_k ? klds0 + (uint32_t)((v % KR) * TILE_B) : vlds0 + (uint32_t)((v % VR) * TILE_B)) + dslab;
     int key0 = dkey0;
     asm volatile("" : "+v"(key0));  // recompute the per-row offsets here instead of holding them
 #pragma unroll
@@ -246,8 +261,7 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
       else row = ((bits >> key) & 1u) ? kb + key : donor;
       const uint32_t ro = (uint32_t)row * ld2;
       const int c = __lane_id() & 31;
-      dma16(kba, ro + (uint32_t)(k_swz(key, c) << 4), klds0 + so + j * 1024);
-      dma16(vba, ro + (uint32_t)(v_swz(key, c) << 4), vlds0 + so + j * 1024);
+      dma16(base, ro + (uint32_t)((is_k ? k_swz(key, c) : v_swz(key, c)) << 4), so + j * 1024);
     }
   };
 
@@ -269,18 +283,28 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
   const uint32_t vx = vlds0 + vkey * (HD * 2) + 64 * (vkey & 3) + 16 * (vdim0 >> 3) +
                       2 * (vdim0 & 7);
 
-  for (int v = 0; v < RING - 1 && v < n_tiles; ++v) issue(v);
+  // Copy schedule (per wave, in issue order): V(0), K(0) .. K(KR-2), then at
+  // tile v: V(v + VR - 1), K(v + KR - 1).  When tile v starts, the copies
+  // still allowed in flight are the K tiles issued after V(v): K(v+1) ..
+  // K(v+KR-VR) -- none when the rings are equally deep.
+  constexpr int CPT = RPW / 2;  // copy instructions per wave per K (or V) tile
+  for (int v = 0; v < VR - 1 && v < n_tiles; ++v) {
+    issue(v, false);
+    issue(v, true);
+  }
+  for (int v = VR - 1; v < KR - 1 && v < n_tiles; ++v) issue(v, true);
   for (int v = 0; v < n_tiles; ++v) {
-    wait_dma_ktile<RPW>(min(n_tiles - 1 - v, RING - 2));  // RPW copies per tile: RPW/2 for K, RPW/2 for V
-    __syncthreads();  // tile v visible; the slot of tile v-1 is free
-    if (v + RING - 1 < n_tiles) issue(v + RING - 1);
+    if (KR == VR) wait_dma_ktile<2 * CPT>(min(n_tiles - 1 - v, VR - 2));
+    else wait_dma_ktile<CPT>(min(n_tiles - 1 - v, KR - VR));  // K(v+1) may still be in flight
+    __syncthreads();  // tile v visible; the slots of tile v-1 are free
+    if (v + VR - 1 < n_tiles) issue(v + VR - 1, false);
+    if (v + KR - 1 < n_tiles) issue(v + KR - 1, true);
     const bool self = v < n_st;
     const int kb = self ? v * BKV : (v - n_st) * BKV;
     // nothing to do: no valid rows in this wave, or a causal tile entirely
     // above its rows (the wave still joins every barrier and copy)
     if (qr0 >= nrow || (self && kb > wave_last)) continue;
-    const uint32_t slot = (uint32_t)((v % RING) * TILE_B);
-    uint32_t kt = kx + slot, vt = vx + slot;
+    uint32_t kt = kx + (uint32_t)((v % KR) * TILE_B), vt = vx + (uint32_t)((v % VR) * TILE_B);
     // opaque per tile: keeps the compiler from hoisting 24 precomputed
     // fragment addresses out of the loop (one XOR per read is cheaper than
     // the registers they would hold)
@@ -406,7 +430,7 @@ __global__ __launch_bounds__(NW * 64, 2) void merged_attn_bf16_kernel(
     for (int i = 0; i < 32 / RPI; ++i) {
       const int rr = RPI * i + lane / CPR, c = lane % CPR;
       const u32x4_t val = lds_read16u(ebase + rr * (DPP * 2) + ((c ^ (rr & (CPR - 1))) << 4));
-      if (qr0 + rr < nrow) *(u32x4_t*)(orow0 + rr * o_ld + pass * DPP + 8 * c) = val;
+      if (qr0 + rr < nrow) ATTN_ST_O(val, (u32x4_t*)(orow0 + rr * o_ld + pass * DPP + 8 * c));
     }
     __builtin_amdgcn_wave_barrier();
   }

@@ -26,6 +26,16 @@ namespace {
 
 enum Epi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_ACC = 2 };
 
+// Streaming (non-temporal) hints: on the outputs (written once; the fp32
+// residual read once) they help; on the activation tiles they were measured
+// to hurt (the column-tile siblings re-read them through L2), so off.
+#ifndef GEMM_STREAM_X
+#define GEMM_STREAM_X false
+#endif
+#ifndef GEMM_STREAM_Y
+#define GEMM_STREAM_Y true
+#endif
+
 // Physical 16-byte chunk of logical chunk c in row `row` of a k-tile whose
 // rows are BK bf16 (64 or 128 bytes).  The gfx950 LDS serves a ds_read_b128
 // 16 lanes at a time across 64 banks (256 bytes); the fragment reads of 16
@@ -46,7 +56,7 @@ __device__ __forceinline__ int swz(int row, int c) {
 // with BK = 64 every row is one whole 128-byte line.  Addresses are a scalar
 // 64-bit tile base plus a 32-bit per-lane byte offset; rows past the matrix
 // end are clamped to its last row (their products are discarded).
-template <int ROWS, int NWAVES, int BK>
+template <int ROWS, int NWAVES, int BK, bool NT>
 struct DmaPlan {
   static constexpr int CPR = BK / 8;                    // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;                  // rows per instruction
@@ -74,10 +84,21 @@ struct DmaPlan {
     for (int j = 0; j < PER; ++j) {
       int kk = k0 + lc8[j];
       if (kk >= K) kk = 0;  // in-bounds dummy; zeroed in LDS by zero_k_tail
-      dma16(base, row_off[j] + (uint32_t)kk * 2u, tile_lds + slab[j]);
+      dma16<NT>(base, row_off[j] + (uint32_t)kk * 2u, tile_lds + slab[j]);
     }
   }
 };
+
+template <typename T>
+__device__ __forceinline__ void st_out(T* p, T v) {
+  if constexpr (GEMM_STREAM_Y) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+template <typename T>
+__device__ __forceinline__ T ld_out(const T* p) {
+  if constexpr (GEMM_STREAM_Y) return __builtin_nontemporal_load(p);
+  else return *p;
+}
 
 // Zero the 16-byte chunks of a staged tile that lie beyond K (last k-tile only).
 template <int ROWS, int BK>
@@ -92,12 +113,12 @@ __device__ __forceinline__ void zero_k_tail(bf16_t* tile, int k0, int K, int tid
 // WM x WN waves split the block tile BM x BN; k advances BK per stage and
 // STAGES k-tiles live in the LDS ring (STAGES - 1 in flight while one feeds
 // the MFMAs); OCC = waves per SIMD it is built for (bounds the registers).
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int OCC>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int OCC, bool STREAM_X = GEMM_STREAM_X>
 __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, int M, int K, int N,
     void* __restrict__ Y, int epi, bf16_t* __restrict__ Ybf, const uint8_t* __restrict__ rmask) {
   constexpr int NW = WM * WN;
-  constexpr int CPS = DmaPlan<BM, NW, BK>::PER + DmaPlan<BN, NW, BK>::PER;  // copies per thread per k-tile
+  constexpr int CPS = DmaPlan<BM, NW, BK, true>::PER + DmaPlan<BN, NW, BK, false>::PER;  // copies per thread per k-tile
   static_assert(STAGES >= 2 && STAGES <= 5, "wait_dma_ktile handles at most three later k-tiles in flight");
   constexpr int NT = NW * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -139,8 +160,8 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
 
   const int nk = tile_live ? (K + BK - 1) / BK : 0;
   const bool k_tail = (K % BK) != 0;
-  DmaPlan<BM, NW, BK> planA;
-  DmaPlan<BN, NW, BK> planB;
+  DmaPlan<BM, NW, BK, STREAM_X> planA;
+  DmaPlan<BN, NW, BK, false> planB;
   planA.init(X, M, K, m0, wave, lane);
   planB.init(W, N, K, n0, wave, lane);
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
@@ -195,12 +216,18 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
   // (WTN * 4 bytes per row for fp32, WTN * 2 for bf16) instead of 32 short
   // pieces per instruction.
   constexpr int EP_LD = WTN + 4;  // fp32 per parked row
-  static_assert(NW * 32 * EP_LD * 4 <= STAGES * STAGE_ELEMS * 2, "epilogue staging fits the ring");
+  // waves take turns when all of their parking areas do not fit the ring at once
+  constexpr int EP_ROUNDS = (NW * 32 * EP_LD * 4 + STAGES * STAGE_ELEMS * 2 - 1) / (STAGES * STAGE_ELEMS * 2);
+  static_assert(EP_ROUNDS <= 2 && NW % EP_ROUNDS == 0, "epilogue staging fits the ring in two rounds");
   __syncthreads();  // every wave is done reading the ring
-  float* park = (float*)smem + wave * (32 * EP_LD);
+  float* park = (float*)smem + (wave / EP_ROUNDS) * (32 * EP_LD);
   constexpr int LPR = WTN / 4;          // lanes per row (16 bytes of fp32 each)
   constexpr int RPI = 64 / LPR;         // rows per wave instruction
   const int prow = lane / LPR, pcol = (lane % LPR) * 4;
+#pragma unroll
+  for (int round = 0; round < EP_ROUNDS; ++round) {
+  if (EP_ROUNDS > 1 && round > 0) __syncthreads();  // the previous round's waves are done with the area
+  if (wave % EP_ROUNDS != round) continue;
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
 #pragma unroll
@@ -217,16 +244,18 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
       if (m < M && n < N) {
         if (rmask && !rmask[m]) v = f32x4_t{0.f, 0.f, 0.f, 0.f};
         const int64_t off = (int64_t)m * N + n;
+        // outputs are written once (and the fp32 stream read once): non-temporal
         if (epi == EPI_BF16) {
-          *(u32x2_t*)((bf16_t*)Y + off) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          st_out((u32x2_t*)((bf16_t*)Y + off), u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
         } else {
-          float* yp = (float*)Y + off;
-          if (epi == EPI_F32_ACC) v += *(const f32x4_t*)yp;
-          *(f32x4_t*)yp = v;
-          if (Ybf) *(u32x2_t*)(Ybf + off) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          f32x4_t* yp = (f32x4_t*)((float*)Y + off);
+          if (epi == EPI_F32_ACC) v += ld_out(yp);
+          st_out(yp, v);
+          if (Ybf) st_out((u32x2_t*)(Ybf + off), u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
         }
       }
     }
+  }
   }
 }
 
@@ -296,8 +325,13 @@ void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, v
   } else if (big_tiles >= 512) {
     // 256 x 256 tiles, k-tiles of 64 (every copied row a whole 128-byte line), two-slot ring
     const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+#ifdef GEMM_W16
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, 4, 64, 2, 4>), dim3(tiles), dim3(1024), 0, s, X, W, M, K, N,
+                       Y, epi, Y_bf16, rmask);
+#else
     hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 64, 2, 1>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y,
                        epi, Y_bf16, rmask);
+#endif
   } else {  // small problems: more, smaller tiles to fill the 256 CUs
     const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 32, 4, 1>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y,

@@ -240,4 +240,18 @@ kalm_status kalm_gather_rows(const float* src, const int32_t* idx, int64_t M, in
   return kalm::check_launch("kalm_gather_rows");
 }
 
+kalm_status kalm_rank_topn(const float* score, int32_t n_queries, int32_t n_docs, int32_t top_n,
+                           int32_t* out_index, float* out_score, void* stream) {
+  kalm::g_err[0] = 0;
+  KALM_REQUIRE(n_queries >= 0 && n_docs >= 0 && top_n >= 0, KALM_ERR_INVALID_ARG, "kalm_rank_topn: negative sizes");
+  KALM_REQUIRE(top_n <= n_docs, KALM_ERR_INVALID_ARG, "kalm_rank_topn: top_n=%d > n_docs=%d", top_n, n_docs);
+  KALM_REQUIRE(n_docs <= 4096, KALM_ERR_UNSUPPORTED, "kalm_rank_topn: n_docs=%d > 4096", n_docs);
+  KALM_REQUIRE(n_queries == 0 || top_n == 0 || (score && out_index && out_score), KALM_ERR_INVALID_ARG,
+               "kalm_rank_topn: null pointer");
+  KALM_DEVICE_OR_RETURN();
+  if (n_queries == 0 || top_n == 0) return KALM_OK;
+  kalm::launch_rank_topn(score, n_queries, n_docs, top_n, out_index, out_score, (hipStream_t)stream);
+  return kalm::check_launch("kalm_rank_topn");
+}
+
 }  // extern "C"

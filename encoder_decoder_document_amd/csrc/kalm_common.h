@@ -55,16 +55,30 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void_t*)p;
 }
+// NT = true marks the data as streaming (non-temporal: the L2 evicts such
+// lines first), for operands read once per kernel so that they do not push
+// out data that is re-read, such as a GEMM's weight tiles.
+template <bool NT = false>
 __device__ __forceinline__ void dma16(uint64_t sbase, uint32_t voff, uint32_t lds_wave_base) {
   uint32_t saved;  // M0 is a compiler-reserved register: restore it after the copy is issued
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(lds_wave_base)
-      : "memory");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds_wave_base)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds_wave_base)
+        : "memory");
 }
 
 // Wait until the copies of the oldest in-flight k-tile are done: at most
@@ -120,6 +134,8 @@ void launch_merged_attn_f32(const float* Q, int64_t q_ld, const float* Ks, const
 void launch_yesno(const void* h, bool h_bf16, int64_t h_ld, int64_t rows, const int32_t* final_row, int P,
                   int H, const void* w, bool w_bf16, float* yes, float* no, float* margin, float* score,
                   hipStream_t s);
+void launch_rank_topn(const float* score, int n_queries, int D, int top_n, int32_t* out_index, float* out_score,
+                      hipStream_t s);
 void launch_gather_rows(const float* src, const int32_t* idx, int64_t M, int H, int64_t n_src,
                         float* dst, bf16_t* dst_bf16, hipStream_t s);
 }  // namespace kalm

@@ -1,4 +1,5 @@
-// a0 -- ragged pair layout, a4 -- yes/no readout, a5 -- residual-stream start.
+// a0 -- ragged pair layout, a4 -- yes/no readout, a5 -- residual-stream start,
+// and the ranking of each query's passages by score.
 //
 // Pair layout: every query reranks the same set of passages ("KaLM-Reranker-V1
 // -Nano -- MLX (Apple Silicon)", Speed), so pair p = (query p / D, doc p % D)
@@ -118,9 +119,50 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const float* __restric
   }
 }
 
+// One workgroup per query: the rank of passage i is the number of passages
+// that come before it in the order "higher score first, lower index first on
+// equal scores, NaN scores last (by index)" -- a total order, so the ranks are
+// a permutation and each passage writes itself to its rank if it is in the
+// top n.  Scores are staged in LDS; D <= 4096.
+constexpr int RANK_MAX_D = 4096;
+__global__ __launch_bounds__(256) void rank_topn_kernel(const float* __restrict__ score, int D, int top_n,
+                                                        int32_t* __restrict__ out_index,
+                                                        float* __restrict__ out_score) {
+  __shared__ float sc[RANK_MAX_D];
+  const int64_t q = blockIdx.x;
+  const float* s = score + q * D;
+  for (int i = threadIdx.x; i < D; i += blockDim.x) sc[i] = s[i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < D; i += blockDim.x) {
+    const float si = sc[i];
+    const bool ni = si != si;
+    int rank = 0;
+    for (int j = 0; j < D; ++j) {
+      const float sj = sc[j];
+      const bool nj = sj != sj;
+      bool before;
+      if (ni != nj) before = ni;                 // a number precedes every NaN
+      else if (ni) before = j < i;               // NaNs by index
+      else before = sj > si || (sj == si && j < i);
+      rank += before ? 1 : 0;
+    }
+    if (rank < top_n) {
+      out_index[q * top_n + rank] = i;
+      out_score[q * top_n + rank] = si;
+    }
+  }
+}
+
 }  // namespace
 
 namespace kalm {
+
+void launch_rank_topn(const float* score, int n_queries, int D, int top_n, int32_t* out_index, float* out_score,
+                      hipStream_t s) {
+  hipLaunchKernelGGL(rank_topn_kernel, dim3((unsigned)n_queries), dim3(256), 0, s, score, D, top_n, out_index,
+                     out_score);
+}
+
 
 void launch_pair_layout(const int32_t* lq, int nQ, int nD, int32_t* cu_q, int32_t* doc_of_pair,
                         int32_t* final_row, int32_t* h0_row, int64_t rows, hipStream_t s) {

@@ -42,6 +42,7 @@ _SIGS = {
     "kalm_yesno_score": (_i32, [_c_p, _i32, _i64, _i64, _c_p, _i32, _i32, _c_p, _i32, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "kalm_linear": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _i32, _c_p, _i32, _i32, _c_p, _c_p]),
     "kalm_gather_rows": (_i32, [_c_p, _c_p, _i64, _i32, _i64, _c_p, _c_p, _c_p]),
+    "kalm_rank_topn": (_i32, [_c_p, _i32, _i32, _i32, _c_p, _c_p, _c_p]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -245,3 +246,15 @@ def kalm_gather_rows(src: torch.Tensor, idx: torch.Tensor, dst: Optional[torch.T
     _check("kalm_gather_rows", load().kalm_gather_rows(_ptr(src), _ptr(idx), M, H, n_src, _ptr(dst), _ptr(dst_bf16),
                                                       _stream(stream)))
     return dst
+
+
+def kalm_rank_topn(score: torch.Tensor, top_n: int, stream=None):
+    """score [Q, D] float32 -> (index [Q, top_n] int32, score [Q, top_n] float32), best first."""
+    _contig(score)
+    Qn, D = score.shape
+    idx = torch.empty(Qn, top_n, dtype=torch.int32, device=score.device)
+    val = torch.empty(Qn, top_n, dtype=torch.float32, device=score.device)
+    _check("kalm_rank_topn", load().kalm_rank_topn(_ptr(score), Qn, D, top_n, _ptr(idx), _ptr(val),
+                                                  _stream(stream)))
+    return idx, val
+

@@ -222,6 +222,22 @@ kalm_status kalm_linear(const void* X, const void* W, int32_t M, int32_t K, int3
 kalm_status kalm_gather_rows(const float* src, const int32_t* idx, int64_t M, int32_t H,
                              int64_t n_src, float* dst, void* dst_bf16, void* stream);
 
+/*
+ * Ranking of each query's passages by relevance score, the step above the
+ * score: rerank(query, docs, top_n) returns the top_n passages highest score
+ * first as (index, relevance_score) ([MLX] What this is / Files: the
+ * rerank(query, docs, top_n) call; [Q4KM] Score a pair: rank larger margins
+ * first -- the score is monotone in the margin).
+ *   score      [n_queries, n_docs] float: row q holds query q's passage scores
+ *              (the kalm_yesno_score output in pair order q * n_docs + d)
+ *   out_index  [n_queries, top_n] int32 out: passage indices, best first
+ *   out_score  [n_queries, top_n] float out: their scores
+ * Order: higher score first; equal scores by lower index; NaN scores last (by
+ * index).  Requires 0 <= top_n <= n_docs <= 4096.
+ */
+kalm_status kalm_rank_topn(const float* score, int32_t n_queries, int32_t n_docs, int32_t top_n,
+                           int32_t* out_index, float* out_score, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,5 +18,5 @@ the functions; the model-level values of the real checkpoints are out of reach
 """
 from .kalm_ref import (  # noqa: F401
     round_bf16, round_f32, chunk_pool, cross_kv, merged_attn, merged_attn_partial,
-    yesno_score, pair_layout, decoder_stack, stack_scores,
+    yesno_score, rank_topn, pair_layout, decoder_stack, stack_scores,
 )

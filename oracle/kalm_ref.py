@@ -220,6 +220,31 @@ def yesno_score(h_final, w_yesno):
 
 
 # --------------------------------------------------------------------------
+# ranking of a query's passages (the step above the score)
+# --------------------------------------------------------------------------
+def rank_topn(scores, top_n: int):
+    """Top-n passages of each query, best first.
+
+    [MLX] What this is / Files: rerank(query, docs, top_n) returns the passages
+    highest relevance score first as (index, relevance_score); [Q4KM] Score a
+    pair: rank larger margins first (the score is increasing in the margin).
+    READING: equal scores keep input order (lower index first); NaN scores
+    (a pair with no valid score) go last, by index.
+
+    scores [Q, D] -> (index [Q, top_n] int, score [Q, top_n])
+    """
+    s = np.asarray(scores, dtype=F64)
+    Qn, D = s.shape
+    idx = np.zeros((Qn, top_n), dtype=np.int64)
+    val = np.zeros((Qn, top_n), dtype=F64)
+    for q in range(Qn):
+        order = sorted(range(D), key=lambda j: (math.isnan(s[q, j]), 0.0 if math.isnan(s[q, j]) else -s[q, j], j))
+        idx[q] = order[:top_n]
+        val[q] = s[q, order[:top_n]]
+    return idx, val
+
+
+# --------------------------------------------------------------------------
 # a0: ragged batch layout
 # --------------------------------------------------------------------------
 def pair_layout(lq: Sequence[int], n_docs: int):

@@ -334,3 +334,29 @@ def test_gather_rows_exact():
     assert np.array_equal(g[ok], src[idx[ok]])
     assert np.isnan(g[7]).all()
     assert torch.equal(dst_b.cpu()[torch.from_numpy(ok)], torch.from_numpy(src[idx[ok]]).to(torch.bfloat16))
+
+
+# ------------------------------------------------------------------ ranking above the score
+@pytest.mark.parametrize("Qn,D,top_n", [(5, 100, 10), (3, 100, 100), (2, 4096, 64), (1, 1, 1)])
+def test_rank_topn_exact(Qn, D, top_n):
+    _announce(f"rank_topn Q={Qn} D={D} top_n={top_n}")
+    rng = np.random.default_rng(D + top_n)
+    sc = (np.round(rng.random((Qn, D)) * 16) / 16).astype(np.float32)   # many equal scores
+    if D > 3:
+        sc[0, [1, D // 2, D - 1]] = np.nan
+    idx, val = ops.kalm_rank_topn(to_dev(sc, torch.float32), top_n)
+    r_idx, r_val = oracle.rank_topn(sc.astype(np.float64), top_n)
+    assert np.array_equal(to_np(idx), r_idx)
+    assert np.array_equal(to_np(val), r_val, equal_nan=True)
+
+
+def test_rerank_records_follow_the_ranking():
+    _announce("rerank records")
+    from encoder_decoder_document_amd import rerank
+    sc = np.array([0.2, 0.9, 0.2, 0.7, 0.5, 0.5], np.float32)       # 2 queries x 3 passages
+    out = rerank.rerank(to_dev(sc, torch.float32), 3, 2)
+    assert out == [[{"index": 1, "relevance_score": float(np.float32(0.9))},
+                    {"index": 0, "relevance_score": float(np.float32(0.2))}],
+                   [{"index": 0, "relevance_score": float(np.float32(0.7))},
+                    {"index": 1, "relevance_score": float(np.float32(0.5))}]]
+

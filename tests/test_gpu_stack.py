@@ -101,3 +101,17 @@ def test_stack_pruned_path_equals_full_path():
     ref = oracle.stack_scores(inp, pairs=pairs, mode="mirror")
     assert_close(pruned[np.asarray(pairs)], ref["score"], SCORE_ATOL, 0.0, "pruned score vs oracle")
 
+
+@pytest.mark.parametrize("chunk", [1, 2, 8, 16])
+def test_stack_matryoshka_chunk_sizes(chunk):
+    # the pooling granularity is a parameter of the path: every chunk size
+    # flows through pooling, cross K/V and the merged attention (Cmax = T / chunk)
+    import dataclasses
+    base = synth.SHAPES[2]
+    sh = dataclasses.replace(base, name=f"nano_chunk{chunk}", n_queries=2, n_layers=2, chunk=chunk)
+    print(f"[case] stack {sh.name}", flush=True)
+    inp = synth.make_inputs(0, seed=300 + chunk, shape=sh)
+    b, got = _run(inp)
+    assert b.Cmax == -(-sh.T // chunk)
+    _check(inp, b, got, _sample_pairs(inp, 10))
+

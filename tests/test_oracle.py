@@ -387,3 +387,31 @@ def test_stack_mirror_close_to_pure_on_bf16_shape():
     mirror = oracle.stack_scores(inp, mode="mirror")
     d = np.abs(pure["score"] - mirror["score"])
     assert d.max() < 5e-3 and d.max() > 0
+
+
+# ------------------------------------------------------------------ ranking
+def test_rank_worked_example():
+    ex = json.load(open(os.path.join(GOLD, "rank_worked_example.json")))
+    sc = np.array([[np.nan if v is None else v for v in row] for row in ex["scores"]])
+    idx, val = oracle.rank_topn(sc, ex["top_n"])
+    assert idx.tolist() == ex["index"]
+    assert np.array_equal(val, np.array(ex["relevance_score"]))
+
+
+def test_rank_is_a_stable_descending_permutation():
+    rng = np.random.default_rng(5)
+    sc = np.round(rng.random((7, 50)) * 8) / 8          # many ties
+    sc[2, [3, 9, 10]] = np.nan
+    idx, val = oracle.rank_topn(sc, 50)
+    for q in range(7):
+        assert sorted(idx[q].tolist()) == list(range(50))   # a permutation
+        finite = ~np.isnan(val[q])
+        assert np.all(np.diff(val[q][finite]) <= 0)         # non-increasing
+        assert not np.any(finite[np.argmin(finite):]) or finite.all()  # NaNs only at the end
+        for a in range(49):                                  # ties by index
+            if val[q, a] == val[q, a + 1] or (np.isnan(val[q, a]) and np.isnan(val[q, a + 1])):
+                assert idx[q, a] < idx[q, a + 1]
+    # numpy's stable argsort of the negated scores agrees where no NaN is present
+    ref = np.argsort(-sc[0], kind="stable")
+    assert np.array_equal(idx[0], ref)
+
