@@ -43,7 +43,15 @@ RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop/byte where the tw
 # sha256 of the source file the kernel was built from when the counters were
 # taken -- after any change to that file the traffic is reported as null.
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    # profiles/hbm_traffic_small_stack26_bf16.md
+    "o_linear": {"src": "fd5eb7414845840a34a0ebbd82b2cf7ea9722515f7cf965bff0fb7fda6bc9da5",
+                 "fetch_kib": 2953030.8, "write_kib": 6481559.6},
+    "qkv_linear": {"src": "fd5eb7414845840a34a0ebbd82b2cf7ea9722515f7cf965bff0fb7fda6bc9da5",
+                   "fetch_kib": 2387936.1, "write_kib": 2688305.4},
+    "merged_attn": {"src": "cebac1591ed9257c11a795ad71e64c15b8ac94be7dfbcf5982a89c3a0d3c1451",
+                    "fetch_kib": 1482533.5, "write_kib": 1792200.0},
+}
 KERNEL_SRC = {"o_linear": "gemm.hip", "qkv_linear": "gemm.hip", "cross_kv": "gemm.hip",
               "merged_attn": "attn.hip", "chunk_pool": "pool.hip", "gather_rows": "rows.hip"}
 
@@ -264,6 +272,10 @@ def main():
                 ent["mfma_frac"] = ent["tflops"] / (PEAK_BF16_TFLOPS if sh.dtype == "bf16" else PEAK_F32_TFLOPS)
             ent["gbs"] = w["bytes"] / (avg_us * 1e-6) / 1e9
             ent["hbm_frac"] = ent["gbs"] / PEAK_HBM_GBS
+        tb = traffic_bytes(k)
+        if tb is not None:
+            ent["hbm_traffic_bytes"] = tb
+            ent["traffic_over_algorithmic"] = tb / work[k]["bytes"] if k in work else None
         kernels[k] = ent
     dom = max((k for k in kernels if k in work), key=lambda k: kernels[k]["total_ms_per_step"])
     w = work[dom]
