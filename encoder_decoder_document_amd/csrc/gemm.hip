@@ -32,6 +32,9 @@ enum Epi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_ACC = 2 };
 #ifndef GEMM_STREAM_X
 #define GEMM_STREAM_X false
 #endif
+#ifndef GEMM_KREV
+#define GEMM_KREV 1
+#endif
 #ifndef GEMM_STREAM_Y
 #define GEMM_STREAM_Y true
 #endif
@@ -165,10 +168,15 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
   planA.init(X, M, K, m0, wave, lane);
   planB.init(W, N, K, n0, wave, lane);
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-  auto issue = [&](int kt) {  // k-tile kt into ring slot kt % STAGES
-    const uint32_t b = lds_base + (uint32_t)((kt % STAGES) * STAGE_ELEMS * 2);
-    planA.issue(b, kt * BK, K);
-    planB.issue(b + BM * BK * 2, kt * BK, K);
+  // k order: each round of co-resident workgroups (256 per CU slot) walks k
+  // in the opposite direction to the previous round, so the weight k-tiles it
+  // needs first are the ones the previous round used last (still in L2).
+  const bool krev = GEMM_KREV && ((blockIdx.x / (256 * (OCC >= 4 ? OCC / 2 : 1))) & 1);
+  auto kidx = [&](int i) { return krev ? nk - 1 - i : i; };
+  auto issue = [&](int i) {  // the i-th k-tile in walk order into ring slot i % STAGES
+    const uint32_t b = lds_base + (uint32_t)((i % STAGES) * STAGE_ELEMS * 2);
+    planA.issue(b, kidx(i) * BK, K);
+    planB.issue(b + BM * BK * 2, kidx(i) * BK, K);
   };
 
   const int r = lane & 31, g = lane >> 5;
@@ -179,9 +187,9 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
     wait_dma_ktile<CPS>(min(nk - 1 - kt, STAGES - 2));
     __syncthreads();  // k-tile kt visible to all waves; slot of k-tile kt-1 free
     bf16_t* cur = smem + (kt % STAGES) * STAGE_ELEMS;
-    if (k_tail && kt == nk - 1) {
-      zero_k_tail<BM, BK>(cur, kt * BK, K, tid, NT);
-      zero_k_tail<BN, BK>(cur + BM * BK, kt * BK, K, tid, NT);
+    if (k_tail && kidx(kt) == nk - 1) {
+      zero_k_tail<BM, BK>(cur, kidx(kt) * BK, K, tid, NT);
+      zero_k_tail<BN, BK>(cur + BM * BK, kidx(kt) * BK, K, tid, NT);
       __syncthreads();
     }
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
