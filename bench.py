@@ -53,7 +53,7 @@ MEASURED_TRAFFIC = {
                     "fetch_kib": 1482533.5, "write_kib": 1792200.0},
 }
 KERNEL_SRC = {"o_linear": "gemm.hip", "qkv_linear": "gemm.hip", "cross_kv": "gemm.hip",
-              "merged_attn": "attn.hip", "chunk_pool": "pool.hip", "gather_rows": "rows.hip"}
+              "merged_attn": "attn_bf16.h", "chunk_pool": "pool.hip", "gather_rows": "rows.hip"}
 
 
 def traffic_bytes(kernel):
