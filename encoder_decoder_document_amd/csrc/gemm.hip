@@ -32,6 +32,9 @@ enum Epi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_ACC = 2 };
 #ifndef GEMM_STREAM_X
 #define GEMM_STREAM_X false
 #endif
+#ifndef GEMM_PERSIST
+#define GEMM_PERSIST 1
+#endif
 #ifndef GEMM_KREV
 #define GEMM_KREV 1
 #endif
@@ -267,6 +270,162 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
   }
 }
 
+// Persistent variant for large problems: a grid of (256 x workgroups per CU)
+// workgroups, each walking its output tiles in rounds (round k: every XCD
+// holds 32 consecutive tiles, so tiles that share activation rows run side by
+// side).  The LDS ring continues across tiles: the first k-tile of the next
+// tile is copied while the current tile's epilogue runs, so no tile starts
+// on a cold pipeline.  The epilogue parks each wave's fp32 accumulator in the
+// ring slot just consumed (32 rows x WTN, 16-byte chunks XOR-swizzled by row),
+// which the in-flight copy does not touch.
+template <int BM, int BN, int WM, int WN, int BK, int OCC>
+__global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_persistent(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, int M, int K, int N, void* __restrict__ Y, int epi,
+    bf16_t* __restrict__ Ybf) {
+  constexpr int STAGES = 2;
+  constexpr int NW = WM * WN;
+  constexpr int NT = NW * 64;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int STAGE_ELEMS = (BM + BN) * BK;
+  constexpr int CPR = BK / 8, RPI_D = 64 / CPR;   // copy plan: chunks per row, rows per instruction
+  constexpr int PER_A = BM / RPI_D / NW, PER_B = BN / RPI_D / NW;
+  constexpr int CPS = PER_A + PER_B;             // copies per thread per k-tile
+  static_assert(NW * 32 * WTN * 4 <= STAGE_ELEMS * 2, "a wave's parked rows fit one ring slot");
+  static_assert(WTN % 64 == 0, "park swizzle: rows of 16 or 32 chunks");
+
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGES * STAGE_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  const int r = lane & 31, g = lane >> 5;
+
+  const int tiles_n = (N + BN - 1) / BN;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int total = tiles_m * tiles_n;
+  const int grid = gridDim.x;                    // a multiple of 8
+  const int per = total / 8;
+  auto tile_of = [&](int vb) { return (vb < per * 8) ? (vb % 8) * per + vb / 8 : vb; };
+  const int nk = (K + BK - 1) / BK;
+  const bool k_tail = (K % BK) != 0;
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+
+  // copy the k-tile of index kk (k0 = kk * BK) of output tile t into ring slot `slot`
+  auto issue = [&](int t, int kk, int slot) {
+    const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
+    const uint32_t b = lds_base + (uint32_t)(slot * STAGE_ELEMS * 2);
+    const int rr = lane / CPR;
+    const int k0 = kk * BK;
+    const uint64_t xa = uniform64((uint64_t)(uintptr_t)(X + (int64_t)m0 * K));
+    const uint64_t wa = uniform64((uint64_t)(uintptr_t)(W + (int64_t)n0 * K));
+#pragma unroll
+    for (int j = 0; j < PER_A + PER_B; ++j) {
+      const bool isA = j < PER_A;
+      const int jj = isA ? j : j - PER_A;
+      const int R0 = RPI_D * (wave * (isA ? PER_A : PER_B) + jj);
+      const int row = isA ? min(m0 + R0 + rr, M - 1) - m0 : min(n0 + R0 + rr, N - 1) - n0;
+      int kk8 = k0 + swz<BK>(R0 + rr, lane % CPR) * 8;
+      if (kk8 >= K) kk8 = 0;  // in-bounds dummy; zeroed in LDS by zero_k_tail
+      const uint32_t off = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)kk8 * 2u;
+      const uint32_t dst = b + (isA ? 0u : (uint32_t)(BM * BK * 2)) + (uint32_t)__builtin_amdgcn_readfirstlane(R0 * BK * 2);
+      dma16(isA ? xa : wa, off, dst);
+    }
+  };
+
+  int vb = blockIdx.x;
+  if (vb >= total) return;
+  int gk = 0;  // k-tiles consumed by this workgroup (ring position)
+  for (int kt = 0; kt < STAGES - 1 && kt < nk; ++kt) issue(tile_of(vb), kt, kt % STAGES);
+  for (int round = 0; vb < total; ++round, vb += grid) {
+    const int t = tile_of(vb);
+    const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
+    const int vb_next = vb + grid;
+    const bool has_next = vb_next < total;
+    f32x16_t acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    for (int kt = 0; kt < nk; ++kt, ++gk) {
+      // this k-tile's copies (issued one step earlier) are complete; vmcnt also
+      // counts the previous tile's epilogue stores, which are waited for here
+      wait_dma_ktile<CPS>(0);
+      __syncthreads();  // k-tile visible to all waves; the other slot is free
+      bf16_t* cur = smem + (gk % STAGES) * STAGE_ELEMS;
+      if (k_tail && kt == nk - 1) {
+        zero_k_tail<BM, BK>(cur, kt * BK, K, tid, NT);
+        zero_k_tail<BN, BK>(cur + BM * BK, kt * BK, K, tid, NT);
+        __syncthreads();
+      }
+      if (kt + 1 < nk) issue(t, kt + 1, (gk + 1) % STAGES);
+      else if (has_next) issue(tile_of(vb_next), 0, (gk + 1) % STAGES);
+      const bf16_t* a = cur;
+      const bf16_t* bb = cur + BM * BK;
+#pragma unroll
+      for (int s = 0; s < BK / 16; ++s) {
+        const int kc = 2 * s + g;
+        bf16x8_t xf[FM], wf[FN];
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          const int row = wm * WTM + j * 32 + r;
+          xf[j] = *(const bf16x8_t*)(a + row * BK + (swz<BK>(row, kc) << 3));
+        }
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          const int row = wn * WTN + i * 32 + r;
+          wf[i] = *(const bf16x8_t*)(bb + row * BK + (swz<BK>(row, kc) << 3));
+        }
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+          for (int j = 0; j < FM; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    // ---- epilogue: park in the slot just consumed ((gk - 1) % STAGES); the
+    // copy in flight targets the other slot
+    __syncthreads();  // every wave is done reading the consumed slot
+    float* park = (float*)(smem + ((gk - 1) % STAGES) * STAGE_ELEMS) + wave * (32 * WTN);
+    constexpr int LPR = WTN / 4;  // lanes per row (16 bytes of fp32 each) = 16 chunks
+    constexpr int RPI = 64 / LPR;
+    const int prow = lane / LPR, pch = lane % LPR;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ch = (8 * i + 2 * q + g) ^ (r & 15);
+          *(f32x4_t*)(park + r * WTN + ch * 4) =
+              f32x4_t{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int n = n0 + wn * WTN + pch * 4;
+#pragma unroll
+      for (int rr = 0; rr < 32; rr += RPI) {
+        const int prr = rr + prow;
+        const int m = m0 + wm * WTM + j * 32 + prr;
+        f32x4_t v = *(const f32x4_t*)(park + prr * WTN + ((pch ^ (prr & 15)) * 4));
+        if (m < M && n < N) {
+          const int64_t off = (int64_t)m * N + n;
+          if (epi == EPI_BF16) {
+            st_out((u32x2_t*)((bf16_t*)Y + off), u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+          } else {
+            f32x4_t* yp = (f32x4_t*)((float*)Y + off);
+            if (epi == EPI_F32_ACC) v += ld_out(yp);
+            st_out(yp, v);
+            if (Ybf) st_out((u32x2_t*)(Ybf + off), u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
 // fp32 path (the small fp32 sanity workload): 64x64 tiles, 4x4 outputs per thread.
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ X,
                                                        const float* __restrict__ W, int M, int K,
@@ -330,6 +489,12 @@ void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, v
     const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 64, 2, 4>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y,
                        epi, Y_bf16, rmask);
+  } else if (big_tiles >= 512 && GEMM_PERSIST) {
+    // persistent 256 x 256 tiles, one workgroup per CU
+    const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    const int grid = tiles < 256 ? ((tiles + 7) / 8) * 8 : 256;
+    hipLaunchKernelGGL((gemm_bf16_persistent<256, 256, 2, 4, 64, 1>), dim3(grid), dim3(512), 0, s, X, W, M, K, N, Y,
+                       epi, Y_bf16);
   } else if (big_tiles >= 512) {
     // 256 x 256 tiles, k-tiles of 64 (every copied row a whole 128-byte line), two-slot ring
     const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
