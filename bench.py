@@ -162,6 +162,21 @@ def work_model(inp, sh):
     }
 
 
+def attn_summary(kernels, work, sh):
+    """All merged-attention launches of a step together (every row mode): useful
+    flops and algorithmic bytes over their summed time."""
+    names = [k for k in kernels if k.startswith("merged_attn") and k in work]
+    t = sum(kernels[k]["total_ms_per_step"] for k in names) * 1e-3
+    if not names or t <= 0:
+        return None
+    fl = sum(work[k]["flops"] * kernels[k]["launches_per_step"] for k in names)
+    by = sum(work[k]["bytes"] * kernels[k]["launches_per_step"] for k in names)
+    peak = PEAK_BF16_TFLOPS if sh.dtype == "bf16" else PEAK_F32_TFLOPS
+    return {"launches_per_step": sum(kernels[k]["launches_per_step"] for k in names), "ms_per_step": t * 1e3,
+            "tflops": fl / t / 1e12, "mfma_frac": fl / t / 1e12 / peak, "gbs": by / t / 1e9,
+            "hbm_frac": by / t / 1e9 / PEAK_HBM_GBS}
+
+
 def cpu_baseline(inp, sh, budget_s):
     import threadpoolctl
     import oracle
@@ -300,7 +315,7 @@ def main():
                    "decoder_rows": b.rows, "pruned_first_last_layer": not a.no_prune,
                    "parallelism": "single GPU"},
         "roofline": roof,
-        "merged_attn": {k: kernels["merged_attn"].get(k) for k in ("avg_us", "tflops", "mfma_frac", "gbs", "hbm_frac")},
+        "merged_attn": attn_summary(kernels, work, sh),
         "kernels": kernels,
     }
     if not a.no_pool_long:
