@@ -32,6 +32,12 @@ enum Epi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_ACC = 2 };
 #ifndef GEMM_STREAM_X
 #define GEMM_STREAM_X false
 #endif
+#ifndef GEMM_PF_DIST
+#define GEMM_PF_DIST 1  // k-tiles before the last at whose start the fp32 stream is loaded
+#endif
+#ifndef GEMM_PF_Y
+#define GEMM_PF_Y true
+#endif
 #ifndef GEMM_PERSIST
 #define GEMM_PERSIST 1
 #endif
@@ -119,7 +125,11 @@ __device__ __forceinline__ void zero_k_tail(bf16_t* tile, int k0, int K, int tid
 // WM x WN waves split the block tile BM x BN; k advances BK per stage and
 // STAGES k-tiles live in the LDS ring (STAGES - 1 in flight while one feeds
 // the MFMAs); OCC = waves per SIMD it is built for (bounds the registers).
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int OCC, bool STREAM_X = GEMM_STREAM_X>
+// PF_Y (residual update only): the fp32 values the epilogue adds to are loaded
+// into registers while the last k-tile is copied and multiplied, so their
+// memory latency is hidden instead of being paid after the k-loop.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int OCC, bool PF_Y = false,
+          bool STREAM_X = GEMM_STREAM_X>
 __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, int M, int K, int N,
     void* __restrict__ Y, int epi, bf16_t* __restrict__ Ybf, const uint8_t* __restrict__ rmask) {
@@ -183,11 +193,31 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
   };
 
   const int r = lane & 31, g = lane >> 5;
+  // epilogue geometry: a wave's accumulator leaves in row segments of WTN
+  // columns, LPR lanes per row, RPI rows per instruction
+  constexpr int LPR = WTN / 4;
+  constexpr int RPI = 64 / LPR;
+  constexpr int NY = FM * (32 / RPI);  // 16-byte pieces of the fp32 stream per lane (PF_Y)
+  const int prow = lane / LPR, pcol = (lane % LPR) * 4;
+  f32x4_t yold[PF_Y ? NY : 1];
+  auto load_yold = [&]() {
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int rr = 0; rr < 32; rr += RPI) {
+        const int m = m0 + wm * WTM + j * 32 + rr + prow, n = n0 + wn * WTN + pcol;
+        yold[j * (32 / RPI) + rr / RPI] =
+            (m < M && n < N) ? ld_out((const f32x4_t*)((const float*)Y + (int64_t)m * N + n)) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+  };
   for (int kt = 0; kt < STAGES - 1 && kt < nk; ++kt) issue(kt);
   for (int kt = 0; kt < nk; ++kt) {
     // this thread's copies of k-tile kt are done once at most those of the
-    // (up to two) later k-tiles already issued are outstanding
-    wait_dma_ktile<CPS>(min(nk - 1 - kt, STAGES - 2));
+    // (up to two) later k-tiles already issued are outstanding -- and, at the
+    // last k-tile with PF_Y, the NY loads of the fp32 stream issued after them
+    if (PF_Y && kt == nk - GEMM_PF_DIST && kt >= 1 && STAGES == 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NY) : "memory");  // the copy is older than the NY loads
+    else wait_dma_ktile<CPS>(min(nk - 1 - kt, STAGES - 2));
     __syncthreads();  // k-tile kt visible to all waves; slot of k-tile kt-1 free
     bf16_t* cur = smem + (kt % STAGES) * STAGE_ELEMS;
     if (k_tail && kidx(kt) == nk - 1) {
@@ -196,6 +226,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
       __syncthreads();
     }
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    if (PF_Y && kt == max(nk - 1 - GEMM_PF_DIST, 0)) load_yold();
     const bf16_t* a = cur;
     const bf16_t* bb = cur + BM * BK;
 #pragma unroll
@@ -232,9 +263,6 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
   static_assert(EP_ROUNDS <= 2 && NW % EP_ROUNDS == 0, "epilogue staging fits the ring in two rounds");
   __syncthreads();  // every wave is done reading the ring
   float* park = (float*)smem + (wave / EP_ROUNDS) * (32 * EP_LD);
-  constexpr int LPR = WTN / 4;          // lanes per row (16 bytes of fp32 each)
-  constexpr int RPI = 64 / LPR;         // rows per wave instruction
-  const int prow = lane / LPR, pcol = (lane % LPR) * 4;
 #pragma unroll
   for (int round = 0; round < EP_ROUNDS; ++round) {
   if (EP_ROUNDS > 1 && round > 0) __syncthreads();  // the previous round's waves are done with the area
@@ -260,7 +288,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
           st_out((u32x2_t*)((bf16_t*)Y + off), u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
         } else {
           f32x4_t* yp = (f32x4_t*)((float*)Y + off);
-          if (epi == EPI_F32_ACC) v += ld_out(yp);
+          if (epi == EPI_F32_ACC) v += PF_Y ? yold[j * (32 / RPI) + rr / RPI] : ld_out(yp);
           st_out(yp, v);
           if (Ybf) st_out((u32x2_t*)(Ybf + off), u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
         }
@@ -487,8 +515,8 @@ void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, v
     // residual update (reads and writes the fp32 stream): 128 x 128 tiles,
     // two workgroups per CU, so one's epilogue traffic overlaps the other's k-loop
     const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 64, 2, 4>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y,
-                       epi, Y_bf16, rmask);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 64, 2, 4, GEMM_PF_Y>), dim3(tiles), dim3(512), 0, s, X, W, M,
+                       K, N, Y, epi, Y_bf16, rmask);
   } else if (big_tiles >= 512 && GEMM_PERSIST) {
     // persistent 256 x 256 tiles, one workgroup per CU
     const int tiles = ((M + 255) / 256) * ((N + 255) / 256);

@@ -123,7 +123,7 @@ def test_cross_kv_parity(D, C, H, kv, bf16):
                                         (130, 64, 96, "f32"), (33, 36, 20, "f32acc"),
                                         # large enough for the big-tile paths (>= 512 tiles of 256 x 256),
                                         # ragged in M, and a K that is not a multiple of 64
-                                        (22093, 1152, 1536, "bf16"), (22093, 1024, 1152, "acc"),
+                                        (22093, 1152, 1536, "bf16"), (22093, 1024, 1152, "acc"), (40003, 1024, 1152, "acc"),
                                         (88001, 1000, 1536, "bf16")])
 def test_linear_parity(M, K, N, mode):
     _announce(f"linear M={M} K={K} N={N} mode={mode}")
