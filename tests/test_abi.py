@@ -72,6 +72,18 @@ def test_invalid_arguments_rejected_before_launch():
     # misaligned pointer
     st = lib.kalm_gather_rows(8, 16, 4, 8, 4, 16, None, None)
     assert st == ops.KALM_ERR_INVALID_ARG
+    # attention over a choice of rows: unknown row mode; shared rows without passages
+    st = lib.kalm_merged_attn_rows(None, 1024, 0, None, None, 512, 0, None, 0, 0, None, None, 512, None, None, 0, 0,
+                                   4, 1, 256, 0.1, ops.KALM_BF16, None, 1024, 0, None, 3, None)
+    assert st == ops.KALM_ERR_INVALID_ARG and b"row_mode" in lib.kalm_last_error()
+    st = lib.kalm_merged_attn_rows(None, 1024, 0, None, None, 512, 0, None, 1, 0, None, None, 512, None, None, 0, 0,
+                                   4, 1, 256, 0.1, ops.KALM_BF16, None, 1024, 0, None, 2, None)
+    assert st == ops.KALM_ERR_INVALID_ARG
+    # ranking: top_n larger than the passages; too many passages for one workgroup
+    st = lib.kalm_rank_topn(None, 1, 10, 11, None, None, None)
+    assert st == ops.KALM_ERR_INVALID_ARG and b"top_n" in lib.kalm_last_error()
+    st = lib.kalm_rank_topn(None, 1, 5000, 10, None, None, None)
+    assert st == ops.KALM_ERR_UNSUPPORTED
 
 
 @needs_lib
