@@ -383,7 +383,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_persistent(
   if (vb >= total) return;
   int gk = 0;  // k-tiles consumed by this workgroup (ring position)
   for (int kt = 0; kt < STAGES - 1 && kt < nk; ++kt) issue(tile_of(vb), kt, kt % STAGES);
-  for (int round = 0; vb < total; ++round, vb += grid) {
+  for (; vb < total; vb += grid) {
     const int t = tile_of(vb);
     const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
     const int vb_next = vb + grid;
