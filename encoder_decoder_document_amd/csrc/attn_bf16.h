@@ -305,6 +305,15 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
     issue(v, true);
   }
   for (int v = VR - 1; v < KR - 1 && v < n_tiles; ++v) issue(v, true);
+  // Make the Q loads complete here, visibly to the compiler: its wait-count
+  // pass does not see the asm copies, and would otherwise keep waiting for
+  // "the Q loads" inside the tile loop with vmcnt values that, on the
+  // hardware counter, also cover the next tile's copies -- serialising every
+  // tile's copy with its compute.
+#pragma unroll
+  for (int u = 0; u < RT; ++u)
+#pragma unroll
+    for (int s = 0; s < HD / 16; ++s) asm volatile("" ::"v"(qf[u][s]));
   for (int v = 0; v < n_tiles; ++v) {
     if (KR == VR) wait_dma_ktile<2 * CPT>(min(n_tiles - 1 - v, VR - 2));
     else wait_dma_ktile<CPT>(min(n_tiles - 1 - v, KR - VR));  // K(v+1) may still be in flight
