@@ -81,6 +81,8 @@ def parse():
                     help="pooling granularity in tokens (Matryoshka variants); default: the workload's (4)")
     ap.add_argument("--no-prune", action="store_true",
                     help="compute every row of the first and last layers (no shared / final-row shortcut)")
+    ap.add_argument("--no-reuse-self", action="store_true",
+                    help="first layer in one merged pass per pair instead of each query's self part once")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     ap.add_argument("--no-pool-long", action="store_true", help="skip the pooling measurement at the 1024x2560 shape")
@@ -145,6 +147,14 @@ def work_model(inp, sh):
         "merged_attn": dict(flops=float(attn_flops), bytes=float(2 * rows * qd * e + self_bytes + cross_bytes)),
         "merged_attn_first": dict(flops=float(attn_flops),
                                   bytes=float(U * qd * e + rows * qd * e + 2 * U * kv * e + cross_bytes)),
+        # first layer split at the self/cross boundary: each query's causal self
+        # part once (fp32 output and lse), then every pair's cross part resumed
+        # from it
+        "self_attn_first": dict(flops=float(4 * nq * d * self_keys // D),
+                                bytes=float(U * qd * e + 2 * U * kv * e + U * qd * 4 + U * nq * 4)),
+        "merged_attn_first_resume": dict(flops=float(4 * nq * d * cross_keys),
+                                         bytes=float(U * qd * e + U * qd * 4 + U * nq * 4 + cross_bytes
+                                                     + rows * qd * e)),
         "merged_attn_last": dict(flops=float(last_flops), bytes=float(2 * P * qd * e + self_bytes + cross_bytes)),
         "qkv_linear": linear(rows, H, nqkv, rows * nqkv * e),
         "qkv_linear_first": linear(U, H, nqkv, U * nqkv * e),
@@ -163,9 +173,10 @@ def work_model(inp, sh):
 
 
 def attn_summary(kernels, work, sh):
-    """All merged-attention launches of a step together (every row mode): useful
+    """All merged-attention launches of a step together (every row mode, and
+    the self and resumed parts of a split first layer): useful
     flops and algorithmic bytes over their summed time."""
-    names = [k for k in kernels if k.startswith("merged_attn") and k in work]
+    names = [k for k in kernels if (k.startswith("merged_attn") or k.startswith("self_attn")) and k in work]
     t = sum(kernels[k]["total_ms_per_step"] for k in names) * 1e-3
     if not names or t <= 0:
         return None
@@ -261,12 +272,12 @@ def main():
     rec = EventRec(torch)
     rec.on = False
     for _ in range(a.warmup):
-        stack.step(b, rec=rec, prune=not a.no_prune)
+        stack.step(b, rec=rec, prune=not a.no_prune, reuse_self=not a.no_reuse_self)
     torch.cuda.synchronize()
     rec.on = True
     t0 = time.perf_counter()
     for i in range(a.steps):
-        stack.step(b, rec=rec, prune=not a.no_prune)
+        stack.step(b, rec=rec, prune=not a.no_prune, reuse_self=not a.no_reuse_self)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_step = el / a.steps * 1e3
@@ -313,6 +324,7 @@ def main():
                    "layers": sh.n_layers, "hidden": sh.H, "q_heads": sh.nq, "kv_heads": sh.nkv, "head_dim": sh.d,
                    "decoder_len": list(sh.lq), "passage_len": list(sh.doc_len), "chunk": sh.chunk,
                    "decoder_rows": b.rows, "pruned_first_last_layer": not a.no_prune,
+                   "first_layer_self_once_per_query": not a.no_prune and not a.no_reuse_self,
                    "parallelism": "single GPU"},
         "roofline": roof,
         "merged_attn": attn_summary(kernels, work, sh),

@@ -9,14 +9,17 @@ namespace {
 
 // fp32 path (the small fp32 workload): one wavefront per (pair, head, row),
 // lanes split the head dim, one online-softmax state per row walking the
-// causal self keys and then the valid cross keys.
+// causal self keys and then the valid cross keys.  part 1 walks the self keys
+// only (a self partial); part 2 walks the cross keys only, starting from the
+// self partial (oi, lsei) of the Q row: m = lse, l = 1, acc = o.
 __global__ __launch_bounds__(256) void merged_attn_f32_kernel(
     const float* __restrict__ Q, int64_t q_ld, const float* __restrict__ Ks,
     const float* __restrict__ Vs, int64_t kv_ld, const int32_t* __restrict__ cu_q, int64_t q_rows,
     int64_t kv_rows, int64_t o_rows, int mode, const float* __restrict__ Kc, const float* __restrict__ Vc, int64_t c_ld,
     const uint8_t* __restrict__ cmask, const int32_t* __restrict__ doc_of_pair, int D, int Cmax,
     int nq, int nkv, int d, float scale, float* __restrict__ O, int64_t o_ld,
-    float* __restrict__ lse, int nrb) {
+    float* __restrict__ lse, int nrb, int part, const float* __restrict__ oi, int64_t oi_ld,
+    const float* __restrict__ lsei) {
   const int lane = threadIdx.x & 63;
   const int64_t blk = blockIdx.x;
   const int i = (int)(blk % nrb) * 4 + (threadIdx.x >> 6);
@@ -26,8 +29,8 @@ __global__ __launch_bounds__(256) void merged_attn_f32_kernel(
   if (!pr.ok || i >= pr.nrow) return;
   const int pos = pr.pos0 + i;  // self position of this query row
   const int kvh = h / (nq / nkv);
-  const int doc = doc_of_pair[p];
-  const bool bad_doc = doc < 0 || doc >= D;
+  const int doc = part == 1 ? 0 : doc_of_pair[p];
+  const bool bad_doc = part != 1 && (doc < 0 || doc >= D);
   constexpr int MAXJ = 4;  // d <= 256
   const int nj = (d + 63) / 64;
   float q[MAXJ], acc[MAXJ];
@@ -35,9 +38,13 @@ __global__ __launch_bounds__(256) void merged_attn_f32_kernel(
   for (int j = 0; j < MAXJ; ++j) {
     const int e = lane + 64 * j;
     q[j] = (j < nj && e < d) ? Q[(pr.q0 + i) * q_ld + (int64_t)h * d + e] : 0.f;
-    acc[j] = 0.f;
+    acc[j] = (part == 2 && j < nj && e < d) ? oi[(pr.q0 + i) * oi_ld + (int64_t)h * d + e] : 0.f;
   }
   float m = -INFINITY, l = 0.f;
+  if (part == 2) {
+    m = lsei[(pr.q0 + i) * nq + h];
+    l = 1.f;
+  }
   auto visit = [&](const float* krow, const float* vrow) {
     float part = 0.f;
 #pragma unroll
@@ -47,7 +54,7 @@ __global__ __launch_bounds__(256) void merged_attn_f32_kernel(
     }
     const float s = wave_sum(part) * scale;
     const float m_new = fmaxf(m, s);
-    const float alpha = expf(m - m_new);
+    const float alpha = expf(m - m_new);  // expf(-inf) = 0 on the first key
     const float pw = expf(s - m_new);
     l = l * alpha + pw;
 #pragma unroll
@@ -58,9 +65,10 @@ __global__ __launch_bounds__(256) void merged_attn_f32_kernel(
     }
     m = m_new;
   };
-  for (int jk = 0; jk <= pos; ++jk)
-    visit(Ks + (pr.kv0 + jk) * kv_ld + (int64_t)kvh * d, Vs + (pr.kv0 + jk) * kv_ld + (int64_t)kvh * d);
-  if (!bad_doc)
+  if (part != 2)
+    for (int jk = 0; jk <= pos; ++jk)
+      visit(Ks + (pr.kv0 + jk) * kv_ld + (int64_t)kvh * d, Vs + (pr.kv0 + jk) * kv_ld + (int64_t)kvh * d);
+  if (part != 1 && !bad_doc)
     for (int c = 0; c < Cmax; ++c)
       if (cmask[(int64_t)doc * Cmax + c])
         visit(Kc + ((int64_t)doc * Cmax + c) * c_ld + (int64_t)kvh * d,
@@ -82,22 +90,25 @@ void launch_merged_attn_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, co
                              int64_t kv_ld, const int32_t* cu_q, int P, int64_t q_rows, int64_t kv_rows,
                              int64_t o_rows, int mode, int max_lq, const bf16_t* Kc, const bf16_t* Vc,
                              int64_t c_ld, const uint8_t* cmask, const int32_t* doc_of_pair, int D, int Cmax,
-                             int nq, int nkv, float scale, bf16_t* O, int64_t o_ld, float* lse, hipStream_t s) {
+                             int nq, int nkv, float scale, void* O, int64_t o_ld, float* lse, int part,
+                             const float* oi, int64_t oi_ld, const float* lsei, hipStream_t s) {
   launch_bf16<ATTN_WAVES, 1>(Q, q_ld, Ks, Vs, kv_ld, cu_q, P, q_rows, kv_rows, o_rows, mode, max_lq, Kc, Vc, c_ld,
-                             cmask, doc_of_pair, D, Cmax, nq, nkv, scale, O, o_ld, lse, s);
+                             cmask, doc_of_pair, D, Cmax, nq, nkv, scale, O, o_ld, lse, part, oi, oi_ld, lsei, s);
 }
 
 void launch_merged_attn_f32(const float* Q, int64_t q_ld, const float* Ks, const float* Vs,
                             int64_t kv_ld, const int32_t* cu_q, int P, int64_t q_rows, int64_t kv_rows,
                             int64_t o_rows, int mode, int max_lq, const float* Kc, const float* Vc, int64_t c_ld,
                             const uint8_t* cmask, const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv,
-                            int d, float scale, float* O, int64_t o_ld, float* lse, hipStream_t s) {
+                            int d, float scale, float* O, int64_t o_ld, float* lse, int part, const float* oi,
+                            int64_t oi_ld, const float* lsei, hipStream_t s) {
   const int max_rows = mode == 1 ? 1 : max_lq;
   if (P == 0 || max_rows == 0) return;
   const int nrb = (max_rows + 3) / 4;  // 4 rows (one per wave) per block
   const dim3 grid((unsigned)((int64_t)nrb * nq * P)), block(256);
   hipLaunchKernelGGL(merged_attn_f32_kernel, grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, q_rows, kv_rows,
-                     o_rows, mode, Kc, Vc, c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, d, scale, O, o_ld, lse, nrb);
+                     o_rows, mode, Kc, Vc, c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, d, scale, O, o_ld, lse, nrb, part,
+                     oi, oi_ld, lsei);
 }
 
 }  // namespace kalm

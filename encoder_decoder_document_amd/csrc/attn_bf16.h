@@ -123,14 +123,24 @@ __device__ __forceinline__ PairRows pair_rows(const int32_t* __restrict__ cu_q, 
 // staged in LDS is shared by 32 * RT * NW (row, head) query vectors, and with
 // RT = 2 every K and V fragment read from LDS feeds two MFMAs (two
 // independent accumulation chains).
-template <int NH, int NW, int RT, int MODE>
+//
+// PART selects which keys the softmax walks (the merged softmax split at the
+// self/cross boundary and put back together by log-sum-exp weights):
+//   0  self then cross keys: the merged attention, bf16 output;
+//   1  the causal self keys only (plain causal self-attention): fp32 output
+//      O and its lse -- a self partial;
+//   2  the cross keys only, starting from a self partial (oi, lsei) read at
+//      the Q row: the online state begins at m = lse, l = 1, acc = o, which is
+//      the state the walk over the self keys would have left; bf16 output.
+template <int NH, int NW, int RT, int MODE, int PART>
 __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_kernel(
     const bf16_t* __restrict__ Q, int64_t q_ld, const bf16_t* __restrict__ Ks,
     const bf16_t* __restrict__ Vs, int64_t kv_ld, const int32_t* __restrict__ cu_q, int P,
     int64_t q_rows, int64_t kv_rows, int64_t o_rows, int nqb, const bf16_t* __restrict__ Kc,
     const bf16_t* __restrict__ Vc, int64_t c_ld, const uint8_t* __restrict__ cmask,
     const int32_t* __restrict__ doc_of_pair, int D, int Cmax, int nq, int nkv, float scale_log2,
-    bf16_t* __restrict__ O, int64_t o_ld, float* __restrict__ lse) {
+    void* __restrict__ Ov, int64_t o_ld, float* __restrict__ lse, const float* __restrict__ oi, int64_t oi_ld,
+    const float* __restrict__ lsei) {
   constexpr int WPH = NW / NH;            // row blocks per head
   constexpr int RB = 32 * RT * WPH;       // decoder rows per block
   // K and V rings: 2 deep for RT = 1 with 4 waves (two workgroups per CU,
@@ -167,13 +177,13 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   const PairRows pr = pair_rows(cu_q, p, D, MODE, q_rows, kv_rows, o_rows);
   if (!pr.ok || qb * RB >= pr.nrow) return;
   const int Lq = pr.Lq, nrow = pr.nrow, pos0 = pr.pos0;
-  const int doc = doc_of_pair[p];
-  const bool bad_doc = doc < 0 || doc >= D;
+  const int doc = PART == 1 ? 0 : doc_of_pair[p];  // a self partial reads no passage
+  const bool bad_doc = PART != 1 && (doc < 0 || doc >= D);
 
   // cross-tile validity words, kept in registers by every wave: lane l holds
   // the words of tiles l and l + 64 (one ballot per 64 chunks); word t is
   // read back with a scalar readlane
-  const int n_ct_all = bad_doc ? 0 : (Cmax + BKV - 1) / BKV;
+  const int n_ct_all = (PART == 1 || bad_doc) ? 0 : (Cmax + BKV - 1) / BKV;
   uint32_t cmw0 = 0, cmw1 = 0;
   {
     const uint8_t* cmd = cmask + (int64_t)(bad_doc ? 0 : doc) * Cmax;
@@ -193,7 +203,10 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
     return t < 64 ? __builtin_amdgcn_readlane(cmw0, t) : __builtin_amdgcn_readlane(cmw1, t - 64);
   };
   const uint64_t nz0 = __ballot(cmw0 != 0), nz1 = __ballot(cmw1 != 0);
-  const int n_ct = nz1 ? 64 + 64 - __builtin_clzll(nz1) : (nz0 ? 64 - __builtin_clzll(nz0) : 0);
+  int n_ct = nz1 ? 64 + 64 - __builtin_clzll(nz1) : (nz0 ? 64 - __builtin_clzll(nz0) : 0);
+  // opaque: a self partial (no cross tile) keeps the loop the merged kernel
+  // has -- with the tile kind known the compiler reorders it into spills
+  asm volatile("" : "+s"(n_ct));
   int donor = 0;  // a valid chunk: masked chunk rows are fetched from it
   if (n_ct) {
     const int t = nz0 ? __builtin_ctzll(nz0) : 64 + __builtin_ctzll(nz1);
@@ -231,9 +244,30 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
     m_run[u] = -INFINITY;
     l_run[u] = 0.f;
   }
+  if constexpr (PART == 2) {
+    // resume from the self partial of each row: its normalised output in the
+    // accumulator layout (dims 32 db + 8 q + 4 g + 0..3 of row r), m = its lse
+    // in log2 units, l = 1 (held by the g = 0 half; the halves are summed at
+    // the end)
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+      const int64_t row = pr.q0 + min(qr0 + 32 * u + r, nrow - 1);
+      const float* op = oi + row * oi_ld + (int64_t)h * HD + 4 * g;
+#pragma unroll
+      for (int i = 0; i < HD / 32; ++i)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4_t t = *(const f32x4_t*)(op + 32 * i + 8 * q4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) oacc[u][i][4 * q4 + j] = t[j];
+        }
+      m_run[u] = lsei[row * nq + h] * 1.4426950408889634f;
+      l_run[u] = g == 0 ? 1.f : 0.f;
+    }
+  }
 
   const int n_self = min(Lq, pos0 + min(nrow, qb * RB + RB));  // causal keys the block needs
-  const int n_st = (n_self + BKV - 1) / BKV;
+  const int n_st = PART == 2 ? 0 : (n_self + BKV - 1) / BKV;
   const int n_tiles = n_st + n_ct;
   // byte addresses of key 0 of this pair (self) / chunk 0 of this passage (cross), head kvh
   const uint64_t ks_base = (uint64_t)(uintptr_t)(Ks + pr.kv0 * kv_ld + (int64_t)kvh * HD);
@@ -311,9 +345,17 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   // hardware counter, also cover the next tile's copies -- serialising every
   // tile's copy with its compute.
 #pragma unroll
-  for (int u = 0; u < RT; ++u)
+  for (int u = 0; u < RT; ++u) {
 #pragma unroll
     for (int s = 0; s < HD / 16; ++s) asm volatile("" ::"v"(qf[u][s]));
+    if constexpr (PART == 2) {
+#pragma unroll
+      for (int i = 0; i < HD / 32; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) asm volatile("" ::"v"(oacc[u][i][e]));  // scalar operands: valid for the host pass too
+      asm volatile("" ::"v"(m_run[u]));
+    }
+  }
   for (int v = 0; v < n_tiles; ++v) {
     if (KR == VR) wait_dma_ktile<2 * CPT>(min(n_tiles - 1 - v, VR - 2));
     else wait_dma_ktile<CPT>(min(n_tiles - 1 - v, KR - VR));  // K(v+1) may still be in flight
@@ -387,8 +429,9 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
       // lazy rescale: the running max moves only when some row's tile max
       // exceeds it by more than LAZY (log2 units); the first tile (m_run =
       // -inf, accumulator 0) always takes this branch with alpha = 0.  Tile 0
-      // holds key 0, visible to every row, so tmax is finite there.  (A row
-      // tile whose rows all lie above a causal tile sees only -inf: no change.)
+      // holds key 0, visible to every row, so tmax is finite there (a resumed
+      // walk starts from a finite m).  (A row tile whose rows all lie above a
+      // causal tile sees only -inf: no change.)
       if (__ballot(tmax > m_run[u] + LAZY)) {
         const float m_new = fmaxf(m_run[u], tmax);
         const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);  // exp2(-inf) = 0
@@ -437,6 +480,38 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   // ---- normalise and store.  The accumulator holds, per lane (r, g), dims
   // 32 db + 8 q + 4 g + (0..3) of row r; it is staged through LDS (now free)
   // so that the global stores write whole rows, 16 bytes per lane.
+#pragma unroll
+  for (int u = 0; u < RT; ++u) {
+    const float l_tot = l_run[u] + __shfl_xor(l_run[u], 32, 64);
+    const float inv = bad_doc ? __builtin_nanf("") : 1.f / l_tot;
+    l_run[u] = inv;  // keep the reciprocal for the stores below
+    const int jl = qr0 + 32 * u + r;
+    if (lse && g == 0 && jl < nrow)
+      lse[(pr.o0 + jl) * nq + h] =
+          bad_doc ? __builtin_nanf("") : (m_run[u] + __builtin_log2f(l_tot)) * 0.69314718055994531f;
+  }
+  if constexpr (PART == 1) {
+    // fp32 partial: 16-byte stores straight from the accumulator (lanes g = 0
+    // and 1 together write 32 contiguous bytes of a row)
+    float* Of = (float*)Ov;
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+      const int jl = qr0 + 32 * u + r;
+      if (jl >= nrow) continue;
+      float* op = Of + (pr.o0 + jl) * o_ld + (int64_t)h * HD + 4 * g;
+#pragma unroll
+      for (int i = 0; i < HD / 32; ++i)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x16_t& a = oacc[u][i];
+          const float inv = l_run[u];
+          *(f32x4_t*)(op + 32 * i + 8 * q4) =
+              f32x4_t{a[4 * q4] * inv, a[4 * q4 + 1] * inv, a[4 * q4 + 2] * inv, a[4 * q4 + 3] * inv};
+        }
+    }
+    return;
+  }
+  bf16_t* O = (bf16_t*)Ov;
   __syncthreads();  // every wave is done with the K/V ring
   constexpr int RING_B = (KR + VR) * TILE_B;
   // dims per pass: a wave stages 32 RT rows x DPP bf16; all NW waves must fit the ring
@@ -445,16 +520,6 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   constexpr int RPI = 64 / CPR;               // rows per read-back instruction
   const uint32_t ebase = lds0 + wave * (32 * RT * DPP * 2);
   bf16_t* orow0 = O + (pr.o0 + qr0) * o_ld + (int64_t)h * HD;
-#pragma unroll
-  for (int u = 0; u < RT; ++u) {
-    const float l_tot = l_run[u] + __shfl_xor(l_run[u], 32, 64);
-    const float inv = bad_doc ? __builtin_nanf("") : 1.f / l_tot;
-    l_run[u] = inv;  // keep the reciprocal for the staging below
-    const int jl = qr0 + 32 * u + r;
-    if (lse && g == 0 && jl < nrow)
-      lse[(pr.o0 + jl) * nq + h] =
-          bad_doc ? __builtin_nanf("") : (m_run[u] + __builtin_log2f(l_tot)) * 0.69314718055994531f;
-  }
 #pragma unroll
   for (int pass = 0; pass < HD / DPP; ++pass) {
 #pragma unroll
@@ -485,13 +550,30 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   }
 }
 
+typedef void (*bf16_kernel_t)(const bf16_t*, int64_t, const bf16_t*, const bf16_t*, int64_t, const int32_t*, int,
+                              int64_t, int64_t, int64_t, int, const bf16_t*, const bf16_t*, int64_t, const uint8_t*,
+                              const int32_t*, int, int, int, int, float, void*, int64_t, float*, const float*, int64_t,
+                              const float*);
+template <int NH, int NW, int RT>
+bf16_kernel_t pick_bf16_kernel(int sel) {
+  switch (sel) {
+    case 0: return merged_attn_bf16_kernel<NH, NW, RT, 0, 1>;
+    case 1: return merged_attn_bf16_kernel<NH, NW, RT, 0, 0>;
+    case 2: return merged_attn_bf16_kernel<NH, NW, RT, 1, 0>;
+    case 3: return merged_attn_bf16_kernel<NH, NW, RT, 2, 0>;
+    case 4: return merged_attn_bf16_kernel<NH, NW, RT, 0, 2>;
+    case 5: return merged_attn_bf16_kernel<NH, NW, RT, 1, 2>;
+    default: return merged_attn_bf16_kernel<NH, NW, RT, 2, 2>;
+  }
+}
+
 // Launch of the bf16 kernel for NW waves and RT row tiles per wave.
 template <int NW, int RT>
 void launch_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, const bf16_t* Vs, int64_t kv_ld,
                  const int32_t* cu_q, int P, int64_t q_rows, int64_t kv_rows, int64_t o_rows, int mode, int max_lq,
                  const bf16_t* Kc, const bf16_t* Vc, int64_t c_ld, const uint8_t* cmask,
-                 const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv, float scale, bf16_t* O, int64_t o_ld,
-                 float* lse, hipStream_t s) {
+                 const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv, float scale, void* O, int64_t o_ld,
+                 float* lse, int part, const float* oi, int64_t oi_ld, const float* lsei, hipStream_t s) {
   const int G = nq / nkv;
   const int NH = G >= 4 ? 4 : G;  // heads per block (G is 1, 2 or a multiple of 4)
   const int RB = 32 * RT * (NW / NH);
@@ -503,18 +585,14 @@ void launch_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, const bf16_t* 
   if (blocks == 0) return;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, P, q_rows, kv_rows, o_rows, nqb, Kc, Vc,
-                       c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, sl2, O, o_ld, lse);
+                       c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, sl2, O, o_ld, lse, oi, oi_ld, lsei);
   };
-  // one instantiation per (heads per block, row mode)
-  if (NH == 4)
-    mode == 0 ? go(merged_attn_bf16_kernel<4, NW, RT, 0>) : mode == 1 ? go(merged_attn_bf16_kernel<4, NW, RT, 1>)
-                                                          : go(merged_attn_bf16_kernel<4, NW, RT, 2>);
-  else if (NH == 2)
-    mode == 0 ? go(merged_attn_bf16_kernel<2, NW, RT, 0>) : mode == 1 ? go(merged_attn_bf16_kernel<2, NW, RT, 1>)
-                                                          : go(merged_attn_bf16_kernel<2, NW, RT, 2>);
-  else
-    mode == 0 ? go(merged_attn_bf16_kernel<1, NW, RT, 0>) : mode == 1 ? go(merged_attn_bf16_kernel<1, NW, RT, 1>)
-                                                          : go(merged_attn_bf16_kernel<1, NW, RT, 2>);
+  // one instantiation per (heads per block, row mode, part); a self partial
+  // (part 1) runs on all rows of its sequences (mode 0) only
+  const int sel = part == 1 ? 0 : 1 + 3 * (part == 2) + mode;  // 0 | 1..3 merged | 4..6 resumed
+  if (NH == 4) go(pick_bf16_kernel<4, NW, RT>(sel));
+  else if (NH == 2) go(pick_bf16_kernel<2, NW, RT>(sel));
+  else go(pick_bf16_kernel<1, NW, RT>(sel));
 }
 
 }  // namespace

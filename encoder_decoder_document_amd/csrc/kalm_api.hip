@@ -145,7 +145,9 @@ static kalm_status merged_attn_impl(const char* fn, const void* Q, int64_t q_ld,
                                     int32_t max_lq, const void* Kc, const void* Vc, int64_t c_ld,
                                     const uint8_t* chunk_mask, const int32_t* doc_of_pair, int32_t D, int32_t Cmax,
                                     int32_t nq, int32_t nkv, int32_t d, float scale, kalm_dtype dt, void* O,
-                                    int64_t o_ld, int64_t o_rows, float* lse, int32_t row_mode, void* stream) {
+                                    int64_t o_ld, int64_t o_rows, float* lse, int32_t row_mode, void* stream,
+                                    int part = 0, const float* oi = nullptr, int64_t oi_ld = 0,
+                                    const float* lsei = nullptr) {
   kalm::g_err[0] = 0;
   KALM_REQUIRE(dt == KALM_F32 || dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)dt);
   KALM_REQUIRE(row_mode >= 0 && row_mode <= 2, KALM_ERR_INVALID_ARG, "%s: row_mode %d not in 0..2", fn, row_mode);
@@ -154,10 +156,15 @@ static kalm_status merged_attn_impl(const char* fn, const void* Q, int64_t q_ld,
   KALM_REQUIRE(row_mode != 2 || P == 0 || D >= 1, KALM_ERR_INVALID_ARG, "%s: row_mode 2 needs D >= 1", fn);
   KALM_REQUIRE(nq >= 1 && nkv >= 1 && nq % nkv == 0, KALM_ERR_INVALID_ARG, "%s: nq=%d nkv=%d", fn, nq, nkv);
   KALM_REQUIRE(scale > 0.f, KALM_ERR_INVALID_ARG, "%s: scale must be positive", fn);
-  KALM_REQUIRE(P == 0 || (Q && Ks && Vs && cu_q && O && doc_of_pair), KALM_ERR_INVALID_ARG, "%s: null pointer", fn);
-  KALM_REQUIRE(Cmax == 0 || D == 0 || (Kc && Vc && chunk_mask), KALM_ERR_INVALID_ARG, "%s: null cross pointer", fn);
-  KALM_REQUIRE(q_ld >= (int64_t)nq * d && kv_ld >= (int64_t)nkv * d && o_ld >= (int64_t)nq * d &&
-                   (Cmax == 0 || c_ld >= (int64_t)nkv * d),
+  // part 1 reads no cross keys and no passage index; part 2 reads no self keys
+  KALM_REQUIRE(P == 0 || (Q && cu_q && O && (part == 2 || (Ks && Vs)) && (part == 1 || doc_of_pair)),
+               KALM_ERR_INVALID_ARG, "%s: null pointer", fn);
+  KALM_REQUIRE(part == 1 || Cmax == 0 || D == 0 || (Kc && Vc && chunk_mask), KALM_ERR_INVALID_ARG,
+               "%s: null cross pointer", fn);
+  KALM_REQUIRE(part != 1 || P == 0 || lse, KALM_ERR_INVALID_ARG, "%s: a self partial needs its lse output", fn);
+  KALM_REQUIRE(part != 2 || P == 0 || (oi && lsei), KALM_ERR_INVALID_ARG, "%s: null self-partial pointer", fn);
+  KALM_REQUIRE(q_ld >= (int64_t)nq * d && (part == 2 || kv_ld >= (int64_t)nkv * d) && o_ld >= (int64_t)nq * d &&
+                   (part != 2 || oi_ld >= (int64_t)nq * d) && (part == 1 || Cmax == 0 || c_ld >= (int64_t)nkv * d),
                KALM_ERR_INVALID_ARG, "%s: leading dimension smaller than the heads", fn);
   if (dt == KALM_BF16) {
     KALM_REQUIRE(d == 256, KALM_ERR_UNSUPPORTED, "%s: bf16 path needs head_dim 256 (got %d)", fn, d);
@@ -165,11 +172,13 @@ static kalm_status merged_attn_impl(const char* fn, const void* Q, int64_t q_ld,
     KALM_REQUIRE(G == 1 || G == 2 || G % 4 == 0, KALM_ERR_UNSUPPORTED,
                  "%s: query heads per KV head must be 1, 2 or a multiple of 4 (got %d)", fn, G);
     KALM_REQUIRE(Cmax <= 4096, KALM_ERR_UNSUPPORTED, "%s: bf16 path supports Cmax <= 4096 (got %d)", fn, Cmax);
-    KALM_REQUIRE((int64_t)max_lq * kv_ld * 2 < (1LL << 31) && (int64_t)Cmax * c_ld * 2 < (1LL << 31),
+    KALM_REQUIRE((part == 2 || (int64_t)max_lq * kv_ld * 2 < (1LL << 31)) &&
+                     (part == 1 || (int64_t)Cmax * c_ld * 2 < (1LL << 31)),
                  KALM_ERR_UNSUPPORTED, "%s: per-pair K block exceeds 2 GiB", fn);
-    KALM_REQUIRE(q_ld % 8 == 0 && kv_ld % 8 == 0 && o_ld % 8 == 0 && c_ld % 8 == 0, KALM_ERR_UNSUPPORTED,
-                 "%s: bf16 leading dimensions must be multiples of 8", fn);
-    KALM_REQUIRE(ALIGNED16(Q) && ALIGNED16(Ks) && ALIGNED16(Vs) && ALIGNED16(O) && ALIGNED16(Kc) && ALIGNED16(Vc),
+    KALM_REQUIRE(q_ld % 8 == 0 && kv_ld % 8 == 0 && o_ld % 8 == 0 && c_ld % 8 == 0 && oi_ld % 4 == 0,
+                 KALM_ERR_UNSUPPORTED, "%s: bf16 leading dimensions must be multiples of 8 (fp32 ones of 4)", fn);
+    KALM_REQUIRE(ALIGNED16(Q) && ALIGNED16(Ks) && ALIGNED16(Vs) && ALIGNED16(O) && ALIGNED16(Kc) && ALIGNED16(Vc) &&
+                     ALIGNED16(oi),
                  KALM_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
   } else {
     KALM_REQUIRE(d >= 1 && d <= 256, KALM_ERR_UNSUPPORTED, "%s: f32 path needs head_dim <= 256", fn);
@@ -179,13 +188,13 @@ static kalm_status merged_attn_impl(const char* fn, const void* Q, int64_t q_ld,
   if (dt == KALM_BF16)
     kalm::launch_merged_attn_bf16((const bf16_t*)Q, q_ld, (const bf16_t*)Ks, (const bf16_t*)Vs, kv_ld, cu_q, P,
                                   q_rows, kv_rows, o_rows, row_mode, max_lq, (const bf16_t*)Kc, (const bf16_t*)Vc,
-                                  c_ld, chunk_mask, doc_of_pair, D, Cmax, nq, nkv, scale, (bf16_t*)O, o_ld, lse,
-                                  (hipStream_t)stream);
+                                  c_ld, chunk_mask, doc_of_pair, D, Cmax, nq, nkv, scale, O, o_ld, lse, part, oi,
+                                  oi_ld, lsei, (hipStream_t)stream);
   else
     kalm::launch_merged_attn_f32((const float*)Q, q_ld, (const float*)Ks, (const float*)Vs, kv_ld, cu_q, P, q_rows,
                                  kv_rows, o_rows, row_mode, max_lq, (const float*)Kc, (const float*)Vc, c_ld,
-                                 chunk_mask, doc_of_pair, D, Cmax, nq, nkv, d, scale, (float*)O, o_ld, lse,
-                                 (hipStream_t)stream);
+                                 chunk_mask, doc_of_pair, D, Cmax, nq, nkv, d, scale, (float*)O, o_ld, lse, part,
+                                 oi, oi_ld, lsei, (hipStream_t)stream);
   return kalm::check_launch(fn);
 }
 
@@ -208,6 +217,27 @@ kalm_status kalm_merged_attn_rows(const void* Q, int64_t q_ld, int64_t q_rows, c
   return merged_attn_impl("kalm_merged_attn_rows", Q, q_ld, q_rows, Ks, Vs, kv_ld, kv_rows, cu_q, P, max_lq, Kc,
                           Vc, c_ld, chunk_mask, doc_of_pair, D, Cmax, nq, nkv, d, scale, dt, O, o_ld, o_rows, lse,
                           row_mode, stream);
+}
+
+kalm_status kalm_self_attn_partial(const void* Q, int64_t q_ld, const void* Ks, const void* Vs, int64_t kv_ld,
+                                   int64_t rows, const int32_t* cu_s, int32_t n_seq, int32_t max_len, int32_t nq,
+                                   int32_t nkv, int32_t d, float scale, kalm_dtype dt, float* O, int64_t o_ld,
+                                   float* lse, void* stream) {
+  return merged_attn_impl("kalm_self_attn_partial", Q, q_ld, rows, Ks, Vs, kv_ld, rows, cu_s, n_seq, max_len,
+                          nullptr, nullptr, 0, nullptr, nullptr, 0, 0, nq, nkv, d, scale, dt, O, o_ld, rows, lse, 0,
+                          stream, 1);
+}
+
+kalm_status kalm_merged_attn_resume(const void* Q, int64_t q_ld, int64_t q_rows, const float* o_self, int64_t s_ld,
+                                    const float* lse_self, const int32_t* cu_q, int32_t P, int32_t max_lq,
+                                    const void* Kc, const void* Vc, int64_t c_ld, const uint8_t* chunk_mask,
+                                    const int32_t* doc_of_pair, int32_t D, int32_t Cmax, int32_t nq, int32_t nkv,
+                                    int32_t d, float scale, kalm_dtype dt, void* O, int64_t o_ld, int64_t o_rows,
+                                    float* lse, int32_t row_mode, void* stream) {
+  // no self keys are read: the self-row bound is the Q-row one
+  return merged_attn_impl("kalm_merged_attn_resume", Q, q_ld, q_rows, nullptr, nullptr, 0, INT64_MAX, cu_q, P,
+                          max_lq, Kc, Vc, c_ld, chunk_mask, doc_of_pair, D, Cmax, nq, nkv, d, scale, dt, O, o_ld,
+                          o_rows, lse, row_mode, stream, 2, o_self, s_ld, lse_self);
 }
 
 kalm_status kalm_yesno_score(const void* h, kalm_dtype h_dt, int64_t h_ld, int64_t rows, const int32_t* final_row,

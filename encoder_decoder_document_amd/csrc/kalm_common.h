@@ -111,7 +111,10 @@ kalm_status check_launch(const char* what);
     if (_s != KALM_OK) return _s;                      \
   } while (0)
 
-// Launchers implemented in the kernel translation units.
+// Launchers implemented in the kernel translation units.  The attention
+// launchers' part: 0 merged self + cross softmax; 1 causal self keys only, fp32
+// O and lse (a self partial); 2 cross keys only, resumed from the self partial
+// (oi, lsei) at each Q row.
 namespace kalm {
 void launch_chunk_pool(const void* x, const uint8_t* mask, int D, int T, int H, int chunk, int Cmax,
                        kalm_dtype dt, void* pooled, uint8_t* cmask, int32_t* n_chunks, hipStream_t s);
@@ -125,12 +128,14 @@ void launch_merged_attn_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, co
                              int64_t kv_ld, const int32_t* cu_q, int P, int64_t q_rows, int64_t kv_rows,
                              int64_t o_rows, int mode, int max_lq, const bf16_t* Kc, const bf16_t* Vc,
                              int64_t c_ld, const uint8_t* cmask, const int32_t* doc_of_pair, int D, int Cmax,
-                             int nq, int nkv, float scale, bf16_t* O, int64_t o_ld, float* lse, hipStream_t s);
+                             int nq, int nkv, float scale, void* O, int64_t o_ld, float* lse, int part,
+                             const float* oi, int64_t oi_ld, const float* lsei, hipStream_t s);
 void launch_merged_attn_f32(const float* Q, int64_t q_ld, const float* Ks, const float* Vs,
                             int64_t kv_ld, const int32_t* cu_q, int P, int64_t q_rows, int64_t kv_rows,
                             int64_t o_rows, int mode, int max_lq, const float* Kc, const float* Vc, int64_t c_ld,
                             const uint8_t* cmask, const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv,
-                            int d, float scale, float* O, int64_t o_ld, float* lse, hipStream_t s);
+                            int d, float scale, float* O, int64_t o_ld, float* lse, int part, const float* oi,
+                            int64_t oi_ld, const float* lsei, hipStream_t s);
 void launch_yesno(const void* h, bool h_bf16, int64_t h_ld, int64_t rows, const int32_t* final_row, int P,
                   int H, const void* w, bool w_bf16, float* yes, float* no, float* margin, float* score,
                   hipStream_t s);

@@ -39,6 +39,11 @@ _SIGS = {
     "kalm_merged_attn_rows": (_i32, [_c_p, _i64, _i64, _c_p, _c_p, _i64, _i64, _c_p, _i32, _i32, _c_p, _c_p, _i64,
                                      _c_p, _c_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_p, _i64, _i64, _c_p,
                                      _i32, _c_p]),
+    "kalm_self_attn_partial": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _i64, _c_p, _i32, _i32, _i32, _i32, _i32, _f32,
+                                      _i32, _c_p, _i64, _c_p, _c_p]),
+    "kalm_merged_attn_resume": (_i32, [_c_p, _i64, _i64, _c_p, _i64, _c_p, _c_p, _i32, _i32, _c_p, _c_p, _i64, _c_p,
+                                       _c_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_p, _i64, _i64, _c_p, _i32,
+                                       _c_p]),
     "kalm_yesno_score": (_i32, [_c_p, _i32, _i64, _i64, _c_p, _i32, _i32, _c_p, _i32, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "kalm_linear": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _i32, _c_p, _i32, _i32, _c_p, _c_p]),
     "kalm_gather_rows": (_i32, [_c_p, _c_p, _i64, _i32, _i64, _c_p, _c_p, _c_p]),
@@ -209,6 +214,51 @@ def kalm_merged_attn_rows(Q: torch.Tensor, Ks: torch.Tensor, Vs: torch.Tensor, c
         _ptr(Q), Q.stride(0), Q.shape[0], _ptr(Ks), _ptr(Vs), Ks.stride(0), Ks.shape[0], _ptr(cu_q), P, max_lq,
         _ptr(Kc), _ptr(Vc), Kc.stride(0), _ptr(chunk_mask), _ptr(doc_of_pair), D, Cmax, nq, nkv, d,
         float(scale), _dt(Q), _ptr(out), out.stride(0), o_rows, _ptr(lse), int(row_mode), _stream(stream)))
+    return out
+
+
+def kalm_self_attn_partial(Q: torch.Tensor, Ks: torch.Tensor, Vs: torch.Tensor, cu_s: torch.Tensor, max_len: int,
+                           nq: int, nkv: int, d: int, scale: Optional[float] = None,
+                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
+    """Causal self-attention of packed sequences (rows cu_s[i] .. cu_s[i+1]-1):
+    Q [rows, >=nq*d], Ks/Vs [rows, >=nkv*d] -> (O [rows, nq*d] float32, lse [rows, nq] float32)."""
+    for t in (Q, Ks, Vs):
+        if t.stride(-1) != 1:
+            raise ValueError("unit column stride required")
+    rows = Q.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(rows, nq * d, dtype=torch.float32, device=Q.device)
+    if lse is None:
+        lse = torch.empty(rows, nq, dtype=torch.float32, device=Q.device)
+    _check("kalm_self_attn_partial", load().kalm_self_attn_partial(
+        _ptr(Q), Q.stride(0), _ptr(Ks), _ptr(Vs), Ks.stride(0), rows, _ptr(cu_s), cu_s.numel() - 1, max_len, nq, nkv,
+        d, float(scale), _dt(Q), _ptr(out), out.stride(0), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def kalm_merged_attn_resume(Q: torch.Tensor, o_self: torch.Tensor, lse_self: torch.Tensor, cu_q: torch.Tensor,
+                            max_lq: int, Kc: torch.Tensor, Vc: torch.Tensor, chunk_mask: torch.Tensor,
+                            doc_of_pair: torch.Tensor, nq: int, nkv: int, d: int, row_mode: int, o_rows: int,
+                            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None, stream=None):
+    """Merged attention finished from a self partial (o_self, lse_self indexed like the Q rows):
+    only the cross keys are read.  Rows as kalm_merged_attn_rows -> O [o_rows, nq*d]."""
+    for t in (Q, o_self, Kc, Vc):
+        if t.stride(-1) != 1:
+            raise ValueError("unit column stride required")
+    _contig(lse_self)
+    P = cu_q.numel() - 1
+    D, Cmax = chunk_mask.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(o_rows, nq * d, dtype=Q.dtype, device=Q.device)
+    _check("kalm_merged_attn_resume", load().kalm_merged_attn_resume(
+        _ptr(Q), Q.stride(0), Q.shape[0], _ptr(o_self), o_self.stride(0), _ptr(lse_self), _ptr(cu_q), P, max_lq,
+        _ptr(Kc), _ptr(Vc), Kc.stride(0), _ptr(chunk_mask), _ptr(doc_of_pair), D, Cmax, nq, nkv, d, float(scale),
+        _dt(Q), _ptr(out), out.stride(0), o_rows, _ptr(lse), int(row_mode), _stream(stream)))
     return out
 
 

@@ -12,8 +12,12 @@ itself only enqueues libkalm calls on the current stream:
 
 With ``prune`` (the default) two layers do less work for the same result:
   * layer 1: every passage of a query still holds the query's own first hidden
-    states, so Q/K/V are projected once per query row (not once per pair row)
-    and the attention reads them shared (kalm_merged_attn_rows, shared rows);
+    states, so Q/K/V are projected once per query row (not once per pair row);
+    the query's causal self-attention is computed once as well
+    (kalm_self_attn_partial) and each pair is finished from it with its
+    passage's cross keys (kalm_merged_attn_resume, shared rows) -- or, without
+    ``reuse_self``, each pair reads the shared rows in one merged pass
+    (kalm_merged_attn_rows, shared rows);
   * the last layer (stacks of two or more layers): the score reads only each
     pair's final position ("KaLM-Reranker-V1-Nano -- MLX (Apple Silicon)",
     What this is), so self K/V are projected for every row but Q, attention,
@@ -111,6 +115,12 @@ def upload(inputs: Dict[str, object], device="cuda", n_layers: Optional[int] = N
         hf=torch.empty(P, H, dtype=torch.float32, device=device),
         qf=torch.empty(P, sh.nq * sh.d, dtype=dt, device=device),
         of=torch.empty(P, sh.nq * sh.d, dtype=dt, device=device),
+        # per-query packing (the pair layout with one passage) and the queries' self partials
+        cu_s=torch.empty(sh.n_queries + 1, dtype=torch.int32, device=device),
+        doc_s=torch.empty(sh.n_queries, dtype=torch.int32, device=device),
+        fin_s=torch.empty(sh.n_queries, dtype=torch.int32, device=device),
+        o_self=torch.empty(U, sh.nq * sh.d, dtype=torch.float32, device=device),
+        lse_self=torch.empty(U, sh.nq, dtype=torch.float32, device=device),
     )
     if dt == torch.bfloat16:
         buf["h0b"] = torch.empty(U, H, dtype=torch.bfloat16, device=device)
@@ -152,8 +162,11 @@ def pruned(b: DeviceBatch, prune: bool = True) -> bool:
     return prune and b.n_layers >= 2
 
 
-def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True):
-    """Row a5 around a3: residual start, then every merged-attention layer."""
+def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_self: bool = True):
+    """Row a5 around a3: residual start, then every merged-attention layer.
+    With ``prune`` and ``reuse_self`` the first layer computes each query's
+    self-attention once and finishes every pair from it with the pair's cross
+    keys (the merged softmax split at the self/cross boundary)."""
     B = b.buf
     bf = b.dtype == torch.bfloat16
     qd, kv = b.nq * b.d, b.nkv * b.d
@@ -174,11 +187,27 @@ def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True):
             u = B["qkv_u"]
             with rec("qkv_linear_first"):
                 ops.kalm_linear(B["h0b"] if bf else b.h0, b.Wqkv[0], Y=u, stream=stream)
-            with rec("merged_attn_first"):
-                ops.kalm_merged_attn_rows(u[:, :qd], u[:, qd:qd + kv], u[:, qd + kv:], B["cu_q"], b.max_lq,
-                                          kvc[:, :kv], kvc[:, kv:], B["chunk_mask"], B["doc_of_pair"], b.nq,
-                                          b.nkv, b.d, ops.ROWS_SHARED, b.rows, scale=scale, out=B["o"],
-                                          stream=stream)
+            if reuse_self:
+                # the query's causal self-attention once, then each pair from it with its passage's cross keys
+                with rec("pair_layout_queries"):
+                    ops._check("kalm_pair_layout", ops.load().kalm_pair_layout(
+                        ops._ptr(b.lq), b.n_queries, 1, ops._ptr(B["cu_s"]), ops._ptr(B["doc_s"]),
+                        ops._ptr(B["fin_s"]), None, 0, ops._stream(stream)))
+                with rec("self_attn_first"):
+                    ops.kalm_self_attn_partial(u[:, :qd], u[:, qd:qd + kv], u[:, qd + kv:], B["cu_s"], b.max_lq,
+                                               b.nq, b.nkv, b.d, scale=scale, out=B["o_self"], lse=B["lse_self"],
+                                               stream=stream)
+                with rec("merged_attn_first_resume"):
+                    ops.kalm_merged_attn_resume(u[:, :qd], B["o_self"], B["lse_self"], B["cu_q"], b.max_lq,
+                                                kvc[:, :kv], kvc[:, kv:], B["chunk_mask"], B["doc_of_pair"], b.nq,
+                                                b.nkv, b.d, ops.ROWS_SHARED, b.rows, scale=scale, out=B["o"],
+                                                stream=stream)
+            else:
+                with rec("merged_attn_first"):
+                    ops.kalm_merged_attn_rows(u[:, :qd], u[:, qd:qd + kv], u[:, qd + kv:], B["cu_q"], b.max_lq,
+                                              kvc[:, :kv], kvc[:, kv:], B["chunk_mask"], B["doc_of_pair"], b.nq,
+                                              b.nkv, b.d, ops.ROWS_SHARED, b.rows, scale=scale, out=B["o"],
+                                              stream=stream)
         elif last_pruned and l == b.n_layers - 1:
             # final rows only: self K/V of every row, Q / attention / projection of the final rows
             kvs = qkv.view(-1)[: b.rows * 2 * kv].view(b.rows, 2 * kv)
@@ -215,8 +244,8 @@ def score(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True):
         return ops.kalm_yesno_score(b.buf["h"], b.buf["final_row"], b.w_yesno, stream=stream)
 
 
-def step(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True):
+def step(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_self: bool = True):
     """One pass of the whole hot path over the batch; returns (yes, no, margin, score)."""
     front(b, stream, rec)
-    decoder(b, stream, rec, prune)
+    decoder(b, stream, rec, prune, reuse_self)
     return score(b, stream, rec, prune)

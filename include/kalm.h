@@ -179,6 +179,56 @@ kalm_status kalm_merged_attn_rows(const void* Q, int64_t q_ld, int64_t q_rows, c
                                   float* lse, int32_t row_mode, void* stream);
 
 /*
+ * a3 split at the self/cross boundary.  The merged softmax over [self keys ;
+ * cross keys] equals the log-sum-exp merge of a softmax over the self keys
+ * alone and one over the cross keys alone ([MLX] What this is: one attention
+ * over the concatenated KV; the merge is the usual online-softmax identity).
+ * While every passage of a query still holds the query's own hidden states
+ * (the first decoder layer; one passage set reranked against many queries,
+ * [MLX] Speed), the self part is the same for all of the query's passages:
+ * kalm_self_attn_partial computes it once per query and
+ * kalm_merged_attn_resume finishes each pair from it with the passage's cross
+ * keys.
+ *
+ * kalm_self_attn_partial -- plain causal self-attention of n_seq packed
+ * sequences (the merged attention with no visible cross key):
+ *   Q, Ks, Vs   as kalm_merged_attn, rows cu_s[i] .. cu_s[i+1]-1 of sequence i
+ *   cu_s        [n_seq+1] int32 row offsets (kalm_pair_layout with n_docs = 1
+ *               gives the per-query packing); max_len >= every length
+ *   O           [rows, *] float out, row stride o_ld (elements): the normalised
+ *               self output of each row and head, fp32 for both dtypes
+ *   lse         [rows, nq] float out, required: log-sum-exp of the scaled self
+ *               logits (natural log)
+ * Requires what kalm_merged_attn requires (bf16: d == 256, o_ld % 8 == 0,
+ * 16-byte aligned pointers).
+ */
+kalm_status kalm_self_attn_partial(const void* Q, int64_t q_ld, const void* Ks, const void* Vs,
+                                   int64_t kv_ld, int64_t rows, const int32_t* cu_s, int32_t n_seq,
+                                   int32_t max_len, int32_t nq, int32_t nkv, int32_t d, float scale,
+                                   kalm_dtype dt, float* O, int64_t o_ld, float* lse, void* stream);
+
+/*
+ * kalm_merged_attn_resume -- the merged attention of every pair given the self
+ * partial of its query rows: only the pair's valid cross keys are read, and
+ * the online softmax starts from (o_self, lse_self) of the Q row, so that
+ *   O = (e^lse_self o_self + sum_c e^s_c v_c) / (e^lse_self + sum_c e^s_c)
+ * and lse (nullable) is the log-sum-exp of all of the row's logits.
+ * Rows follow kalm_merged_attn_rows with the same row_mode (0..2); o_self
+ * [q_rows, *] float (row stride s_ld, elements, s_ld % 4 == 0 and 16-byte
+ * aligned for bf16) and lse_self [q_rows, nq] are indexed like Q.  With the
+ * partial of kalm_self_attn_partial on the same Q/K/V rows the result is that
+ * of kalm_merged_attn_rows up to rounding.  Other arguments as
+ * kalm_merged_attn_rows (there are no self-key arguments).
+ */
+kalm_status kalm_merged_attn_resume(const void* Q, int64_t q_ld, int64_t q_rows, const float* o_self,
+                                    int64_t s_ld, const float* lse_self, const int32_t* cu_q, int32_t P,
+                                    int32_t max_lq, const void* Kc, const void* Vc, int64_t c_ld,
+                                    const uint8_t* chunk_mask, const int32_t* doc_of_pair, int32_t D,
+                                    int32_t Cmax, int32_t nq, int32_t nkv, int32_t d, float scale,
+                                    kalm_dtype dt, void* O, int64_t o_ld, int64_t o_rows, float* lse,
+                                    int32_t row_mode, void* stream);
+
+/*
  * a4 -- yes/no readout ([MLX] What this is: score = softmax([logit_yes,
  * logit_no])[yes] at the decoder's final position; [Q4KM] Score a pair and [Q80]
  * Frozen inference contract: margin = yes - no, score = sigmoid(margin)).

@@ -79,6 +79,20 @@ def test_invalid_arguments_rejected_before_launch():
     st = lib.kalm_merged_attn_rows(None, 1024, 0, None, None, 512, 0, None, 1, 0, None, None, 512, None, None, 0, 0,
                                    4, 1, 256, 0.1, ops.KALM_BF16, None, 1024, 0, None, 2, None)
     assert st == ops.KALM_ERR_INVALID_ARG
+    # self partial: its lse output is required
+    st = lib.kalm_self_attn_partial(1, 1024, 1, 1, 512, 10, 1, 1, 10, 4, 1, 256, 0.1, ops.KALM_BF16, 1, 1024, None,
+                                    None)
+    assert st == ops.KALM_ERR_INVALID_ARG and b"lse" in lib.kalm_last_error()
+    # resume: the self partial is required; row_mode outside 0..2; partial stride smaller than the heads
+    st = lib.kalm_merged_attn_resume(1, 1024, 10, None, 1024, None, 1, 1, 10, 1, 1, 512, 1, 1, 1, 8, 4, 1, 256, 0.1,
+                                     ops.KALM_BF16, 1, 1024, 10, None, 0, None)
+    assert st == ops.KALM_ERR_INVALID_ARG and b"self-partial" in lib.kalm_last_error()
+    st = lib.kalm_merged_attn_resume(1, 1024, 10, 1, 1024, 1, 1, 1, 10, 1, 1, 512, 1, 1, 1, 8, 4, 1, 256, 0.1,
+                                     ops.KALM_BF16, 1, 1024, 10, None, 3, None)
+    assert st == ops.KALM_ERR_INVALID_ARG and b"row_mode" in lib.kalm_last_error()
+    st = lib.kalm_merged_attn_resume(1, 1024, 10, 1, 512, 1, 1, 1, 10, 1, 1, 512, 1, 1, 1, 8, 4, 1, 256, 0.1,
+                                     ops.KALM_BF16, 1, 1024, 10, None, 0, None)
+    assert st == ops.KALM_ERR_INVALID_ARG and b"leading dimension" in lib.kalm_last_error()
     # ranking: top_n larger than the passages; too many passages for one workgroup
     st = lib.kalm_rank_topn(None, 1, 10, 11, None, None, None)
     assert st == ops.KALM_ERR_INVALID_ARG and b"top_n" in lib.kalm_last_error()

@@ -305,6 +305,157 @@ def test_merged_attn_bad_doc_gives_nan_rows():
     assert np.isfinite(g[:20]).all() and np.isnan(g[20:]).all()
 
 
+# ------------------------------------------------------------------ a3 split at the self/cross boundary
+def _self_ref(Q, Ks, Vs, cu, nq, nkv, d):
+    """Oracle causal self-attention of packed sequences: the merged attention
+    with no visible cross key."""
+    rows = Q.shape[0]
+    O = np.zeros((rows, nq * d))
+    L = np.zeros((rows, nq))
+    none = np.zeros((0, nkv, d))
+    for i in range(len(cu) - 1):
+        a, b = cu[i], cu[i + 1]
+        o, lse = oracle.merged_attn(Q[a:b].reshape(-1, nq, d), Ks[a:b].reshape(-1, nkv, d),
+                                    Vs[a:b].reshape(-1, nkv, d), none, none, np.zeros(0, np.uint8))
+        O[a:b] = o.reshape(b - a, nq * d)
+        L[a:b] = lse
+    return O, L
+
+
+@pytest.mark.parametrize("name,lqs,nq,nkv,bf16", [
+    ("g4_ragged", [1, 31, 32, 33, 100, 300], 4, 1, True),
+    ("g2_gqa", [64, 129, 5], 8, 4, True),
+    ("g1_long", [512, 17], 2, 2, True),
+    ("f32_gqa", [1, 9, 40, 33], 4, 2, False),
+])
+def test_self_attn_partial_parity(name, lqs, nq, nkv, bf16):
+    _announce(f"self_attn_partial {name}")
+    d = 256 if bf16 else 64
+    case = _attn_case(zlib.crc32(name.encode()) % 1000 + 300, lqs, [0], 1, nq, nkv, d, bf16)
+    Q, Ks, Vs, _, _, _, _, cu = case
+    dt = torch.bfloat16 if bf16 else torch.float32
+    O, lse = ops.kalm_self_attn_partial(to_dev(Q, dt), to_dev(Ks, dt), to_dev(Vs, dt), to_dev(cu, torch.int32),
+                                        max(lqs), nq, nkv, d)
+    torch.cuda.synchronize()
+    assert O.dtype == torch.float32
+    rO, rL = _self_ref(Q, Ks, Vs, cu, nq, nkv, d)
+    tol = BF16_TOL if bf16 else F32_TOL
+    assert_close(to_np(O), rO, *tol, f"O self ({name})")
+    assert_close(to_np(lse), rL, *tol, f"lse self ({name})")
+
+
+@pytest.mark.parametrize("name,lqs,docs_c,Cmax,nq,nkv,bf16", [
+    ("g4_ragged", [1, 31, 32, 33, 100, 300], [0, 1, 31, 32, 33, 70], 70, 4, 1, True),
+    ("g2_gqa_long", [64, 512, 3], [256, 100, 0], 256, 8, 4, True),
+    ("f32", [1, 9, 40], [0, 3, 20], 20, 4, 2, False),
+])
+def test_merged_attn_resume_from_oracle_partial(name, lqs, docs_c, Cmax, nq, nkv, bf16):
+    """Cross keys only, the online softmax started from the oracle's self
+    partial: equals the oracle's merged attention (all rows)."""
+    _announce(f"merged_attn_resume {name}")
+    d = 256 if bf16 else 64
+    case = _attn_case(zlib.crc32(name.encode()) % 1000 + 400, lqs, docs_c, Cmax, nq, nkv, d, bf16)
+    Q, Ks, Vs, Kc, Vc, cm, dop, cu_q = case
+    rows = Q.shape[0]
+    sO, sL = _self_ref(Q, Ks, Vs, cu_q, nq, nkv, d)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    f = torch.float32
+    lse = torch.empty(rows, nq, dtype=f, device="cuda")
+    O = ops.kalm_merged_attn_resume(to_dev(Q, dt), to_dev(sO, f), to_dev(sL, f), to_dev(cu_q, torch.int32), max(lqs),
+                                    to_dev(Kc, dt), to_dev(Vc, dt), to_dev(cm, torch.uint8), to_dev(dop, torch.int32),
+                                    nq, nkv, d, ops.ROWS_ALL, rows, lse=lse)
+    torch.cuda.synchronize()
+    rO, rL = _attn_ref(*case, nq, nkv, d)
+    tol = BF16_TOL if bf16 else F32_TOL
+    assert_close(to_np(O), rO, *tol, f"O resumed ({name})")
+    assert_close(to_np(lse), rL, *tol, f"lse resumed ({name})")
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_merged_attn_resume_final_row_mode(bf16):
+    _announce(f"merged_attn_resume final-row mode bf16={bf16}")
+    d = 256 if bf16 else 64
+    lqs = [1, 33, 64, 100, 7]
+    case = _attn_case(12, lqs, [0, 31, 70, 5, 64], 70, 4, 1, d, bf16)
+    Q, Ks, Vs, Kc, Vc, cm, dop, cu_q = case
+    P = len(lqs)
+    fin = cu_q[1:] - 1
+    sO, sL = _self_ref(Q, Ks, Vs, cu_q, 4, 1, d)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    f = torch.float32
+    O = ops.kalm_merged_attn_resume(to_dev(Q[fin], dt), to_dev(sO[fin], f), to_dev(sL[fin], f),
+                                    to_dev(cu_q, torch.int32), max(lqs), to_dev(Kc, dt), to_dev(Vc, dt),
+                                    to_dev(cm, torch.uint8), to_dev(dop, torch.int32), 4, 1, d, ops.ROWS_FINAL, P)
+    torch.cuda.synchronize()
+    rO, _ = _attn_ref(*case, 4, 1, d)
+    assert_close(to_np(O), rO[fin], *(BF16_TOL if bf16 else F32_TOL), "O resumed final rows")
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_self_partial_then_resume_shared_rows(bf16):
+    """The first-layer reuse: each query's causal self-attention computed once
+    (kalm_self_attn_partial over the per-query packing that kalm_pair_layout
+    gives with one passage), then every pair finished from it with its
+    passage's cross keys (shared rows); equals the oracle's merged attention
+    of every pair."""
+    _announce(f"self partial + resume shared rows bf16={bf16}")
+    d = 256 if bf16 else 32
+    nq, nkv, D, Cmax = 4, 1, 5, 40
+    lq = np.array([5, 37, 70, 1], np.int64)
+    docs_c = [0, 3, 32, 33, 40]
+    U = int(lq.sum())
+    Qu = synth.normal(31, (U, nq * d), 0.7, bf16)
+    Ku = synth.normal(32, (U, nkv * d), 0.7, bf16)
+    Vu = synth.normal(33, (U, nkv * d), 1.0, bf16)
+    Kc = synth.normal(34, (D * Cmax, nkv * d), 0.7, bf16)
+    Vc = synth.normal(35, (D * Cmax, nkv * d), 1.0, bf16)
+    cm = (np.arange(Cmax)[None] < np.asarray(docs_c)[:, None]).astype(np.uint8)
+    Kc.reshape(D, Cmax, -1)[cm == 0] = np.nan
+    Vc.reshape(D, Cmax, -1)[cm == 0] = np.nan
+    starts = np.concatenate([[0], np.cumsum(lq)])
+    idx = np.concatenate([np.arange(starts[q], starts[q + 1]) for q in range(len(lq)) for _ in range(D)])
+    lq_d = to_dev(lq.astype(np.int32), torch.int32)
+    n_q = len(lq)
+    P = n_q * D
+    rows = int(D * U)
+    cu_q = torch.empty(P + 1, dtype=torch.int32, device="cuda")
+    dop = torch.empty(P, dtype=torch.int32, device="cuda")
+    fin = torch.empty(P, dtype=torch.int32, device="cuda")
+    lib = ops.load()
+    ops._check("kalm_pair_layout", lib.kalm_pair_layout(ops._ptr(lq_d), n_q, D, ops._ptr(cu_q), ops._ptr(dop),
+                                                         ops._ptr(fin), None, rows, None))
+    cu_s = torch.empty(n_q + 1, dtype=torch.int32, device="cuda")
+    dop1 = torch.empty(n_q, dtype=torch.int32, device="cuda")
+    fin1 = torch.empty(n_q, dtype=torch.int32, device="cuda")
+    ops._check("kalm_pair_layout", lib.kalm_pair_layout(ops._ptr(lq_d), n_q, 1, ops._ptr(cu_s), ops._ptr(dop1),
+                                                         ops._ptr(fin1), None, U, None))
+    dt = torch.bfloat16 if bf16 else torch.float32
+    Qd, Kd, Vd = to_dev(Qu, dt), to_dev(Ku, dt), to_dev(Vu, dt)
+    sO, sL = ops.kalm_self_attn_partial(Qd, Kd, Vd, cu_s, int(lq.max()), nq, nkv, d)
+    O = ops.kalm_merged_attn_resume(Qd, sO, sL, cu_q, int(lq.max()), to_dev(Kc, dt), to_dev(Vc, dt),
+                                    to_dev(cm, torch.uint8), dop, nq, nkv, d, ops.ROWS_SHARED, rows)
+    torch.cuda.synchronize()
+    cu_np = np.concatenate([[0], np.cumsum(np.repeat(lq, D))]).astype(np.int32)
+    assert (to_np(cu_q) == cu_np).all()
+    dop_np = (np.arange(P) % D).astype(np.int32)
+    rO, _ = _attn_ref(Qu[idx], Ku[idx], Vu[idx], Kc, Vc, cm, dop_np, cu_np, nq, nkv, d)
+    assert_close(to_np(O), rO, *(BF16_TOL if bf16 else F32_TOL), "O self partial + resume")
+
+
+def test_merged_attn_resume_bad_doc_gives_nan_rows():
+    _announce("merged_attn_resume out-of-range doc")
+    case = _attn_case(13, [20, 20], [5, 5], 32, 4, 1, 256, True)
+    Q, Ks, Vs, Kc, Vc, cm, dop, cu_q = case
+    sO, sL = _self_ref(Q, Ks, Vs, cu_q, 4, 1, 256)
+    dop = np.array([0, 7], np.int32)
+    bf, f = torch.bfloat16, torch.float32
+    O = ops.kalm_merged_attn_resume(to_dev(Q, bf), to_dev(sO, f), to_dev(sL, f), to_dev(cu_q, torch.int32), 20,
+                                    to_dev(Kc, bf), to_dev(Vc, bf), to_dev(cm, torch.uint8), to_dev(dop, torch.int32),
+                                    4, 1, 256, ops.ROWS_ALL, 40)
+    g = to_np(O)
+    assert np.isfinite(g[:20]).all() and np.isnan(g[20:]).all()
+
+
 # ------------------------------------------------------------------ a4 score
 @pytest.mark.parametrize("H,hb,wb", [(640, False, True), (1152, True, True), (64, False, False)])
 def test_yesno_score_parity(H, hb, wb):

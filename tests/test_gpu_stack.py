@@ -85,16 +85,18 @@ def test_stack_edge_empty_and_one_token_passages():
     _check(inp, b, got, list(range(sh.pairs)))
 
 
-def test_stack_pruned_path_equals_full_path():
-    # the shared first layer and the final-row last layer change how much is
-    # computed, not the result: scores of both paths agree, and with the oracle
+@pytest.mark.parametrize("reuse_self", [True, False])
+def test_stack_pruned_path_equals_full_path(reuse_self):
+    # the shared first layer (with or without its self part computed once per
+    # query) and the final-row last layer change how much is computed, not the
+    # result: scores of both paths agree, and with the oracle
     idx = 2
     sh = synth.SHAPES[idx]
-    print(f"[case] stack {sh.name} 3 layers, pruned vs full", flush=True)
+    print(f"[case] stack {sh.name} 3 layers, pruned (reuse_self={reuse_self}) vs full", flush=True)
     inp = synth.make_inputs(idx, nan_padding=True, n_layers=3)
     b = stack.upload(inp)
     full = to_np(stack.step(b, prune=False)[3])
-    pruned = to_np(stack.step(b, prune=True)[3])
+    pruned = to_np(stack.step(b, prune=True, reuse_self=reuse_self)[3])
     torch.cuda.synchronize()
     assert_close(pruned, full, 1e-3, 0.0, "pruned vs full score")
     pairs = _sample_pairs(inp, 8)
