@@ -45,12 +45,12 @@ RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop/byte where the tw
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 MEASURED_TRAFFIC = {
     # profiles/hbm_traffic_small_stack26_bf16.md
-    "o_linear": {"src": "fd5eb7414845840a34a0ebbd82b2cf7ea9722515f7cf965bff0fb7fda6bc9da5",
-                 "fetch_kib": 2953030.8, "write_kib": 6481559.6},
-    "qkv_linear": {"src": "fd5eb7414845840a34a0ebbd82b2cf7ea9722515f7cf965bff0fb7fda6bc9da5",
-                   "fetch_kib": 2387936.1, "write_kib": 2688305.4},
-    "merged_attn": {"src": "cebac1591ed9257c11a795ad71e64c15b8ac94be7dfbcf5982a89c3a0d3c1451",
-                    "fetch_kib": 1482533.5, "write_kib": 1792200.0},
+    "o_linear": {"src": "1ac37431fbadf90a7420ae28adc0c318d18297856aeb8e2bbeac68bd819470da",
+                 "fetch_kib": 3107738.0, "write_kib": 6443285.0},
+    "qkv_linear": {"src": "1ac37431fbadf90a7420ae28adc0c318d18297856aeb8e2bbeac68bd819470da",
+                   "fetch_kib": 2385666.0, "write_kib": 2616612.0},
+    "merged_attn": {"src": "c6c79ac4186c8f138fef4c9840b2afca7f4919d640011c5b16bba3f476e7413a",
+                    "fetch_kib": 1483483.0, "write_kib": 1792200.0},
 }
 KERNEL_SRC = {"o_linear": "gemm.hip", "qkv_linear": "gemm.hip", "cross_kv": "gemm.hip",
               "merged_attn": "attn_bf16.h", "chunk_pool": "pool.hip", "gather_rows": "rows.hip"}
