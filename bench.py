@@ -116,7 +116,7 @@ class EventRec:
         return {k: [s.elapsed_time(e) for s, e in v] for k, v in self.ev.items()}
 
 
-def work_model(inp, sh):
+def work_model(inp, sh, single=False):
     """Algorithmic work per launch of each recorded call (flops and bytes).
 
     Names follow the step: the full-size projections and attention of the
@@ -142,6 +142,26 @@ def work_model(inp, sh):
 
     def linear(M, K, N, out_bytes):
         return dict(flops=2.0 * M * K * N, bytes=float(M * K * e + N * K * e + out_bytes))
+
+    if single:
+        # one pruned layer: the queries' own rows and every pair's final row only
+        nQ = len(lq)
+        return {
+            "qkv_linear_first": linear(U, H, nqkv, U * nqkv * e),
+            "self_attn_first": dict(flops=float(4 * nq * d * self_keys // D),
+                                    bytes=float(U * qd * e + 2 * U * kv * e + U * qd * 4 + U * nq * 4)),
+            "merged_attn_first_resume": dict(flops=float(4 * nq * d * nQ * int(C.sum())),
+                                             bytes=float(nQ * qd * e + nQ * (qd + nq) * 4 + cross_bytes
+                                                         + P * qd * e)),
+            "merged_attn_first": dict(flops=float(last_flops),
+                                      bytes=float(nQ * qd * e + 2 * U * kv * e + cross_bytes + P * qd * e)),
+            "o_linear_last": linear(P, qd, H, P * H * 8),
+            "cross_kv": dict(flops=2.0 * int(C.sum()) * H * 2 * kv, bytes=float(D * Cmax * (H + 2 * kv) * e)),
+            "chunk_pool": dict(flops=0.0, bytes=float(int(dl.sum()) * H * e + D * Cmax * H * e + D * T + D * Cmax
+                                                      + 4 * D)),
+            "gather_query_rows": dict(flops=0.0, bytes=float(U * H * (4 + 4 + 2))),
+            "gather_final_rows": dict(flops=0.0, bytes=float(P * H * (4 + 4))),
+        }
 
     return {
         "merged_attn": dict(flops=float(attn_flops), bytes=float(2 * rows * qd * e + self_bytes + cross_bytes)),
@@ -285,7 +305,7 @@ def main():
     print(f"[bench] {a.steps} steps: {ms_step:.2f} ms/step, {pairs_s:.1f} pairs/s", file=sys.stderr, flush=True)
 
     dur = rec.durations_ms()
-    work = work_model(inp, sh)
+    work = work_model(inp, sh, single=not a.no_prune and sh.n_layers == 1)
     kernels = {}
     for k, v in dur.items():
         n_per = len(v) / a.steps

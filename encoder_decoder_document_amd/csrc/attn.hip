@@ -102,7 +102,7 @@ void launch_merged_attn_f32(const float* Q, int64_t q_ld, const float* Ks, const
                             const uint8_t* cmask, const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv,
                             int d, float scale, float* O, int64_t o_ld, float* lse, int part, const float* oi,
                             int64_t oi_ld, const float* lsei, hipStream_t s) {
-  const int max_rows = mode == 1 ? 1 : max_lq;
+  const int max_rows = (mode == 1 || mode == 3) ? 1 : max_lq;
   if (P == 0 || max_rows == 0) return;
   const int nrb = (max_rows + 3) / 4;  // 4 rows (one per wave) per block
   const dim3 grid((unsigned)((int64_t)nrb * nq * P)), block(256);

@@ -92,7 +92,10 @@ __device__ __forceinline__ void lds_write8(uint32_t addr, u32x2_t v) { *(lds_u32
 //                        (self K/V rows still start at cu_q[p]);
 //   mode 2 (shared):     Q and self K/V are the rows of the pair's query
 //                        (p / D), shared by all its D passages, at cu_q[qD]/D;
-//                        O rows start at cu_q[p].
+//                        O rows start at cu_q[p];
+//   mode 3 (shared final row): the final position only, of the shared rows:
+//                        Q row cu_q[qD]/D + Lq-1, self K/V rows as mode 2,
+//                        O row p.
 // A pair whose rows fall outside the given row counts is skipped (no access).
 struct PairRows {
   int64_t kv0, q0, o0;
@@ -105,14 +108,19 @@ __device__ __forceinline__ PairRows pair_rows(const int32_t* __restrict__ cu_q, 
   const int64_t c0 = cu_q[p];
   pr.Lq = (int)((int64_t)cu_q[p + 1] - c0);
   pr.kv0 = pr.q0 = pr.o0 = c0;
-  if (mode == 2) {
+  const bool fin = mode == 1 || mode == 3;
+  if (mode == 2 || mode == 3) {
     const int64_t qs = (int64_t)cu_q[(int64_t)(p / D) * D] / D;
     pr.kv0 = pr.q0 = qs;
+    if (mode == 3) {
+      pr.q0 = qs + pr.Lq - 1;
+      pr.o0 = p;
+    }
   } else if (mode == 1) {
     pr.q0 = pr.o0 = p;
   }
-  pr.nrow = mode == 1 ? (pr.Lq > 0 ? 1 : 0) : pr.Lq;
-  pr.pos0 = mode == 1 ? pr.Lq - 1 : 0;
+  pr.nrow = fin ? (pr.Lq > 0 ? 1 : 0) : pr.Lq;
+  pr.pos0 = fin ? pr.Lq - 1 : 0;
   pr.ok = c0 >= 0 && pr.Lq >= 0 && pr.kv0 >= 0 && pr.kv0 + pr.Lq <= kv_rows && pr.q0 >= 0 &&
           pr.q0 + pr.nrow <= q_rows && pr.o0 >= 0 && pr.o0 + pr.nrow <= o_rows;
   return pr;
@@ -561,9 +569,11 @@ bf16_kernel_t pick_bf16_kernel(int sel) {
     case 1: return merged_attn_bf16_kernel<NH, NW, RT, 0, 0>;
     case 2: return merged_attn_bf16_kernel<NH, NW, RT, 1, 0>;
     case 3: return merged_attn_bf16_kernel<NH, NW, RT, 2, 0>;
-    case 4: return merged_attn_bf16_kernel<NH, NW, RT, 0, 2>;
-    case 5: return merged_attn_bf16_kernel<NH, NW, RT, 1, 2>;
-    default: return merged_attn_bf16_kernel<NH, NW, RT, 2, 2>;
+    case 4: return merged_attn_bf16_kernel<NH, NW, RT, 3, 0>;
+    case 5: return merged_attn_bf16_kernel<NH, NW, RT, 0, 2>;
+    case 6: return merged_attn_bf16_kernel<NH, NW, RT, 1, 2>;
+    case 7: return merged_attn_bf16_kernel<NH, NW, RT, 2, 2>;
+    default: return merged_attn_bf16_kernel<NH, NW, RT, 3, 2>;
   }
 }
 
@@ -577,7 +587,7 @@ void launch_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, const bf16_t* 
   const int G = nq / nkv;
   const int NH = G >= 4 ? 4 : G;  // heads per block (G is 1, 2 or a multiple of 4)
   const int RB = 32 * RT * (NW / NH);
-  const int max_rows = mode == 1 ? 1 : max_lq;  // query rows per pair
+  const int max_rows = (mode == 1 || mode == 3) ? 1 : max_lq;  // query rows per pair
   const int nqb = (max_rows + RB - 1) / RB;
   const int64_t blocks = (int64_t)P * nkv * (G / NH) * nqb;
   const float sl2 = scale * 1.4426950408889634f;
@@ -589,7 +599,7 @@ void launch_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, const bf16_t* 
   };
   // one instantiation per (heads per block, row mode, part); a self partial
   // (part 1) runs on all rows of its sequences (mode 0) only
-  const int sel = part == 1 ? 0 : 1 + 3 * (part == 2) + mode;  // 0 | 1..3 merged | 4..6 resumed
+  const int sel = part == 1 ? 0 : 1 + 4 * (part == 2) + mode;  // 0 | 1..4 merged | 5..8 resumed
   if (NH == 4) go(pick_bf16_kernel<4, NW, RT>(sel));
   else if (NH == 2) go(pick_bf16_kernel<2, NW, RT>(sel));
   else go(pick_bf16_kernel<1, NW, RT>(sel));

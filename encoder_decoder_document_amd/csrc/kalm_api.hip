@@ -59,7 +59,7 @@ kalm_status kalm_device_check(void) { return kalm::check_device(); }
 
 kalm_status kalm_pair_layout(const int32_t* lq, int32_t n_queries, int32_t n_docs, int32_t* cu_q,
                              int32_t* doc_of_pair, int32_t* final_row, int32_t* h0_row, int64_t rows,
-                             void* stream) {
+                             int32_t* h0_final, void* stream) {
   kalm::g_err[0] = 0;
   KALM_REQUIRE(n_queries >= 0 && n_docs >= 0, KALM_ERR_INVALID_ARG, "kalm_pair_layout: negative sizes");
   KALM_REQUIRE((int64_t)n_queries * n_docs < (1LL << 31), KALM_ERR_UNSUPPORTED, "kalm_pair_layout: too many pairs");
@@ -67,7 +67,8 @@ kalm_status kalm_pair_layout(const int32_t* lq, int32_t n_queries, int32_t n_doc
                "kalm_pair_layout: null pointer");
   KALM_REQUIRE(rows >= 0 && rows < (1LL << 31), KALM_ERR_INVALID_ARG, "kalm_pair_layout: rows out of range");
   KALM_DEVICE_OR_RETURN();
-  kalm::launch_pair_layout(lq, n_queries, n_docs, cu_q, doc_of_pair, final_row, h0_row, rows, (hipStream_t)stream);
+  kalm::launch_pair_layout(lq, n_queries, n_docs, cu_q, doc_of_pair, final_row, h0_row, rows, h0_final,
+                           (hipStream_t)stream);
   return kalm::check_launch("kalm_pair_layout");
 }
 
@@ -150,10 +151,11 @@ static kalm_status merged_attn_impl(const char* fn, const void* Q, int64_t q_ld,
                                     const float* lsei = nullptr) {
   kalm::g_err[0] = 0;
   KALM_REQUIRE(dt == KALM_F32 || dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)dt);
-  KALM_REQUIRE(row_mode >= 0 && row_mode <= 2, KALM_ERR_INVALID_ARG, "%s: row_mode %d not in 0..2", fn, row_mode);
+  KALM_REQUIRE(row_mode >= 0 && row_mode <= 3, KALM_ERR_INVALID_ARG, "%s: row_mode %d not in 0..3", fn, row_mode);
   KALM_REQUIRE(P >= 0 && q_rows >= 0 && kv_rows >= 0 && o_rows >= 0 && max_lq >= 0 && D >= 0 && Cmax >= 0,
                KALM_ERR_INVALID_ARG, "%s: negative sizes", fn);
-  KALM_REQUIRE(row_mode != 2 || P == 0 || D >= 1, KALM_ERR_INVALID_ARG, "%s: row_mode 2 needs D >= 1", fn);
+  KALM_REQUIRE(row_mode < 2 || P == 0 || D >= 1, KALM_ERR_INVALID_ARG, "%s: row_mode %d needs D >= 1", fn,
+               row_mode);
   KALM_REQUIRE(nq >= 1 && nkv >= 1 && nq % nkv == 0, KALM_ERR_INVALID_ARG, "%s: nq=%d nkv=%d", fn, nq, nkv);
   KALM_REQUIRE(scale > 0.f, KALM_ERR_INVALID_ARG, "%s: scale must be positive", fn);
   // part 1 reads no cross keys and no passage index; part 2 reads no self keys

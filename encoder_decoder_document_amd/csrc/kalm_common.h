@@ -119,7 +119,7 @@ namespace kalm {
 void launch_chunk_pool(const void* x, const uint8_t* mask, int D, int T, int H, int chunk, int Cmax,
                        kalm_dtype dt, void* pooled, uint8_t* cmask, int32_t* n_chunks, hipStream_t s);
 void launch_pair_layout(const int32_t* lq, int nQ, int nD, int32_t* cu_q, int32_t* doc_of_pair,
-                        int32_t* final_row, int32_t* h0_row, int64_t rows, hipStream_t s);
+                        int32_t* final_row, int32_t* h0_row, int64_t rows, int32_t* h0_final, hipStream_t s);
 void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, void* Y, bool y_f32,
                         bool accumulate, bf16_t* Y_bf16, const uint8_t* row_mask, hipStream_t s);
 void launch_linear_f32(const float* X, const float* W, int M, int K, int N, float* Y, bool accumulate,

@@ -16,7 +16,8 @@ namespace {
 __global__ __launch_bounds__(1024) void pair_layout_kernel(const int32_t* __restrict__ lq, int nQ,
                                                            int nD, int32_t* __restrict__ cu_q,
                                                            int32_t* __restrict__ doc_of_pair,
-                                                           int32_t* __restrict__ final_row) {
+                                                           int32_t* __restrict__ final_row,
+                                                           int32_t* __restrict__ h0_final) {
   __shared__ int32_t scan[1024];
   __shared__ int32_t carry;
   if (threadIdx.x == 0) carry = 0;
@@ -40,6 +41,7 @@ __global__ __launch_bounds__(1024) void pair_layout_kernel(const int32_t* __rest
         cu_q[p] = r0;
         doc_of_pair[p] = dd;
         final_row[p] = r0 + len - 1;
+        if (h0_final) h0_final[p] = start + len - 1;
       }
     }
     __syncthreads();
@@ -165,8 +167,9 @@ void launch_rank_topn(const float* score, int n_queries, int D, int top_n, int32
 
 
 void launch_pair_layout(const int32_t* lq, int nQ, int nD, int32_t* cu_q, int32_t* doc_of_pair,
-                        int32_t* final_row, int32_t* h0_row, int64_t rows, hipStream_t s) {
-  hipLaunchKernelGGL(pair_layout_kernel, dim3(1), dim3(1024), 0, s, lq, nQ, nD, cu_q, doc_of_pair, final_row);
+                        int32_t* final_row, int32_t* h0_row, int64_t rows, int32_t* h0_final, hipStream_t s) {
+  hipLaunchKernelGGL(pair_layout_kernel, dim3(1), dim3(1024), 0, s, lq, nQ, nD, cu_q, doc_of_pair, final_row,
+                     h0_final);
   if (h0_row && (int64_t)nQ * nD > 0)
     hipLaunchKernelGGL(h0_row_kernel, dim3((unsigned)((int64_t)nQ * nD)), dim3(256), 0, s, cu_q, nD, h0_row, rows);
 }

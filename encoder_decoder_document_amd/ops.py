@@ -31,7 +31,7 @@ _SIGS = {
     "kalm_version": (_i32, []),
     "kalm_last_error": (ctypes.c_char_p, []),
     "kalm_device_check": (_i32, []),
-    "kalm_pair_layout": (_i32, [_c_p, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _i64, _c_p]),
+    "kalm_pair_layout": (_i32, [_c_p, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _i64, _c_p, _c_p]),
     "kalm_chunk_pool": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p]),
     "kalm_cross_kv": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _c_p, _i32, _i32, _c_p, _c_p]),
     "kalm_merged_attn": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i32, _i64, _i32, _c_p, _c_p, _i64,
@@ -123,7 +123,7 @@ def device_check() -> int:
 
 def kalm_pair_layout(lq: torch.Tensor, n_docs: int, rows: Optional[int] = None, with_h0_row: bool = True,
                      stream=None):
-    """lq [Q] int32 (device) -> dict(cu_q, doc_of_pair, final_row, h0_row)."""
+    """lq [Q] int32 (device) -> dict(cu_q, doc_of_pair, final_row, h0_row, h0_final)."""
     _contig(lq)
     Qn = lq.numel()
     P = Qn * n_docs
@@ -136,9 +136,10 @@ def kalm_pair_layout(lq: torch.Tensor, n_docs: int, rows: Optional[int] = None, 
         if rows is None:
             raise ValueError("rows (= n_docs * sum(lq)) is needed for h0_row")
         h0 = torch.empty(rows, dtype=torch.int32, device=dev)
+    h0f = torch.empty(P, dtype=torch.int32, device=dev)
     _check("kalm_pair_layout", load().kalm_pair_layout(_ptr(lq), Qn, n_docs, _ptr(cu_q), _ptr(doc), _ptr(fin),
-                                                      _ptr(h0), rows or 0, _stream(stream)))
-    return dict(cu_q=cu_q, doc_of_pair=doc, final_row=fin, h0_row=h0)
+                                                      _ptr(h0), rows or 0, _ptr(h0f), _stream(stream)))
+    return dict(cu_q=cu_q, doc_of_pair=doc, final_row=fin, h0_row=h0, h0_final=h0f)
 
 
 def kalm_chunk_pool(x: torch.Tensor, token_mask: torch.Tensor, chunk: int = 4, out=None, stream=None):
@@ -192,7 +193,7 @@ def kalm_merged_attn(Q: torch.Tensor, Ks: torch.Tensor, Vs: torch.Tensor, cu_q: 
     return out
 
 
-ROWS_ALL, ROWS_FINAL, ROWS_SHARED = 0, 1, 2
+ROWS_ALL, ROWS_FINAL, ROWS_SHARED, ROWS_SHARED_FINAL = 0, 1, 2, 3
 
 
 def kalm_merged_attn_rows(Q: torch.Tensor, Ks: torch.Tensor, Vs: torch.Tensor, cu_q: torch.Tensor, max_lq: int,

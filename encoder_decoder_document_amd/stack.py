@@ -18,11 +18,13 @@ With ``prune`` (the default) two layers do less work for the same result:
     passage's cross keys (kalm_merged_attn_resume, shared rows) -- or, without
     ``reuse_self``, each pair reads the shared rows in one merged pass
     (kalm_merged_attn_rows, shared rows);
-  * the last layer (stacks of two or more layers): the score reads only each
-    pair's final position ("KaLM-Reranker-V1-Nano -- MLX (Apple Silicon)",
-    What this is), so self K/V are projected for every row but Q, attention,
-    the output projection and the residual update only for the final rows
-    (kalm_merged_attn_rows, final row).
+  * the last layer: the score reads only each pair's final position
+    ("KaLM-Reranker-V1-Nano -- MLX (Apple Silicon)", What this is), so self K/V
+    are projected for every row but Q, attention, the output projection and the
+    residual update only for the final rows (kalm_merged_attn_rows, final row);
+    in a one-layer stack, where the first layer is also the last, only the
+    queries' own rows and each pair's final row are computed at all (shared
+    final row; the residual starts from the query's final hidden state).
 
 The decoder layer is the reading stated on the pages' behalf: the pages give
 only the layer counts ("KaLM-Reranker-V1-Nano -- MLX (Apple Silicon)", What
@@ -95,6 +97,7 @@ def upload(inputs: Dict[str, object], device="cuda", n_layers: Optional[int] = N
         cu_q=torch.empty(P + 1, dtype=torch.int32, device=device),
         doc_of_pair=torch.empty(P, dtype=torch.int32, device=device),
         final_row=torch.empty(P, dtype=torch.int32, device=device),
+        h0_final=torch.empty(P, dtype=torch.int32, device=device),
         h0_row=torch.empty(rows, dtype=torch.int32, device=device),
         pooled=torch.empty(D, Cmax, H, dtype=dt, device=device),
         chunk_mask=torch.empty(D, Cmax, dtype=torch.uint8, device=device),
@@ -141,14 +144,15 @@ def front(b: DeviceBatch, stream=None, rec=_no_rec):
     ``rec(name)`` is an optional context-manager factory wrapped around each call
     (the benchmark records HIP events with it)."""
     B = b.buf
-    lay = dict(cu_q=B["cu_q"], doc_of_pair=B["doc_of_pair"], final_row=B["final_row"], h0_row=B["h0_row"])
+    lay = dict(cu_q=B["cu_q"], doc_of_pair=B["doc_of_pair"], final_row=B["final_row"], h0_row=B["h0_row"],
+               h0_final=B["h0_final"])
     _check = ops._check
     lib = ops.load()
     s = ops._stream(stream)
     with rec("pair_layout"):
         _check("kalm_pair_layout", lib.kalm_pair_layout(
             ops._ptr(b.lq), b.n_queries, b.D, ops._ptr(lay["cu_q"]), ops._ptr(lay["doc_of_pair"]),
-            ops._ptr(lay["final_row"]), ops._ptr(lay["h0_row"]), b.rows, s))
+            ops._ptr(lay["final_row"]), ops._ptr(lay["h0_row"]), b.rows, ops._ptr(lay["h0_final"]), s))
     with rec("chunk_pool"):
         ops.kalm_chunk_pool(b.x, b.token_mask, b.chunk, out=(B["pooled"], B["chunk_mask"], B["n_chunks"]),
                             stream=stream)
@@ -158,8 +162,8 @@ def front(b: DeviceBatch, stream=None, rec=_no_rec):
 
 
 def pruned(b: DeviceBatch, prune: bool = True) -> bool:
-    """Whether the last layer runs on final rows only (needs two or more layers)."""
-    return prune and b.n_layers >= 2
+    """Whether the last layer runs on final rows only (the score reads nothing else)."""
+    return prune and b.n_layers >= 1
 
 
 def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_self: bool = True):
@@ -170,8 +174,12 @@ def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_
     B = b.buf
     bf = b.dtype == torch.bfloat16
     qd, kv = b.nq * b.d, b.nkv * b.d
-    with rec("gather_rows"):
-        ops.kalm_gather_rows(b.h0, B["h0_row"], dst=B["h"], dst_bf16=B["hb"] if bf else None, stream=stream)
+    # one pruned layer is both the first and the last: only the queries' own
+    # rows and the pairs' final rows are ever computed
+    single = prune and b.n_layers == 1
+    if not single:
+        with rec("gather_rows"):
+            ops.kalm_gather_rows(b.h0, B["h0_row"], dst=B["h"], dst_bf16=B["hb"] if bf else None, stream=stream)
     qkv = B["qkv"]
     Q, Ks, Vs = qkv[:, :qd], qkv[:, qd:qd + kv], qkv[:, qd + kv:]
     scale = 1.0 / math.sqrt(b.d)
@@ -187,12 +195,15 @@ def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_
             u = B["qkv_u"]
             with rec("qkv_linear_first"):
                 ops.kalm_linear(B["h0b"] if bf else b.h0, b.Wqkv[0], Y=u, stream=stream)
+            # every row of every pair, or (single layer) the final row of every pair
+            rmode, o_rows, o_buf = ((ops.ROWS_SHARED_FINAL, b.P, B["of"]) if single
+                                    else (ops.ROWS_SHARED, b.rows, B["o"]))
             if reuse_self:
                 # the query's causal self-attention once, then each pair from it with its passage's cross keys
                 with rec("pair_layout_queries"):
                     ops._check("kalm_pair_layout", ops.load().kalm_pair_layout(
                         ops._ptr(b.lq), b.n_queries, 1, ops._ptr(B["cu_s"]), ops._ptr(B["doc_s"]),
-                        ops._ptr(B["fin_s"]), None, 0, ops._stream(stream)))
+                        ops._ptr(B["fin_s"]), None, 0, None, ops._stream(stream)))
                 with rec("self_attn_first"):
                     ops.kalm_self_attn_partial(u[:, :qd], u[:, qd:qd + kv], u[:, qd + kv:], B["cu_s"], b.max_lq,
                                                b.nq, b.nkv, b.d, scale=scale, out=B["o_self"], lse=B["lse_self"],
@@ -200,15 +211,20 @@ def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_
                 with rec("merged_attn_first_resume"):
                     ops.kalm_merged_attn_resume(u[:, :qd], B["o_self"], B["lse_self"], B["cu_q"], b.max_lq,
                                                 kvc[:, :kv], kvc[:, kv:], B["chunk_mask"], B["doc_of_pair"], b.nq,
-                                                b.nkv, b.d, ops.ROWS_SHARED, b.rows, scale=scale, out=B["o"],
-                                                stream=stream)
+                                                b.nkv, b.d, rmode, o_rows, scale=scale, out=o_buf, stream=stream)
             else:
                 with rec("merged_attn_first"):
                     ops.kalm_merged_attn_rows(u[:, :qd], u[:, qd:qd + kv], u[:, qd + kv:], B["cu_q"], b.max_lq,
                                               kvc[:, :kv], kvc[:, kv:], B["chunk_mask"], B["doc_of_pair"], b.nq,
-                                              b.nkv, b.d, ops.ROWS_SHARED, b.rows, scale=scale, out=B["o"],
-                                              stream=stream)
-        elif last_pruned and l == b.n_layers - 1:
+                                              b.nkv, b.d, rmode, o_rows, scale=scale, out=o_buf, stream=stream)
+            if single:
+                # each pair's residual starts from its query's final hidden state
+                with rec("gather_final_rows"):
+                    ops.kalm_gather_rows(b.h0, B["h0_final"], dst=B["hf"], stream=stream)
+                with rec("o_linear_last"):
+                    ops.kalm_linear(B["of"], b.Wo[l], Y=B["hf"], accumulate=True, stream=stream)
+                continue
+        elif last_pruned and l == b.n_layers - 1 and l > 0:
             # final rows only: self K/V of every row, Q / attention / projection of the final rows
             kvs = qkv.view(-1)[: b.rows * 2 * kv].view(b.rows, 2 * kv)
             with rec("kv_linear_last"):

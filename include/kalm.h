@@ -73,10 +73,12 @@ kalm_status kalm_device_check(void);
  *   h0_row    [rows] int32 out, nullable: row of the query's first-layer hidden
  *             state (queries packed in order) that pair row r starts from
  *   rows      capacity of h0_row; must equal n_docs * sum(lq) when h0_row is given
+ *   h0_final  [P] int32 out, nullable: that row for the pair's final position
+ *             (the query's last row in the per-query packing)
  */
 kalm_status kalm_pair_layout(const int32_t* lq, int32_t n_queries, int32_t n_docs,
                              int32_t* cu_q, int32_t* doc_of_pair, int32_t* final_row,
-                             int32_t* h0_row, int64_t rows, void* stream);
+                             int32_t* h0_row, int64_t rows, int32_t* h0_final, void* stream);
 
 /*
  * a1 -- chunk pooling ([Q80] Frozen inference contract: masked mean over
@@ -165,9 +167,13 @@ kalm_status kalm_merged_attn(const void* Q, int64_t q_ld, const void* Ks, const 
  *      holds the query's own hidden states (the decoder models the query,
  *      [MLX] What this is; one passage set reranked against many queries,
  *      [MLX] Speed), their Q/K/V projections are one set of rows.
+ *   3  the final position of the shared rows: Q row cu_q[(p/D)*D] / D + Lq-1
+ *      (the query's last row in the per-query packing), Ks/Vs rows as mode 2,
+ *      O/lse row p.  A one-layer stack needs nothing else: its only layer is
+ *      both the first and the last.
  *   q_rows, kv_rows, o_rows  rows in Q, in Ks/Vs and in O (and lse); a pair
  *      whose rows fall outside them is skipped (its outputs are not written).
- * Other arguments as kalm_merged_attn; row_mode outside 0..2 is
+ * Other arguments as kalm_merged_attn; row_mode outside 0..3 is
  * KALM_ERR_INVALID_ARG.
  */
 kalm_status kalm_merged_attn_rows(const void* Q, int64_t q_ld, int64_t q_rows, const void* Ks,
@@ -213,7 +219,7 @@ kalm_status kalm_self_attn_partial(const void* Q, int64_t q_ld, const void* Ks, 
  * the online softmax starts from (o_self, lse_self) of the Q row, so that
  *   O = (e^lse_self o_self + sum_c e^s_c v_c) / (e^lse_self + sum_c e^s_c)
  * and lse (nullable) is the log-sum-exp of all of the row's logits.
- * Rows follow kalm_merged_attn_rows with the same row_mode (0..2); o_self
+ * Rows follow kalm_merged_attn_rows with the same row_mode (0..3); o_self
  * [q_rows, *] float (row stride s_ld, elements, s_ld % 4 == 0 and 16-byte
  * aligned for bf16) and lse_self [q_rows, nq] are indexed like Q.  With the
  * partial of kalm_self_attn_partial on the same Q/K/V rows the result is that

@@ -256,14 +256,15 @@ def pair_layout(lq: Sequence[int], n_docs: int):
     score is read at the pair's last row ([MLX] What this is: final position).
 
     Returns dict(cu_q [P+1], doc_of_pair [P], query_of_pair [P],
-    final_row [P], h0_row [rows]) as int32, where h0_row[r] is the row of the
-    query's first-layer hidden state that pair row r starts from.
+    final_row [P], h0_row [rows], h0_final [P]) as int32, where h0_row[r] is
+    the row of the query's first-layer hidden state that pair row r starts
+    from and h0_final[p] that row for the pair's final position.
     """
     lq = [int(v) for v in lq]
     Qn = len(lq)
     P = Qn * n_docs
     cu_q = [0]
-    doc_of_pair, query_of_pair, final_row, h0_row = [], [], [], []
+    doc_of_pair, query_of_pair, final_row, h0_row, h0_final = [], [], [], [], []
     q_start = [0]
     for v in lq:
         q_start.append(q_start[-1] + v)
@@ -273,12 +274,13 @@ def pair_layout(lq: Sequence[int], n_docs: int):
         doc_of_pair.append(dd)
         query_of_pair.append(q)
         final_row.append(cu_q[-1] + n - 1)
+        h0_final.append(q_start[q] + n - 1)
         for r in range(n):
             h0_row.append(q_start[q] + r)
         cu_q.append(cu_q[-1] + n)
     i32 = lambda v: np.asarray(v, dtype=np.int32)
     return dict(cu_q=i32(cu_q), doc_of_pair=i32(doc_of_pair), query_of_pair=i32(query_of_pair),
-                final_row=i32(final_row), h0_row=i32(h0_row))
+                final_row=i32(final_row), h0_row=i32(h0_row), h0_final=i32(h0_final))
 
 
 # --------------------------------------------------------------------------

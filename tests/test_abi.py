@@ -74,8 +74,11 @@ def test_invalid_arguments_rejected_before_launch():
     assert st == ops.KALM_ERR_INVALID_ARG
     # attention over a choice of rows: unknown row mode; shared rows without passages
     st = lib.kalm_merged_attn_rows(None, 1024, 0, None, None, 512, 0, None, 0, 0, None, None, 512, None, None, 0, 0,
-                                   4, 1, 256, 0.1, ops.KALM_BF16, None, 1024, 0, None, 3, None)
+                                   4, 1, 256, 0.1, ops.KALM_BF16, None, 1024, 0, None, 4, None)
     assert st == ops.KALM_ERR_INVALID_ARG and b"row_mode" in lib.kalm_last_error()
+    st = lib.kalm_merged_attn_rows(None, 1024, 0, None, None, 512, 0, None, 1, 0, None, None, 512, None, None, 0, 0,
+                                   4, 1, 256, 0.1, ops.KALM_BF16, None, 1024, 0, None, 3, None)
+    assert st == ops.KALM_ERR_INVALID_ARG and b"D >= 1" in lib.kalm_last_error()
     st = lib.kalm_merged_attn_rows(None, 1024, 0, None, None, 512, 0, None, 1, 0, None, None, 512, None, None, 0, 0,
                                    4, 1, 256, 0.1, ops.KALM_BF16, None, 1024, 0, None, 2, None)
     assert st == ops.KALM_ERR_INVALID_ARG
@@ -83,12 +86,12 @@ def test_invalid_arguments_rejected_before_launch():
     st = lib.kalm_self_attn_partial(1, 1024, 1, 1, 512, 10, 1, 1, 10, 4, 1, 256, 0.1, ops.KALM_BF16, 1, 1024, None,
                                     None)
     assert st == ops.KALM_ERR_INVALID_ARG and b"lse" in lib.kalm_last_error()
-    # resume: the self partial is required; row_mode outside 0..2; partial stride smaller than the heads
+    # resume: the self partial is required; row_mode outside 0..3; partial stride smaller than the heads
     st = lib.kalm_merged_attn_resume(1, 1024, 10, None, 1024, None, 1, 1, 10, 1, 1, 512, 1, 1, 1, 8, 4, 1, 256, 0.1,
                                      ops.KALM_BF16, 1, 1024, 10, None, 0, None)
     assert st == ops.KALM_ERR_INVALID_ARG and b"self-partial" in lib.kalm_last_error()
     st = lib.kalm_merged_attn_resume(1, 1024, 10, 1, 1024, 1, 1, 1, 10, 1, 1, 512, 1, 1, 1, 8, 4, 1, 256, 0.1,
-                                     ops.KALM_BF16, 1, 1024, 10, None, 3, None)
+                                     ops.KALM_BF16, 1, 1024, 10, None, -1, None)
     assert st == ops.KALM_ERR_INVALID_ARG and b"row_mode" in lib.kalm_last_error()
     st = lib.kalm_merged_attn_resume(1, 1024, 10, 1, 512, 1, 1, 1, 10, 1, 1, 512, 1, 1, 1, 8, 4, 1, 256, 0.1,
                                      ops.KALM_BF16, 1, 1024, 10, None, 0, None)

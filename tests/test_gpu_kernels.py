@@ -35,7 +35,7 @@ def test_pair_layout_bit_exact(lq, D):
     got = ops.kalm_pair_layout(to_dev(lq, torch.int32), D, rows=rows)
     torch.cuda.synchronize()
     ref = oracle.pair_layout(lq, D)
-    for k in ("cu_q", "doc_of_pair", "final_row", "h0_row"):
+    for k in ("cu_q", "doc_of_pair", "final_row", "h0_row", "h0_final"):
         assert np.array_equal(got[k].cpu().numpy(), ref[k]), k
 
 
@@ -423,12 +423,12 @@ def test_self_partial_then_resume_shared_rows(bf16):
     fin = torch.empty(P, dtype=torch.int32, device="cuda")
     lib = ops.load()
     ops._check("kalm_pair_layout", lib.kalm_pair_layout(ops._ptr(lq_d), n_q, D, ops._ptr(cu_q), ops._ptr(dop),
-                                                         ops._ptr(fin), None, rows, None))
+                                                         ops._ptr(fin), None, rows, None, None))
     cu_s = torch.empty(n_q + 1, dtype=torch.int32, device="cuda")
     dop1 = torch.empty(n_q, dtype=torch.int32, device="cuda")
     fin1 = torch.empty(n_q, dtype=torch.int32, device="cuda")
     ops._check("kalm_pair_layout", lib.kalm_pair_layout(ops._ptr(lq_d), n_q, 1, ops._ptr(cu_s), ops._ptr(dop1),
-                                                         ops._ptr(fin1), None, U, None))
+                                                         ops._ptr(fin1), None, U, None, None))
     dt = torch.bfloat16 if bf16 else torch.float32
     Qd, Kd, Vd = to_dev(Qu, dt), to_dev(Ku, dt), to_dev(Vu, dt)
     sO, sL = ops.kalm_self_attn_partial(Qd, Kd, Vd, cu_s, int(lq.max()), nq, nkv, d)
@@ -440,6 +440,52 @@ def test_self_partial_then_resume_shared_rows(bf16):
     dop_np = (np.arange(P) % D).astype(np.int32)
     rO, _ = _attn_ref(Qu[idx], Ku[idx], Vu[idx], Kc, Vc, cm, dop_np, cu_np, nq, nkv, d)
     assert_close(to_np(O), rO, *(BF16_TOL if bf16 else F32_TOL), "O self partial + resume")
+
+
+@pytest.mark.parametrize("bf16,reuse", [(True, True), (True, False), (False, True), (False, False)])
+def test_shared_final_row_mode(bf16, reuse):
+    """row_mode 3: each pair's final position only, its Q (and self partial)
+    the query's last row in the per-query packing, O row p -- in one merged
+    pass, or resumed from the query's self partial."""
+    _announce(f"shared final-row mode bf16={bf16} reuse={reuse}")
+    d = 256 if bf16 else 32
+    nq, nkv, D, Cmax = 4, 1, 6, 70
+    lq = np.array([5, 37, 64, 1, 100], np.int64)
+    docs_c = [0, 3, 32, 33, 64, 70]
+    U = int(lq.sum())
+    Qu = synth.normal(41, (U, nq * d), 0.7, bf16)
+    Ku = synth.normal(42, (U, nkv * d), 0.7, bf16)
+    Vu = synth.normal(43, (U, nkv * d), 1.0, bf16)
+    Kc = synth.normal(44, (D * Cmax, nkv * d), 0.7, bf16)
+    Vc = synth.normal(45, (D * Cmax, nkv * d), 1.0, bf16)
+    cm = (np.arange(Cmax)[None] < np.asarray(docs_c)[:, None]).astype(np.uint8)
+    Kc.reshape(D, Cmax, -1)[cm == 0] = np.nan
+    Vc.reshape(D, Cmax, -1)[cm == 0] = np.nan
+    n_q = len(lq)
+    P = n_q * D
+    lay = ops.kalm_pair_layout(to_dev(lq.astype(np.int32), torch.int32), D, rows=int(D * U))
+    lay1 = ops.kalm_pair_layout(to_dev(lq.astype(np.int32), torch.int32), 1, with_h0_row=False)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    Qd, Kd, Vd = to_dev(Qu, dt), to_dev(Ku, dt), to_dev(Vu, dt)
+    args = (to_dev(Kc, dt), to_dev(Vc, dt), to_dev(cm, torch.uint8), lay["doc_of_pair"], nq, nkv, d,
+            ops.ROWS_SHARED_FINAL, P)
+    lse = torch.full((P, nq), -7.0, dtype=torch.float32, device="cuda")
+    if reuse:
+        sO, sL = ops.kalm_self_attn_partial(Qd, Kd, Vd, lay1["cu_q"], int(lq.max()), nq, nkv, d)
+        O = ops.kalm_merged_attn_resume(Qd, sO, sL, lay["cu_q"], int(lq.max()), *args, lse=lse)
+    else:
+        O = ops.kalm_merged_attn_rows(Qd, Kd, Vd, lay["cu_q"], int(lq.max()), *args, lse=lse)
+    torch.cuda.synchronize()
+    # oracle: every pair's merged attention over its expanded rows, read at its final row
+    starts = np.concatenate([[0], np.cumsum(lq)])
+    idx = np.concatenate([np.arange(starts[q], starts[q + 1]) for q in range(n_q) for _ in range(D)])
+    cu_np = np.concatenate([[0], np.cumsum(np.repeat(lq, D))]).astype(np.int32)
+    dop_np = (np.arange(P) % D).astype(np.int32)
+    rO, rL = _attn_ref(Qu[idx], Ku[idx], Vu[idx], Kc, Vc, cm, dop_np, cu_np, nq, nkv, d)
+    fin = cu_np[1:] - 1
+    tol = BF16_TOL if bf16 else F32_TOL
+    assert_close(to_np(O), rO[fin], *tol, "O shared final rows")
+    assert_close(to_np(lse), rL[fin], *tol, "lse shared final rows")
 
 
 def test_merged_attn_resume_bad_doc_gives_nan_rows():

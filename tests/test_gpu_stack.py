@@ -104,6 +104,25 @@ def test_stack_pruned_path_equals_full_path(reuse_self):
     assert_close(pruned[np.asarray(pairs)], ref["score"], SCORE_ATOL, 0.0, "pruned score vs oracle")
 
 
+@pytest.mark.parametrize("reuse_self", [True, False])
+def test_stack_single_layer_pruned_equals_full(reuse_self):
+    # one layer is both the first and the last: the pruned path computes the
+    # queries' own rows and each pair's final row only; the scores agree with
+    # the path that computes every row, and with the oracle
+    idx = 1
+    sh = synth.SHAPES[idx]
+    print(f"[case] stack {sh.name} single layer, pruned (reuse_self={reuse_self}) vs full", flush=True)
+    inp = synth.make_inputs(idx, nan_padding=True)
+    b = stack.upload(inp)
+    full = to_np(stack.step(b, prune=False)[3])
+    pruned = to_np(stack.step(b, prune=True, reuse_self=reuse_self)[3])
+    torch.cuda.synchronize()
+    assert_close(pruned, full, 1e-3, 0.0, "pruned vs full score")
+    pairs = _sample_pairs(inp, 8)
+    ref = oracle.stack_scores(inp, pairs=pairs, mode="mirror")
+    assert_close(pruned[np.asarray(pairs)], ref["score"], SCORE_ATOL, 0.0, "pruned score vs oracle")
+
+
 @pytest.mark.parametrize("chunk", [1, 2, 8, 16])
 def test_stack_matryoshka_chunk_sizes(chunk):
     # the pooling granularity is a parameter of the path: every chunk size
