@@ -83,6 +83,9 @@ def parse():
                     help="compute every row of the first and last layers (no shared / final-row shortcut)")
     ap.add_argument("--no-reuse-self", action="store_true",
                     help="first layer in one merged pass per pair instead of each query's self part once")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured as a HIP graph (per-kernel times from the eager "
+                         "warm-up steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     ap.add_argument("--no-pool-long", action="store_true", help="skip the pooling measurement at the 1024x2560 shape")
@@ -303,6 +306,22 @@ def main():
     ms_step = el / a.steps * 1e3
     pairs_s = sh.pairs / (el / a.steps)
     print(f"[bench] {a.steps} steps: {ms_step:.2f} ms/step, {pairs_s:.1f} pairs/s", file=sys.stderr, flush=True)
+    eager_ms = ms_step
+    if a.graph:
+        # the same step captured once as a HIP graph; the timed steps are replays
+        g = stack.StepGraph(b, prune=not a.no_prune, reuse_self=not a.no_reuse_self)
+        for _ in range(a.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(a.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        ms_step = el / a.steps * 1e3
+        pairs_s = sh.pairs / (el / a.steps)
+        print(f"[bench] {a.steps} graph replays: {ms_step:.3f} ms/step, {pairs_s:.1f} pairs/s", file=sys.stderr,
+              flush=True)
 
     dur = rec.durations_ms()
     work = work_model(inp, sh, single=not a.no_prune and sh.n_layers == 1)
@@ -345,6 +364,7 @@ def main():
                    "decoder_len": list(sh.lq), "passage_len": list(sh.doc_len), "chunk": sh.chunk,
                    "decoder_rows": b.rows, "pruned_first_last_layer": not a.no_prune,
                    "first_layer_self_once_per_query": not a.no_prune and not a.no_reuse_self,
+                   "hip_graph": a.graph, "eager_ms_per_step": eager_ms,
                    "parallelism": "single GPU"},
         "roofline": roof,
         "merged_attn": attn_summary(kernels, work, sh),

@@ -265,3 +265,29 @@ def step(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_sel
     front(b, stream, rec)
     decoder(b, stream, rec, prune, reuse_self)
     return score(b, stream, rec, prune)
+
+
+class StepGraph:
+    """One step captured as a HIP graph (torch.cuda.CUDAGraph records the
+    libkalm launches of ``step`` on its capture stream), so that a replay
+    enqueues the whole hot path with one call: for the small workloads, whose
+    kernels run for microseconds, the host-side launch cost otherwise sets the
+    step time.  Every buffer the step writes is allocated by ``upload``
+    beforehand and no libkalm call allocates, clears memory with a memset or
+    synchronises, so the captured step is the eager step.  ``replay`` returns
+    the (yes, no, margin, score) tensors the captured step wrote."""
+
+    def __init__(self, b: DeviceBatch, prune: bool = True, reuse_self: bool = True):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # one eager step off the default stream before capture
+            step(b, prune=prune, reuse_self=reuse_self)
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.out = step(b, prune=prune, reuse_self=reuse_self)
+
+    def replay(self):
+        self.graph.replay()
+        return self.out
+

@@ -123,6 +123,27 @@ def test_stack_single_layer_pruned_equals_full(reuse_self):
     assert_close(pruned[np.asarray(pairs)], ref["score"], SCORE_ATOL, 0.0, "pruned score vs oracle")
 
 
+@pytest.mark.parametrize("idx,n_layers", [(1, None), (2, 3)])
+def test_step_graph_replays_equal_eager(idx, n_layers):
+    # the step captured as a HIP graph: every replay, with eager work and
+    # synchronisations between replays, gives the eager step's scores exactly
+    sh = synth.SHAPES[idx]
+    print(f"[case] step graph {sh.name} layers={n_layers}", flush=True)
+    inp = synth.make_inputs(idx, nan_padding=True, n_layers=n_layers)
+    b = stack.upload(inp)
+    eager = [to_np(t).copy() for t in stack.step(b)]
+    torch.cuda.synchronize()
+    g = stack.StepGraph(b)
+    for i in range(3):
+        out = [to_np(t) for t in g.replay()]
+        torch.cuda.synchronize()
+        for k, (x, y) in enumerate(zip(out, eager)):
+            assert np.array_equal(x, y, equal_nan=True), f"replay {i} output {k}"
+        again = to_np(stack.step(b)[3])  # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(again, eager[3], equal_nan=True)
+
+
 @pytest.mark.parametrize("chunk", [1, 2, 8, 16])
 def test_stack_matryoshka_chunk_sizes(chunk):
     # the pooling granularity is a parameter of the path: every chunk size
