@@ -83,6 +83,8 @@ def parse():
                     help="compute every row of the first and last layers (no shared / final-row shortcut)")
     ap.add_argument("--no-reuse-self", action="store_true",
                     help="first layer in one merged pass per pair instead of each query's self part once")
+    ap.add_argument("--split-kv", action="store_true",
+                    help="one-layer stacks: each pair's cross keys in shares over several workgroups")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step captured as a HIP graph (per-kernel times from the eager "
                          "warm-up steps)")
@@ -158,6 +160,10 @@ def work_model(inp, sh, single=False):
                                                          + P * qd * e)),
             "merged_attn_first": dict(flops=float(last_flops),
                                       bytes=float(nQ * qd * e + 2 * U * kv * e + cross_bytes + P * qd * e)),
+            # split-KV: the shares' fp32 partials are written and read back by the merge
+            "merged_attn_first_split": dict(flops=float(4 * nq * d * nQ * int(C.sum())),
+                                            bytes=float(nQ * qd * e + nQ * (qd + nq) * 4 + cross_bytes
+                                                        + P * qd * e)),
             "o_linear_last": linear(P, qd, H, P * H * 8),
             "cross_kv": dict(flops=2.0 * int(C.sum()) * H * 2 * kv, bytes=float(D * Cmax * (H + 2 * kv) * e)),
             "chunk_pool": dict(flops=0.0, bytes=float(int(dl.sum()) * H * e + D * Cmax * H * e + D * T + D * Cmax
@@ -295,12 +301,12 @@ def main():
     rec = EventRec(torch)
     rec.on = False
     for _ in range(a.warmup):
-        stack.step(b, rec=rec, prune=not a.no_prune, reuse_self=not a.no_reuse_self)
+        stack.step(b, rec=rec, prune=not a.no_prune, reuse_self=not a.no_reuse_self, split_kv=a.split_kv)
     torch.cuda.synchronize()
     rec.on = True
     t0 = time.perf_counter()
     for i in range(a.steps):
-        stack.step(b, rec=rec, prune=not a.no_prune, reuse_self=not a.no_reuse_self)
+        stack.step(b, rec=rec, prune=not a.no_prune, reuse_self=not a.no_reuse_self, split_kv=a.split_kv)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_step = el / a.steps * 1e3
@@ -309,7 +315,7 @@ def main():
     eager_ms = ms_step
     if a.graph:
         # the same step captured once as a HIP graph; the timed steps are replays
-        g = stack.StepGraph(b, prune=not a.no_prune, reuse_self=not a.no_reuse_self)
+        g = stack.StepGraph(b, prune=not a.no_prune, reuse_self=not a.no_reuse_self, split_kv=a.split_kv)
         for _ in range(a.warmup):
             g.replay()
         torch.cuda.synchronize()

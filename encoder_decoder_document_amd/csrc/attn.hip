@@ -82,6 +82,45 @@ __global__ __launch_bounds__(256) void merged_attn_f32_kernel(
   if (lse && lane == 0) lse[(pr.o0 + i) * nq + h] = bad_doc ? __builtin_nanf("") : m + logf(l);
 }
 
+// Log-sum-exp merge of split-KV shares: the self partial (oi, lsei at the Q
+// row) and n_split partials over disjoint shares of the cross keys (slices of
+// ws_o / ws_l at the O row) combine into the softmax over all of them:
+//   M = max lse_i,  w_i = e^(lse_i - M),  O = sum w_i o_i / sum w_i,
+//   lse = M + log sum w_i.
+// One block per (pair, query head); wave w takes rows w, w + 4, ...; each
+// lane four of the 256 dims.
+__global__ __launch_bounds__(256) void split_merge_kernel(
+    const int32_t* __restrict__ cu_q, int D, int mode, int64_t q_rows, int64_t o_rows,
+    const float* __restrict__ oi, int64_t oi_ld, const float* __restrict__ lsei, const float* __restrict__ ws_o,
+    const float* __restrict__ ws_l, int S, int nq, bf16_t* __restrict__ O, int64_t o_ld,
+    float* __restrict__ lse) {
+  const int p = blockIdx.x, h = blockIdx.y;
+  const PairRows pr = pair_rows(cu_q, p, D, mode, q_rows, INT64_MAX, o_rows);
+  if (!pr.ok) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t dim0 = (int64_t)h * HD + 4 * lane;
+  for (int i = wave; i < pr.nrow; i += 4) {
+    const int64_t qrow = pr.q0 + i, orow = pr.o0 + i;
+    const float ls = lsei[qrow * nq + h];
+    float M = ls;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ws_l[((int64_t)s * o_rows + orow) * nq + h]);
+    float w = expf(ls - M), sum = w;
+    const f32x4_t os = *(const f32x4_t*)(oi + qrow * oi_ld + dim0);
+    f32x4_t acc = os * w;
+    for (int s = 0; s < S; ++s) {
+      const float wl = expf(ws_l[((int64_t)s * o_rows + orow) * nq + h] - M);  // e^-inf = 0: empty share
+      sum += wl;
+      if (wl != 0.f) acc += *(const f32x4_t*)(ws_o + ((int64_t)s * o_rows + orow) * nq * HD + dim0) * wl;
+    }
+    const float inv = 1.f / sum;
+    u32x2_t o;
+    o[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    o[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *(u32x2_t*)(O + orow * o_ld + dim0) = o;
+    if (lse && lane == 0) lse[orow * nq + h] = M + logf(sum);
+  }
+}
+
 }  // namespace
 
 namespace kalm {
@@ -93,7 +132,22 @@ void launch_merged_attn_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, co
                              int nq, int nkv, float scale, void* O, int64_t o_ld, float* lse, int part,
                              const float* oi, int64_t oi_ld, const float* lsei, hipStream_t s) {
   launch_bf16<ATTN_WAVES, 1>(Q, q_ld, Ks, Vs, kv_ld, cu_q, P, q_rows, kv_rows, o_rows, mode, max_lq, Kc, Vc, c_ld,
-                             cmask, doc_of_pair, D, Cmax, nq, nkv, scale, O, o_ld, lse, part, oi, oi_ld, lsei, s);
+                             cmask, doc_of_pair, D, Cmax, nq, nkv, scale, O, o_ld, lse, part, oi, oi_ld, lsei, 1, s);
+}
+
+void launch_merged_attn_split(const bf16_t* Q, int64_t q_ld, const int32_t* cu_q, int P, int64_t q_rows,
+                              int64_t o_rows, int mode, int max_lq, const bf16_t* Kc, const bf16_t* Vc, int64_t c_ld,
+                              const uint8_t* cmask, const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv,
+                              float scale, const float* oi, int64_t oi_ld, const float* lsei, int n_split,
+                              float* ws, bf16_t* O, int64_t o_ld, float* lse, hipStream_t s) {
+  float* ws_o = ws;
+  float* ws_l = ws + (int64_t)n_split * o_rows * nq * HD;
+  launch_bf16<ATTN_WAVES, 1>(Q, q_ld, nullptr, nullptr, 0, cu_q, P, q_rows, INT64_MAX, o_rows, mode, max_lq, Kc, Vc,
+                             c_ld, cmask, doc_of_pair, D, Cmax, nq, nkv, scale, ws_o, (int64_t)nq * HD, ws_l, 3,
+                             nullptr, 0, nullptr, n_split, s);
+  if (P == 0) return;
+  hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)P, (unsigned)nq), dim3(256), 0, s, cu_q, D, mode, q_rows,
+                     o_rows, oi, oi_ld, lsei, ws_o, ws_l, n_split, nq, O, o_ld, lse);
 }
 
 void launch_merged_attn_f32(const float* Q, int64_t q_ld, const float* Ks, const float* Vs,

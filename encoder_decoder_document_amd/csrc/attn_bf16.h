@@ -139,7 +139,12 @@ __device__ __forceinline__ PairRows pair_rows(const int32_t* __restrict__ cu_q, 
 //      O and its lse -- a self partial;
 //   2  the cross keys only, starting from a self partial (oi, lsei) read at
 //      the Q row: the online state begins at m = lse, l = 1, acc = o, which is
-//      the state the walk over the self keys would have left; bf16 output.
+//      the state the walk over the self keys would have left; bf16 output;
+//   3  one share of the cross keys (split-KV): block row y of the grid walks
+//      cross tiles [y T, y T + T), T = ceil(tiles / gridDim.y), from an empty
+//      state and writes an fp32 partial (o, lse) to slice y of Ov / lse (slice
+//      stride o_rows rows); a share with no visible key writes o = 0,
+//      lse = -inf.  The shares are combined by the log-sum-exp merge.
 template <int NH, int NW, int RT, int MODE, int PART>
 __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_kernel(
     const bf16_t* __restrict__ Q, int64_t q_ld, const bf16_t* __restrict__ Ks,
@@ -220,6 +225,13 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
     const int t = nz0 ? __builtin_ctzll(nz0) : 64 + __builtin_ctzll(nz1);
     donor = t * BKV + __builtin_ctz(cm_word(t));
   }
+  // this block's share of the cross tiles (split-KV); all of them otherwise
+  int ct0 = 0;
+  if constexpr (PART == 3) {
+    const int tps = (n_ct_all + (int)gridDim.y - 1) / (int)gridDim.y;
+    ct0 = (int)blockIdx.y * tps;
+    n_ct = max(0, min(n_ct, ct0 + tps) - ct0);
+  }
 
   const int h = kvh * G + hg * NH + wave / WPH;
   const int qr0 = qb * RB + (wave % WPH) * 32 * RT;  // first handled query row of this wave
@@ -275,7 +287,7 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   }
 
   const int n_self = min(Lq, pos0 + min(nrow, qb * RB + RB));  // causal keys the block needs
-  const int n_st = PART == 2 ? 0 : (n_self + BKV - 1) / BKV;
+  const int n_st = (PART == 2 || PART == 3) ? 0 : (n_self + BKV - 1) / BKV;
   const int n_tiles = n_st + n_ct;
   // byte addresses of key 0 of this pair (self) / chunk 0 of this passage (cross), head kvh
   const uint64_t ks_base = (uint64_t)(uintptr_t)(Ks + pr.kv0 * kv_ld + (int64_t)kvh * HD);
@@ -300,10 +312,10 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   // multiplies a finite value.
   auto issue = [&](int v, bool is_k) {
     const bool self = v < n_st;
-    const int kb = self ? v * BKV : (v - n_st) * BKV;
+    const int kb = self ? v * BKV : (v - n_st + ct0) * BKV;
     const uint32_t ld2 = self ? kv_ld2 : c_ld2;
     const uint64_t base = is_k ? (self ? ks_base : kc_base) : (self ? vs_base : vc_base);
-    const uint32_t bits = self ? 0u : cm_word(v - n_st);
+    const uint32_t bits = self ? 0u : cm_word(v - n_st + ct0);
     const uint32_t so = (is_k ? klds0 + (uint32_t)((v % KR) * TILE_B) : vlds0 + (uint32_t)((v % VR) * TILE_B)) + dslab;
     int key0 = dkey0;
     asm volatile("" : "+v"(key0));  // recompute the per-row offsets here instead of holding them
@@ -371,10 +383,13 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
     if (v + VR - 1 < n_tiles) issue(v + VR - 1, false);
     if (v + KR - 1 < n_tiles) issue(v + KR - 1, true);
     const bool self = v < n_st;
-    const int kb = self ? v * BKV : (v - n_st) * BKV;
+    const int kb = self ? v * BKV : (v - n_st + ct0) * BKV;
     // nothing to do: no valid rows in this wave, or a causal tile entirely
-    // above its rows (the wave still joins every barrier and copy)
+    // above its rows (the wave still joins every barrier and copy); a share
+    // of the cross keys also skips tiles with no visible chunk, so that its
+    // first walked tile sets a finite running max
     if (qr0 >= nrow || (self && kb > wave_last)) continue;
+    if (PART == 3 && cm_word(v - n_st + ct0) == 0u) continue;
     uint32_t kt = kx + (uint32_t)((v % KR) * TILE_B), vt = vx + (uint32_t)((v % VR) * TILE_B);
     // opaque per tile: keeps the compiler from hoisting 24 precomputed
     // fragment addresses out of the loop (one XOR per read is cheaper than
@@ -408,7 +423,7 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
       __builtin_amdgcn_sched_barrier(0);
     }
     // masking only for the causal diagonal / ragged self tiles and partial cross tiles
-    const uint32_t bits = self ? 0u : cm_word(v - n_st);
+    const uint32_t bits = self ? 0u : cm_word(v - n_st + ct0);
     bf16x8_t pf[RT][2];
 #pragma unroll
     for (int u = 0; u < RT; ++u) {
@@ -488,17 +503,25 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   // ---- normalise and store.  The accumulator holds, per lane (r, g), dims
   // 32 db + 8 q + 4 g + (0..3) of row r; it is staged through LDS (now free)
   // so that the global stores write whole rows, 16 bytes per lane.
+  // split-KV: this block's slice of the partial outputs
+  if constexpr (PART == 3) {
+    Ov = (float*)Ov + (int64_t)blockIdx.y * o_rows * o_ld;
+    lse += (int64_t)blockIdx.y * o_rows * nq;
+  }
 #pragma unroll
   for (int u = 0; u < RT; ++u) {
     const float l_tot = l_run[u] + __shfl_xor(l_run[u], 32, 64);
-    const float inv = bad_doc ? __builtin_nanf("") : 1.f / l_tot;
+    // an empty share of the cross keys (PART 3 only: every other walk has a
+    // visible key) is the zero partial o = 0, lse = -inf
+    const float inv = bad_doc ? __builtin_nanf("") : (PART == 3 && l_tot == 0.f) ? 0.f : 1.f / l_tot;
     l_run[u] = inv;  // keep the reciprocal for the stores below
     const int jl = qr0 + 32 * u + r;
     if (lse && g == 0 && jl < nrow)
-      lse[(pr.o0 + jl) * nq + h] =
-          bad_doc ? __builtin_nanf("") : (m_run[u] + __builtin_log2f(l_tot)) * 0.69314718055994531f;
+      lse[(pr.o0 + jl) * nq + h] = bad_doc                        ? __builtin_nanf("")
+                                   : (PART == 3 && l_tot == 0.f) ? -INFINITY
+                                       : (m_run[u] + __builtin_log2f(l_tot)) * 0.69314718055994531f;
   }
-  if constexpr (PART == 1) {
+  if constexpr (PART == 1 || PART == 3) {
     // fp32 partial: 16-byte stores straight from the accumulator (lanes g = 0
     // and 1 together write 32 contiguous bytes of a row)
     float* Of = (float*)Ov;
@@ -573,7 +596,11 @@ bf16_kernel_t pick_bf16_kernel(int sel) {
     case 5: return merged_attn_bf16_kernel<NH, NW, RT, 0, 2>;
     case 6: return merged_attn_bf16_kernel<NH, NW, RT, 1, 2>;
     case 7: return merged_attn_bf16_kernel<NH, NW, RT, 2, 2>;
-    default: return merged_attn_bf16_kernel<NH, NW, RT, 3, 2>;
+    case 8: return merged_attn_bf16_kernel<NH, NW, RT, 3, 2>;
+    case 9: return merged_attn_bf16_kernel<NH, NW, RT, 0, 3>;
+    case 10: return merged_attn_bf16_kernel<NH, NW, RT, 1, 3>;
+    case 11: return merged_attn_bf16_kernel<NH, NW, RT, 2, 3>;
+    default: return merged_attn_bf16_kernel<NH, NW, RT, 3, 3>;
   }
 }
 
@@ -583,7 +610,8 @@ void launch_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, const bf16_t* 
                  const int32_t* cu_q, int P, int64_t q_rows, int64_t kv_rows, int64_t o_rows, int mode, int max_lq,
                  const bf16_t* Kc, const bf16_t* Vc, int64_t c_ld, const uint8_t* cmask,
                  const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv, float scale, void* O, int64_t o_ld,
-                 float* lse, int part, const float* oi, int64_t oi_ld, const float* lsei, hipStream_t s) {
+                 float* lse, int part, const float* oi, int64_t oi_ld, const float* lsei, int n_split,
+                 hipStream_t s) {
   const int G = nq / nkv;
   const int NH = G >= 4 ? 4 : G;  // heads per block (G is 1, 2 or a multiple of 4)
   const int RB = 32 * RT * (NW / NH);
@@ -591,7 +619,7 @@ void launch_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, const bf16_t* 
   const int nqb = (max_rows + RB - 1) / RB;
   const int64_t blocks = (int64_t)P * nkv * (G / NH) * nqb;
   const float sl2 = scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)blocks), block(NW * 64);
+  const dim3 grid((unsigned)blocks, part == 3 ? (unsigned)n_split : 1u), block(NW * 64);
   if (blocks == 0) return;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, s, Q, q_ld, Ks, Vs, kv_ld, cu_q, P, q_rows, kv_rows, o_rows, nqb, Kc, Vc,
@@ -599,7 +627,8 @@ void launch_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, const bf16_t* 
   };
   // one instantiation per (heads per block, row mode, part); a self partial
   // (part 1) runs on all rows of its sequences (mode 0) only
-  const int sel = part == 1 ? 0 : 1 + 4 * (part == 2) + mode;  // 0 | 1..4 merged | 5..8 resumed
+  // 0 self partial | 1..4 merged | 5..8 resumed | 9..12 split shares (by row mode)
+  const int sel = part == 1 ? 0 : 1 + 4 * (part >= 2) + 4 * (part == 3) + mode;
   if (NH == 4) go(pick_bf16_kernel<4, NW, RT>(sel));
   else if (NH == 2) go(pick_bf16_kernel<2, NW, RT>(sel));
   else go(pick_bf16_kernel<1, NW, RT>(sel));

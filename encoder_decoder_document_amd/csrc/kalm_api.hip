@@ -59,7 +59,7 @@ kalm_status kalm_device_check(void) { return kalm::check_device(); }
 
 kalm_status kalm_pair_layout(const int32_t* lq, int32_t n_queries, int32_t n_docs, int32_t* cu_q,
                              int32_t* doc_of_pair, int32_t* final_row, int32_t* h0_row, int64_t rows,
-                             int32_t* h0_final, void* stream) {
+                             int32_t* h0_final, int32_t* cu_u, void* stream) {
   kalm::g_err[0] = 0;
   KALM_REQUIRE(n_queries >= 0 && n_docs >= 0, KALM_ERR_INVALID_ARG, "kalm_pair_layout: negative sizes");
   KALM_REQUIRE((int64_t)n_queries * n_docs < (1LL << 31), KALM_ERR_UNSUPPORTED, "kalm_pair_layout: too many pairs");
@@ -67,7 +67,7 @@ kalm_status kalm_pair_layout(const int32_t* lq, int32_t n_queries, int32_t n_doc
                "kalm_pair_layout: null pointer");
   KALM_REQUIRE(rows >= 0 && rows < (1LL << 31), KALM_ERR_INVALID_ARG, "kalm_pair_layout: rows out of range");
   KALM_DEVICE_OR_RETURN();
-  kalm::launch_pair_layout(lq, n_queries, n_docs, cu_q, doc_of_pair, final_row, h0_row, rows, h0_final,
+  kalm::launch_pair_layout(lq, n_queries, n_docs, cu_q, doc_of_pair, final_row, h0_row, rows, h0_final, cu_u,
                            (hipStream_t)stream);
   return kalm::check_launch("kalm_pair_layout");
 }
@@ -148,9 +148,22 @@ static kalm_status merged_attn_impl(const char* fn, const void* Q, int64_t q_ld,
                                     int32_t nq, int32_t nkv, int32_t d, float scale, kalm_dtype dt, void* O,
                                     int64_t o_ld, int64_t o_rows, float* lse, int32_t row_mode, void* stream,
                                     int part = 0, const float* oi = nullptr, int64_t oi_ld = 0,
-                                    const float* lsei = nullptr) {
+                                    const float* lsei = nullptr, int32_t n_split = 1, void* ws = nullptr,
+                                    int64_t ws_bytes = 0) {
   kalm::g_err[0] = 0;
   KALM_REQUIRE(dt == KALM_F32 || dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)dt);
+  // part 3: the cross keys in n_split shares merged with a self partial (bf16 path)
+  const bool split = part == 3;
+  if (split) {
+    KALM_REQUIRE(dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "%s: split-KV is implemented for bf16 only", fn);
+    KALM_REQUIRE(n_split >= 1 && n_split <= 64, KALM_ERR_INVALID_ARG, "%s: n_split %d not in 1..64", fn, n_split);
+    KALM_REQUIRE(o_rows >= 0 && ws_bytes >= (int64_t)n_split * o_rows * nq * (d + 1) * 4, KALM_ERR_INVALID_ARG,
+                 "%s: workspace of %lld bytes is smaller than n_split * o_rows * nq * (d + 1) * 4", fn,
+                 (long long)ws_bytes);
+    KALM_REQUIRE(P == 0 || o_rows == 0 || (ws && ALIGNED16(ws)), KALM_ERR_INVALID_ARG,
+                 "%s: workspace missing or not 16-byte aligned", fn);
+    part = 2;  // the checks below are those of a resumed pass
+  }
   KALM_REQUIRE(row_mode >= 0 && row_mode <= 3, KALM_ERR_INVALID_ARG, "%s: row_mode %d not in 0..3", fn, row_mode);
   KALM_REQUIRE(P >= 0 && q_rows >= 0 && kv_rows >= 0 && o_rows >= 0 && max_lq >= 0 && D >= 0 && Cmax >= 0,
                KALM_ERR_INVALID_ARG, "%s: negative sizes", fn);
@@ -187,7 +200,12 @@ static kalm_status merged_attn_impl(const char* fn, const void* Q, int64_t q_ld,
   }
   KALM_DEVICE_OR_RETURN();
   if (P == 0 || o_rows == 0) return KALM_OK;
-  if (dt == KALM_BF16)
+  if (split)
+    kalm::launch_merged_attn_split((const bf16_t*)Q, q_ld, cu_q, P, q_rows, o_rows, row_mode, max_lq,
+                                   (const bf16_t*)Kc, (const bf16_t*)Vc, c_ld, chunk_mask, doc_of_pair, D, Cmax, nq,
+                                   nkv, scale, oi, oi_ld, lsei, n_split, (float*)ws, (bf16_t*)O, o_ld, lse,
+                                   (hipStream_t)stream);
+  else if (dt == KALM_BF16)
     kalm::launch_merged_attn_bf16((const bf16_t*)Q, q_ld, (const bf16_t*)Ks, (const bf16_t*)Vs, kv_ld, cu_q, P,
                                   q_rows, kv_rows, o_rows, row_mode, max_lq, (const bf16_t*)Kc, (const bf16_t*)Vc,
                                   c_ld, chunk_mask, doc_of_pair, D, Cmax, nq, nkv, scale, O, o_ld, lse, part, oi,
@@ -240,6 +258,19 @@ kalm_status kalm_merged_attn_resume(const void* Q, int64_t q_ld, int64_t q_rows,
   return merged_attn_impl("kalm_merged_attn_resume", Q, q_ld, q_rows, nullptr, nullptr, 0, INT64_MAX, cu_q, P,
                           max_lq, Kc, Vc, c_ld, chunk_mask, doc_of_pair, D, Cmax, nq, nkv, d, scale, dt, O, o_ld,
                           o_rows, lse, row_mode, stream, 2, o_self, s_ld, lse_self);
+}
+
+kalm_status kalm_merged_attn_split(const void* Q, int64_t q_ld, int64_t q_rows, const float* o_self, int64_t s_ld,
+                                   const float* lse_self, const int32_t* cu_q, int32_t P, int32_t max_lq,
+                                   const void* Kc, const void* Vc, int64_t c_ld, const uint8_t* chunk_mask,
+                                   const int32_t* doc_of_pair, int32_t D, int32_t Cmax, int32_t nq, int32_t nkv,
+                                   int32_t d, float scale, kalm_dtype dt, void* O, int64_t o_ld, int64_t o_rows,
+                                   float* lse, int32_t row_mode, int32_t n_split, void* workspace,
+                                   int64_t workspace_bytes, void* stream) {
+  return merged_attn_impl("kalm_merged_attn_split", Q, q_ld, q_rows, nullptr, nullptr, 0, INT64_MAX, cu_q, P,
+                          max_lq, Kc, Vc, c_ld, chunk_mask, doc_of_pair, D, Cmax, nq, nkv, d, scale, dt, O, o_ld,
+                          o_rows, lse, row_mode, stream, 3, o_self, s_ld, lse_self, n_split, workspace,
+                          workspace_bytes);
 }
 
 kalm_status kalm_yesno_score(const void* h, kalm_dtype h_dt, int64_t h_ld, int64_t rows, const int32_t* final_row,

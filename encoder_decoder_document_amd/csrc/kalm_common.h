@@ -119,7 +119,8 @@ namespace kalm {
 void launch_chunk_pool(const void* x, const uint8_t* mask, int D, int T, int H, int chunk, int Cmax,
                        kalm_dtype dt, void* pooled, uint8_t* cmask, int32_t* n_chunks, hipStream_t s);
 void launch_pair_layout(const int32_t* lq, int nQ, int nD, int32_t* cu_q, int32_t* doc_of_pair,
-                        int32_t* final_row, int32_t* h0_row, int64_t rows, int32_t* h0_final, hipStream_t s);
+                        int32_t* final_row, int32_t* h0_row, int64_t rows, int32_t* h0_final, int32_t* cu_u,
+                        hipStream_t s);
 void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, void* Y, bool y_f32,
                         bool accumulate, bf16_t* Y_bf16, const uint8_t* row_mask, hipStream_t s);
 void launch_linear_f32(const float* X, const float* W, int M, int K, int N, float* Y, bool accumulate,
@@ -130,6 +131,14 @@ void launch_merged_attn_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, co
                              int64_t c_ld, const uint8_t* cmask, const int32_t* doc_of_pair, int D, int Cmax,
                              int nq, int nkv, float scale, void* O, int64_t o_ld, float* lse, int part,
                              const float* oi, int64_t oi_ld, const float* lsei, hipStream_t s);
+// Split-KV over the cross keys: n_split shares (part 3) into the workspace ws
+// (fp32 partials: n_split * o_rows * nq * 256 outputs, then n_split * o_rows *
+// nq lse values), merged with the self partial (oi, lsei) into O and lse.
+void launch_merged_attn_split(const bf16_t* Q, int64_t q_ld, const int32_t* cu_q, int P, int64_t q_rows,
+                              int64_t o_rows, int mode, int max_lq, const bf16_t* Kc, const bf16_t* Vc, int64_t c_ld,
+                              const uint8_t* cmask, const int32_t* doc_of_pair, int D, int Cmax, int nq, int nkv,
+                              float scale, const float* oi, int64_t oi_ld, const float* lsei, int n_split,
+                              float* ws, bf16_t* O, int64_t o_ld, float* lse, hipStream_t s);
 void launch_merged_attn_f32(const float* Q, int64_t q_ld, const float* Ks, const float* Vs,
                             int64_t kv_ld, const int32_t* cu_q, int P, int64_t q_rows, int64_t kv_rows,
                             int64_t o_rows, int mode, int max_lq, const float* Kc, const float* Vc, int64_t c_ld,

@@ -17,7 +17,8 @@ __global__ __launch_bounds__(1024) void pair_layout_kernel(const int32_t* __rest
                                                            int nD, int32_t* __restrict__ cu_q,
                                                            int32_t* __restrict__ doc_of_pair,
                                                            int32_t* __restrict__ final_row,
-                                                           int32_t* __restrict__ h0_final) {
+                                                           int32_t* __restrict__ h0_final,
+                                                           int32_t* __restrict__ cu_u) {
   __shared__ int32_t scan[1024];
   __shared__ int32_t carry;
   if (threadIdx.x == 0) carry = 0;
@@ -35,6 +36,7 @@ __global__ __launch_bounds__(1024) void pair_layout_kernel(const int32_t* __rest
     }
     const int32_t start = carry + scan[threadIdx.x] - len;  // exclusive prefix of query rows
     if (q < nQ) {
+      if (cu_u) cu_u[q] = start;
       for (int dd = 0; dd < nD; ++dd) {
         const int64_t p = (int64_t)q * nD + dd;
         const int32_t r0 = nD * start + dd * len;
@@ -48,7 +50,10 @@ __global__ __launch_bounds__(1024) void pair_layout_kernel(const int32_t* __rest
     if (threadIdx.x == 1023) carry += scan[1023];
     __syncthreads();
   }
-  if (threadIdx.x == 0) cu_q[(int64_t)nQ * nD] = nD * carry;
+  if (threadIdx.x == 0) {
+    cu_q[(int64_t)nQ * nD] = nD * carry;
+    if (cu_u) cu_u[nQ] = carry;
+  }
 }
 
 // One block per pair: h0_row[cu_q[p] + r] = (first row of the pair's query) + r.
@@ -167,9 +172,10 @@ void launch_rank_topn(const float* score, int n_queries, int D, int top_n, int32
 
 
 void launch_pair_layout(const int32_t* lq, int nQ, int nD, int32_t* cu_q, int32_t* doc_of_pair,
-                        int32_t* final_row, int32_t* h0_row, int64_t rows, int32_t* h0_final, hipStream_t s) {
+                        int32_t* final_row, int32_t* h0_row, int64_t rows, int32_t* h0_final, int32_t* cu_u,
+                        hipStream_t s) {
   hipLaunchKernelGGL(pair_layout_kernel, dim3(1), dim3(1024), 0, s, lq, nQ, nD, cu_q, doc_of_pair, final_row,
-                     h0_final);
+                     h0_final, cu_u);
   if (h0_row && (int64_t)nQ * nD > 0)
     hipLaunchKernelGGL(h0_row_kernel, dim3((unsigned)((int64_t)nQ * nD)), dim3(256), 0, s, cu_q, nD, h0_row, rows);
 }

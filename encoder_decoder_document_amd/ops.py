@@ -31,7 +31,7 @@ _SIGS = {
     "kalm_version": (_i32, []),
     "kalm_last_error": (ctypes.c_char_p, []),
     "kalm_device_check": (_i32, []),
-    "kalm_pair_layout": (_i32, [_c_p, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _i64, _c_p, _c_p]),
+    "kalm_pair_layout": (_i32, [_c_p, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _i64, _c_p, _c_p, _c_p]),
     "kalm_chunk_pool": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p]),
     "kalm_cross_kv": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _c_p, _i32, _i32, _c_p, _c_p]),
     "kalm_merged_attn": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i32, _i64, _i32, _c_p, _c_p, _i64,
@@ -44,6 +44,9 @@ _SIGS = {
     "kalm_merged_attn_resume": (_i32, [_c_p, _i64, _i64, _c_p, _i64, _c_p, _c_p, _i32, _i32, _c_p, _c_p, _i64, _c_p,
                                        _c_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_p, _i64, _i64, _c_p, _i32,
                                        _c_p]),
+    "kalm_merged_attn_split": (_i32, [_c_p, _i64, _i64, _c_p, _i64, _c_p, _c_p, _i32, _i32, _c_p, _c_p, _i64, _c_p,
+                                      _c_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_p, _i64, _i64, _c_p, _i32,
+                                      _i32, _c_p, _i64, _c_p]),
     "kalm_yesno_score": (_i32, [_c_p, _i32, _i64, _i64, _c_p, _i32, _i32, _c_p, _i32, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "kalm_linear": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _i32, _c_p, _i32, _i32, _c_p, _c_p]),
     "kalm_gather_rows": (_i32, [_c_p, _c_p, _i64, _i32, _i64, _c_p, _c_p, _c_p]),
@@ -123,7 +126,7 @@ def device_check() -> int:
 
 def kalm_pair_layout(lq: torch.Tensor, n_docs: int, rows: Optional[int] = None, with_h0_row: bool = True,
                      stream=None):
-    """lq [Q] int32 (device) -> dict(cu_q, doc_of_pair, final_row, h0_row, h0_final)."""
+    """lq [Q] int32 (device) -> dict(cu_q, doc_of_pair, final_row, h0_row, h0_final, cu_u)."""
     _contig(lq)
     Qn = lq.numel()
     P = Qn * n_docs
@@ -137,9 +140,10 @@ def kalm_pair_layout(lq: torch.Tensor, n_docs: int, rows: Optional[int] = None, 
             raise ValueError("rows (= n_docs * sum(lq)) is needed for h0_row")
         h0 = torch.empty(rows, dtype=torch.int32, device=dev)
     h0f = torch.empty(P, dtype=torch.int32, device=dev)
+    cu_u = torch.empty(Qn + 1, dtype=torch.int32, device=dev)
     _check("kalm_pair_layout", load().kalm_pair_layout(_ptr(lq), Qn, n_docs, _ptr(cu_q), _ptr(doc), _ptr(fin),
-                                                      _ptr(h0), rows or 0, _ptr(h0f), _stream(stream)))
-    return dict(cu_q=cu_q, doc_of_pair=doc, final_row=fin, h0_row=h0, h0_final=h0f)
+                                                      _ptr(h0), rows or 0, _ptr(h0f), _ptr(cu_u), _stream(stream)))
+    return dict(cu_q=cu_q, doc_of_pair=doc, final_row=fin, h0_row=h0, h0_final=h0f, cu_u=cu_u)
 
 
 def kalm_chunk_pool(x: torch.Tensor, token_mask: torch.Tensor, chunk: int = 4, out=None, stream=None):
@@ -260,6 +264,41 @@ def kalm_merged_attn_resume(Q: torch.Tensor, o_self: torch.Tensor, lse_self: tor
         _ptr(Q), Q.stride(0), Q.shape[0], _ptr(o_self), o_self.stride(0), _ptr(lse_self), _ptr(cu_q), P, max_lq,
         _ptr(Kc), _ptr(Vc), Kc.stride(0), _ptr(chunk_mask), _ptr(doc_of_pair), D, Cmax, nq, nkv, d, float(scale),
         _dt(Q), _ptr(out), out.stride(0), o_rows, _ptr(lse), int(row_mode), _stream(stream)))
+    return out
+
+
+def split_workspace_bytes(n_split: int, o_rows: int, nq: int, d: int) -> int:
+    """Bytes of workspace kalm_merged_attn_split needs."""
+    return n_split * o_rows * nq * (d + 1) * 4
+
+
+def kalm_merged_attn_split(Q: torch.Tensor, o_self: torch.Tensor, lse_self: torch.Tensor, cu_q: torch.Tensor,
+                           max_lq: int, Kc: torch.Tensor, Vc: torch.Tensor, chunk_mask: torch.Tensor,
+                           doc_of_pair: torch.Tensor, nq: int, nkv: int, d: int, row_mode: int, o_rows: int,
+                           n_split: int, workspace: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
+    """kalm_merged_attn_resume with the cross keys in n_split shares (split-KV), merged by
+    log-sum-exp weights; ``workspace`` (uint8 or any dtype, >= split_workspace_bytes) is
+    allocated here when not given."""
+    for t in (Q, o_self, Kc, Vc):
+        if t.stride(-1) != 1:
+            raise ValueError("unit column stride required")
+    _contig(lse_self, workspace)
+    P = cu_q.numel() - 1
+    D, Cmax = chunk_mask.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(o_rows, nq * d, dtype=Q.dtype, device=Q.device)
+    need = split_workspace_bytes(n_split, o_rows, nq, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("kalm_merged_attn_split", load().kalm_merged_attn_split(
+        _ptr(Q), Q.stride(0), Q.shape[0], _ptr(o_self), o_self.stride(0), _ptr(lse_self), _ptr(cu_q), P, max_lq,
+        _ptr(Kc), _ptr(Vc), Kc.stride(0), _ptr(chunk_mask), _ptr(doc_of_pair), D, Cmax, nq, nkv, d, float(scale),
+        _dt(Q), _ptr(out), out.stride(0), o_rows, _ptr(lse), int(row_mode), int(n_split), _ptr(workspace), ws_bytes,
+        _stream(stream)))
     return out
 
 

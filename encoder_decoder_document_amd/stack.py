@@ -24,7 +24,9 @@ With ``prune`` (the default) two layers do less work for the same result:
     residual update only for the final rows (kalm_merged_attn_rows, final row);
     in a one-layer stack, where the first layer is also the last, only the
     queries' own rows and each pair's final row are computed at all (shared
-    final row; the residual starts from the query's final hidden state).
+    final row; the residual starts from the query's final hidden state); with
+    ``split_kv`` each pair's cross keys run in shares over several workgroups
+    (kalm_merged_attn_split).
 
 The decoder layer is the reading stated on the pages' behalf: the pages give
 only the layer counts ("KaLM-Reranker-V1-Nano -- MLX (Apple Silicon)", What
@@ -118,13 +120,16 @@ def upload(inputs: Dict[str, object], device="cuda", n_layers: Optional[int] = N
         hf=torch.empty(P, H, dtype=torch.float32, device=device),
         qf=torch.empty(P, sh.nq * sh.d, dtype=dt, device=device),
         of=torch.empty(P, sh.nq * sh.d, dtype=dt, device=device),
-        # per-query packing (the pair layout with one passage) and the queries' self partials
-        cu_s=torch.empty(sh.n_queries + 1, dtype=torch.int32, device=device),
-        doc_s=torch.empty(sh.n_queries, dtype=torch.int32, device=device),
-        fin_s=torch.empty(sh.n_queries, dtype=torch.int32, device=device),
+        # row offsets of the queries' own rows and the queries' self partials
+        cu_u=torch.empty(sh.n_queries + 1, dtype=torch.int32, device=device),
         o_self=torch.empty(U, sh.nq * sh.d, dtype=torch.float32, device=device),
         lse_self=torch.empty(U, sh.nq, dtype=torch.float32, device=device),
     )
+    # split-KV workspace for the final rows of a one-layer stack (bf16)
+    n_split = final_row_splits(P, sh.nq, sh.nkv, Cmax)
+    if dt == torch.bfloat16 and L == 1 and n_split > 1:
+        buf["split_ws"] = torch.empty(ops.split_workspace_bytes(n_split, P, sh.nq, sh.d), dtype=torch.uint8,
+                                      device=device)
     if dt == torch.bfloat16:
         buf["h0b"] = torch.empty(U, H, dtype=torch.bfloat16, device=device)
         buf["hfb"] = torch.empty(P, H, dtype=torch.bfloat16, device=device)
@@ -135,24 +140,37 @@ def upload(inputs: Dict[str, object], device="cuda", n_layers: Optional[int] = N
         h0=dev(inputs["h0"], torch.float32), Wqkv=Wqkv, Wkvc=Wkvc, Wo=Wo, w_yesno=dev(inputs["w_yesno"]), buf=buf)
 
 
+def final_row_splits(P: int, nq: int, nkv: int, Cmax: int, cus: int = 256) -> int:
+    """Shares of the cross keys for the final-row attention: enough workgroups
+    for two per compute unit, at most one share per 32-chunk tile.  One
+    workgroup takes a pair's final row for up to four query heads of one KV
+    head."""
+    groups = P * nkv * max(1, (nq // nkv) // 4)
+    tiles = -(-Cmax // 32)
+    return max(1, min(tiles, -(-2 * cus // max(1, groups)), 64))
+
+
 def _no_rec(_name):
     return contextlib.nullcontext()
 
 
-def front(b: DeviceBatch, stream=None, rec=_no_rec):
+def front(b: DeviceBatch, stream=None, rec=_no_rec, h0_rows: bool = True):
     """Rows a0-a2: pair layout, chunk pooling and the cross K/V of every layer.
     ``rec(name)`` is an optional context-manager factory wrapped around each call
-    (the benchmark records HIP events with it)."""
+    (the benchmark records HIP events with it).  ``h0_rows`` = False skips the
+    per-row residual-start index, which only a stack that computes every row
+    of some layer reads."""
     B = b.buf
     lay = dict(cu_q=B["cu_q"], doc_of_pair=B["doc_of_pair"], final_row=B["final_row"], h0_row=B["h0_row"],
-               h0_final=B["h0_final"])
+               h0_final=B["h0_final"], cu_u=B["cu_u"])
     _check = ops._check
     lib = ops.load()
     s = ops._stream(stream)
     with rec("pair_layout"):
         _check("kalm_pair_layout", lib.kalm_pair_layout(
             ops._ptr(b.lq), b.n_queries, b.D, ops._ptr(lay["cu_q"]), ops._ptr(lay["doc_of_pair"]),
-            ops._ptr(lay["final_row"]), ops._ptr(lay["h0_row"]), b.rows, ops._ptr(lay["h0_final"]), s))
+            ops._ptr(lay["final_row"]), ops._ptr(lay["h0_row"]) if h0_rows else None, b.rows,
+            ops._ptr(lay["h0_final"]), ops._ptr(lay["cu_u"]), s))
     with rec("chunk_pool"):
         ops.kalm_chunk_pool(b.x, b.token_mask, b.chunk, out=(B["pooled"], B["chunk_mask"], B["n_chunks"]),
                             stream=stream)
@@ -166,11 +184,16 @@ def pruned(b: DeviceBatch, prune: bool = True) -> bool:
     return prune and b.n_layers >= 1
 
 
-def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_self: bool = True):
+def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_self: bool = True,
+            split_kv: bool = False):
     """Row a5 around a3: residual start, then every merged-attention layer.
     With ``prune`` and ``reuse_self`` the first layer computes each query's
     self-attention once and finishes every pair from it with the pair's cross
-    keys (the merged softmax split at the self/cross boundary)."""
+    keys (the merged softmax split at the self/cross boundary); ``split_kv``
+    spreads those cross keys over several workgroups per pair in a one-layer
+    stack with few pairs (off by default: at the one-query Nano shape the
+    resumed pass is bound by per-workgroup start-up latency, not by its few
+    key tiles, and the extra merge launch costs more than the split saves)."""
     B = b.buf
     bf = b.dtype == torch.bfloat16
     qd, kv = b.nq * b.d, b.nkv * b.d
@@ -200,18 +223,24 @@ def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_
                                     else (ops.ROWS_SHARED, b.rows, B["o"]))
             if reuse_self:
                 # the query's causal self-attention once, then each pair from it with its passage's cross keys
-                with rec("pair_layout_queries"):
-                    ops._check("kalm_pair_layout", ops.load().kalm_pair_layout(
-                        ops._ptr(b.lq), b.n_queries, 1, ops._ptr(B["cu_s"]), ops._ptr(B["doc_s"]),
-                        ops._ptr(B["fin_s"]), None, 0, None, ops._stream(stream)))
                 with rec("self_attn_first"):
-                    ops.kalm_self_attn_partial(u[:, :qd], u[:, qd:qd + kv], u[:, qd + kv:], B["cu_s"], b.max_lq,
+                    ops.kalm_self_attn_partial(u[:, :qd], u[:, qd:qd + kv], u[:, qd + kv:], B["cu_u"], b.max_lq,
                                                b.nq, b.nkv, b.d, scale=scale, out=B["o_self"], lse=B["lse_self"],
                                                stream=stream)
-                with rec("merged_attn_first_resume"):
-                    ops.kalm_merged_attn_resume(u[:, :qd], B["o_self"], B["lse_self"], B["cu_q"], b.max_lq,
-                                                kvc[:, :kv], kvc[:, kv:], B["chunk_mask"], B["doc_of_pair"], b.nq,
-                                                b.nkv, b.d, rmode, o_rows, scale=scale, out=o_buf, stream=stream)
+                if single and split_kv and "split_ws" in B:
+                    # few pairs: each pair's cross keys in shares over more workgroups (split-KV)
+                    with rec("merged_attn_first_split"):
+                        ops.kalm_merged_attn_split(u[:, :qd], B["o_self"], B["lse_self"], B["cu_q"], b.max_lq,
+                                                   kvc[:, :kv], kvc[:, kv:], B["chunk_mask"], B["doc_of_pair"],
+                                                   b.nq, b.nkv, b.d, rmode, o_rows,
+                                                   final_row_splits(b.P, b.nq, b.nkv, b.Cmax),
+                                                   workspace=B["split_ws"], scale=scale, out=o_buf, stream=stream)
+                else:
+                    with rec("merged_attn_first_resume"):
+                        ops.kalm_merged_attn_resume(u[:, :qd], B["o_self"], B["lse_self"], B["cu_q"], b.max_lq,
+                                                    kvc[:, :kv], kvc[:, kv:], B["chunk_mask"], B["doc_of_pair"],
+                                                    b.nq, b.nkv, b.d, rmode, o_rows, scale=scale, out=o_buf,
+                                                    stream=stream)
             else:
                 with rec("merged_attn_first"):
                     ops.kalm_merged_attn_rows(u[:, :qd], u[:, qd:qd + kv], u[:, qd + kv:], B["cu_q"], b.max_lq,
@@ -260,10 +289,11 @@ def score(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True):
         return ops.kalm_yesno_score(b.buf["h"], b.buf["final_row"], b.w_yesno, stream=stream)
 
 
-def step(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_self: bool = True):
+def step(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_self: bool = True,
+         split_kv: bool = False):
     """One pass of the whole hot path over the batch; returns (yes, no, margin, score)."""
-    front(b, stream, rec)
-    decoder(b, stream, rec, prune, reuse_self)
+    front(b, stream, rec, h0_rows=not (prune and b.n_layers == 1))
+    decoder(b, stream, rec, prune, reuse_self, split_kv)
     return score(b, stream, rec, prune)
 
 
@@ -277,15 +307,15 @@ class StepGraph:
     synchronises, so the captured step is the eager step.  ``replay`` returns
     the (yes, no, margin, score) tensors the captured step wrote."""
 
-    def __init__(self, b: DeviceBatch, prune: bool = True, reuse_self: bool = True):
+    def __init__(self, b: DeviceBatch, prune: bool = True, reuse_self: bool = True, split_kv: bool = False):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):  # one eager step off the default stream before capture
-            step(b, prune=prune, reuse_self=reuse_self)
+            step(b, prune=prune, reuse_self=reuse_self, split_kv=split_kv)
         torch.cuda.current_stream().wait_stream(side)
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph):
-            self.out = step(b, prune=prune, reuse_self=reuse_self)
+            self.out = step(b, prune=prune, reuse_self=reuse_self, split_kv=split_kv)
 
     def replay(self):
         self.graph.replay()

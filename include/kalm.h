@@ -75,10 +75,13 @@ kalm_status kalm_device_check(void);
  *   rows      capacity of h0_row; must equal n_docs * sum(lq) when h0_row is given
  *   h0_final  [P] int32 out, nullable: that row for the pair's final position
  *             (the query's last row in the per-query packing)
+ *   cu_u      [n_queries+1] int32 out, nullable: row offsets of the per-query
+ *             packing itself (cu_u[0] = 0; the layout with n_docs = 1)
  */
 kalm_status kalm_pair_layout(const int32_t* lq, int32_t n_queries, int32_t n_docs,
                              int32_t* cu_q, int32_t* doc_of_pair, int32_t* final_row,
-                             int32_t* h0_row, int64_t rows, int32_t* h0_final, void* stream);
+                             int32_t* h0_row, int64_t rows, int32_t* h0_final, int32_t* cu_u,
+                             void* stream);
 
 /*
  * a1 -- chunk pooling ([Q80] Frozen inference contract: masked mean over
@@ -199,8 +202,8 @@ kalm_status kalm_merged_attn_rows(const void* Q, int64_t q_ld, int64_t q_rows, c
  * kalm_self_attn_partial -- plain causal self-attention of n_seq packed
  * sequences (the merged attention with no visible cross key):
  *   Q, Ks, Vs   as kalm_merged_attn, rows cu_s[i] .. cu_s[i+1]-1 of sequence i
- *   cu_s        [n_seq+1] int32 row offsets (kalm_pair_layout with n_docs = 1
- *               gives the per-query packing); max_len >= every length
+ *   cu_s        [n_seq+1] int32 row offsets (kalm_pair_layout's cu_u gives the
+ *               per-query packing); max_len >= every length
  *   O           [rows, *] float out, row stride o_ld (elements): the normalised
  *               self output of each row and head, fp32 for both dtypes
  *   lse         [rows, nq] float out, required: log-sum-exp of the scaled self
@@ -233,6 +236,32 @@ kalm_status kalm_merged_attn_resume(const void* Q, int64_t q_ld, int64_t q_rows,
                                     int32_t Cmax, int32_t nq, int32_t nkv, int32_t d, float scale,
                                     kalm_dtype dt, void* O, int64_t o_ld, int64_t o_rows, float* lse,
                                     int32_t row_mode, void* stream);
+
+/*
+ * kalm_merged_attn_split -- kalm_merged_attn_resume with the cross keys split
+ * into n_split shares that run as separate workgroups (split-KV, for batches
+ * whose pairs alone cannot fill the GPU, such as one query against 100
+ * passages at the final row): share s walks cross tiles of 32 chunks
+ * [s T, s T + T), T = ceil(ceil(Cmax / 32) / n_split), and writes an fp32
+ * partial (o, lse) to the workspace; a second kernel merges the self partial
+ * and the shares with log-sum-exp weights ([MLX] What this is: the one softmax
+ * over the concatenated KV, regrouped).  Same result as
+ * kalm_merged_attn_resume up to rounding.
+ *   workspace        device memory of at least n_split * o_rows * nq * (d + 1)
+ *                    * 4 bytes, 16-byte aligned, owned by the caller; its
+ *                    contents on entry do not matter and are overwritten
+ *   n_split          1..64
+ * BF16 only (KALM_ERR_UNSUPPORTED for F32).  Other arguments as
+ * kalm_merged_attn_resume.
+ */
+kalm_status kalm_merged_attn_split(const void* Q, int64_t q_ld, int64_t q_rows, const float* o_self,
+                                   int64_t s_ld, const float* lse_self, const int32_t* cu_q, int32_t P,
+                                   int32_t max_lq, const void* Kc, const void* Vc, int64_t c_ld,
+                                   const uint8_t* chunk_mask, const int32_t* doc_of_pair, int32_t D,
+                                   int32_t Cmax, int32_t nq, int32_t nkv, int32_t d, float scale,
+                                   kalm_dtype dt, void* O, int64_t o_ld, int64_t o_rows, float* lse,
+                                   int32_t row_mode, int32_t n_split, void* workspace,
+                                   int64_t workspace_bytes, void* stream);
 
 /*
  * a4 -- yes/no readout ([MLX] What this is: score = softmax([logit_yes,

@@ -256,9 +256,10 @@ def pair_layout(lq: Sequence[int], n_docs: int):
     score is read at the pair's last row ([MLX] What this is: final position).
 
     Returns dict(cu_q [P+1], doc_of_pair [P], query_of_pair [P],
-    final_row [P], h0_row [rows], h0_final [P]) as int32, where h0_row[r] is
-    the row of the query's first-layer hidden state that pair row r starts
-    from and h0_final[p] that row for the pair's final position.
+    final_row [P], h0_row [rows], h0_final [P], cu_u [Q+1]) as int32, where
+    h0_row[r] is the row of the query's first-layer hidden state that pair row
+    r starts from, h0_final[p] that row for the pair's final position, and
+    cu_u the row offsets of the queries' own rows (packed in order).
     """
     lq = [int(v) for v in lq]
     Qn = len(lq)
@@ -280,7 +281,7 @@ def pair_layout(lq: Sequence[int], n_docs: int):
         cu_q.append(cu_q[-1] + n)
     i32 = lambda v: np.asarray(v, dtype=np.int32)
     return dict(cu_q=i32(cu_q), doc_of_pair=i32(doc_of_pair), query_of_pair=i32(query_of_pair),
-                final_row=i32(final_row), h0_row=i32(h0_row), h0_final=i32(h0_final))
+                final_row=i32(final_row), h0_row=i32(h0_row), h0_final=i32(h0_final), cu_u=i32(q_start))
 
 
 # --------------------------------------------------------------------------

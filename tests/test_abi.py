@@ -96,6 +96,16 @@ def test_invalid_arguments_rejected_before_launch():
     st = lib.kalm_merged_attn_resume(1, 1024, 10, 1, 512, 1, 1, 1, 10, 1, 1, 512, 1, 1, 1, 8, 4, 1, 256, 0.1,
                                      ops.KALM_BF16, 1, 1024, 10, None, 0, None)
     assert st == ops.KALM_ERR_INVALID_ARG and b"leading dimension" in lib.kalm_last_error()
+    # split-KV: workspace too small; n_split out of range; fp32 not implemented
+    args = (1, 1024, 10, 1, 1024, 1, 1, 1, 10, 1, 1, 512, 1, 1, 1, 8, 4, 1, 256, 0.1, ops.KALM_BF16, 1, 1024, 10,
+            None, 0)
+    need = 2 * 10 * 4 * 257 * 4
+    st = lib.kalm_merged_attn_split(*args, 2, 16, need - 1, None)
+    assert st == ops.KALM_ERR_INVALID_ARG and b"workspace" in lib.kalm_last_error()
+    st = lib.kalm_merged_attn_split(*args, 65, 16, 1 << 30, None)
+    assert st == ops.KALM_ERR_INVALID_ARG and b"n_split" in lib.kalm_last_error()
+    st = lib.kalm_merged_attn_split(*args[:20], ops.KALM_F32, *args[21:], 2, 16, need, None)
+    assert st == ops.KALM_ERR_UNSUPPORTED
     # ranking: top_n larger than the passages; too many passages for one workgroup
     st = lib.kalm_rank_topn(None, 1, 10, 11, None, None, None)
     assert st == ops.KALM_ERR_INVALID_ARG and b"top_n" in lib.kalm_last_error()

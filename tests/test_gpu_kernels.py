@@ -35,7 +35,7 @@ def test_pair_layout_bit_exact(lq, D):
     got = ops.kalm_pair_layout(to_dev(lq, torch.int32), D, rows=rows)
     torch.cuda.synchronize()
     ref = oracle.pair_layout(lq, D)
-    for k in ("cu_q", "doc_of_pair", "final_row", "h0_row", "h0_final"):
+    for k in ("cu_q", "doc_of_pair", "final_row", "h0_row", "h0_final", "cu_u"):
         assert np.array_equal(got[k].cpu().numpy(), ref[k]), k
 
 
@@ -423,12 +423,12 @@ def test_self_partial_then_resume_shared_rows(bf16):
     fin = torch.empty(P, dtype=torch.int32, device="cuda")
     lib = ops.load()
     ops._check("kalm_pair_layout", lib.kalm_pair_layout(ops._ptr(lq_d), n_q, D, ops._ptr(cu_q), ops._ptr(dop),
-                                                         ops._ptr(fin), None, rows, None, None))
+                                                         ops._ptr(fin), None, rows, None, None, None))
     cu_s = torch.empty(n_q + 1, dtype=torch.int32, device="cuda")
     dop1 = torch.empty(n_q, dtype=torch.int32, device="cuda")
     fin1 = torch.empty(n_q, dtype=torch.int32, device="cuda")
     ops._check("kalm_pair_layout", lib.kalm_pair_layout(ops._ptr(lq_d), n_q, 1, ops._ptr(cu_s), ops._ptr(dop1),
-                                                         ops._ptr(fin1), None, U, None, None))
+                                                         ops._ptr(fin1), None, U, None, None, None))
     dt = torch.bfloat16 if bf16 else torch.float32
     Qd, Kd, Vd = to_dev(Qu, dt), to_dev(Ku, dt), to_dev(Vu, dt)
     sO, sL = ops.kalm_self_attn_partial(Qd, Kd, Vd, cu_s, int(lq.max()), nq, nkv, d)
@@ -486,6 +486,83 @@ def test_shared_final_row_mode(bf16, reuse):
     tol = BF16_TOL if bf16 else F32_TOL
     assert_close(to_np(O), rO[fin], *tol, "O shared final rows")
     assert_close(to_np(lse), rL[fin], *tol, "lse shared final rows")
+
+
+@pytest.mark.parametrize("name,lqs,docs_c,Cmax,nq,nkv,n_split,general", [
+    ("g4_ragged_s3", [1, 31, 32, 33, 100, 300], [0, 1, 31, 32, 33, 70], 70, 4, 1, 3, False),
+    ("g4_general_s4", [45, 129, 7], [0, 0, 0], 256, 4, 1, 4, True),
+    ("g2_gqa_s8", [64, 65, 3], [256, 100, 17], 256, 8, 4, 8, False),
+    ("g4_s1", [40, 97], [33, 64], 64, 4, 1, 1, False),
+    ("g4_more_splits_than_tiles", [20, 9], [5, 64], 64, 4, 1, 7, False),
+])
+def test_merged_attn_split_from_oracle_partial(name, lqs, docs_c, Cmax, nq, nkv, n_split, general):
+    """Cross keys in n_split shares (split-KV) merged with the oracle's self
+    partial by log-sum-exp weights: equals the oracle's merged attention."""
+    _announce(f"merged_attn_split {name}")
+    d = 256
+    case = _attn_case(zlib.crc32(name.encode()) % 1000 + 500, lqs, docs_c, Cmax, nq, nkv, d, True, 0.7, general)
+    Q, Ks, Vs, Kc, Vc, cm, dop, cu_q = case
+    rows = Q.shape[0]
+    sO, sL = _self_ref(Q, Ks, Vs, cu_q, nq, nkv, d)
+    bf, f = torch.bfloat16, torch.float32
+    lse = torch.empty(rows, nq, dtype=f, device="cuda")
+    ws = torch.full((ops.split_workspace_bytes(n_split, rows, nq, d) // 4,), float("nan"), dtype=f, device="cuda")
+    O = ops.kalm_merged_attn_split(to_dev(Q, bf), to_dev(sO, f), to_dev(sL, f), to_dev(cu_q, torch.int32), max(lqs),
+                                   to_dev(Kc, bf), to_dev(Vc, bf), to_dev(cm, torch.uint8), to_dev(dop, torch.int32),
+                                   nq, nkv, d, ops.ROWS_ALL, rows, n_split, workspace=ws, lse=lse)
+    torch.cuda.synchronize()
+    rO, rL = _attn_ref(*case, nq, nkv, d)
+    assert_close(to_np(O), rO, *BF16_TOL, f"O split ({name})")
+    assert_close(to_np(lse), rL, *BF16_TOL, f"lse split ({name})")
+
+
+@pytest.mark.parametrize("n_split", [1, 2, 8])
+def test_merged_attn_split_shared_final_rows(n_split):
+    """The one-query, many-passage case split-KV is for: final rows of the
+    shared layout, self partial from kalm_self_attn_partial."""
+    _announce(f"merged_attn_split shared final rows n_split={n_split}")
+    d, nq, nkv, D, Cmax = 256, 4, 1, 100, 256
+    lq = np.array([64], np.int64)
+    rng = np.random.default_rng(77)
+    docs_c = rng.integers(8, 257, D)
+    U = int(lq.sum())
+    Qu = synth.normal(51, (U, nq * d), 0.7, True)
+    Ku = synth.normal(52, (U, nkv * d), 0.7, True)
+    Vu = synth.normal(53, (U, nkv * d), 1.0, True)
+    Kc = synth.normal(54, (D * Cmax, nkv * d), 0.7, True)
+    Vc = synth.normal(55, (D * Cmax, nkv * d), 1.0, True)
+    cm = (np.arange(Cmax)[None] < np.asarray(docs_c)[:, None]).astype(np.uint8)
+    Kc.reshape(D, Cmax, -1)[cm == 0] = np.nan
+    Vc.reshape(D, Cmax, -1)[cm == 0] = np.nan
+    P = D
+    lay = ops.kalm_pair_layout(to_dev(lq.astype(np.int32), torch.int32), D, rows=int(D * U))
+    lay1 = ops.kalm_pair_layout(to_dev(lq.astype(np.int32), torch.int32), 1, with_h0_row=False)
+    bf = torch.bfloat16
+    Qd, Kd, Vd = to_dev(Qu, bf), to_dev(Ku, bf), to_dev(Vu, bf)
+    sO, sL = ops.kalm_self_attn_partial(Qd, Kd, Vd, lay1["cu_q"], int(lq.max()), nq, nkv, d)
+    O = ops.kalm_merged_attn_split(Qd, sO, sL, lay["cu_q"], int(lq.max()), to_dev(Kc, bf), to_dev(Vc, bf),
+                                   to_dev(cm, torch.uint8), lay["doc_of_pair"], nq, nkv, d, ops.ROWS_SHARED_FINAL, P,
+                                   n_split)
+    torch.cuda.synchronize()
+    idx = np.tile(np.arange(U), D)
+    cu_np = np.concatenate([[0], np.cumsum(np.repeat(lq, D))]).astype(np.int32)
+    dop_np = (np.arange(P) % D).astype(np.int32)
+    rO, _ = _attn_ref(Qu[idx], Ku[idx], Vu[idx], Kc, Vc, cm, dop_np, cu_np, nq, nkv, d)
+    assert_close(to_np(O), rO[cu_np[1:] - 1], *BF16_TOL, "O split shared final rows")
+
+
+def test_merged_attn_split_bad_doc_gives_nan_rows():
+    _announce("merged_attn_split out-of-range doc")
+    case = _attn_case(14, [20, 20], [5, 64], 64, 4, 1, 256, True)
+    Q, Ks, Vs, Kc, Vc, cm, dop, cu_q = case
+    sO, sL = _self_ref(Q, Ks, Vs, cu_q, 4, 1, 256)
+    dop = np.array([0, 7], np.int32)
+    bf, f = torch.bfloat16, torch.float32
+    O = ops.kalm_merged_attn_split(to_dev(Q, bf), to_dev(sO, f), to_dev(sL, f), to_dev(cu_q, torch.int32), 20,
+                                   to_dev(Kc, bf), to_dev(Vc, bf), to_dev(cm, torch.uint8), to_dev(dop, torch.int32),
+                                   4, 1, 256, ops.ROWS_ALL, 40, 2)
+    g = to_np(O)
+    assert np.isfinite(g[:20]).all() and np.isnan(g[20:]).all()
 
 
 def test_merged_attn_resume_bad_doc_gives_nan_rows():

@@ -45,7 +45,9 @@ def _run(inp):
 def _check(inp, b, got, pairs):
     sh = inp["shape"]
     lay = oracle.pair_layout(inp["lq"], sh.n_docs)
-    for k in ("cu_q", "doc_of_pair", "final_row", "h0_row"):
+    # a pruned one-layer step never reads the per-row index and leaves it unwritten
+    keys = ("cu_q", "doc_of_pair", "final_row", "h0_final", "cu_u") + (("h0_row",) if b.n_layers > 1 else ())
+    for k in keys:
         assert np.array_equal(b.buf[k].cpu().numpy(), lay[k]), k
     _, rcm, rnc = oracle.chunk_pool(np.zeros((sh.n_docs, sh.T, 1)), inp["token_mask"], sh.chunk)
     assert np.array_equal(b.buf["chunk_mask"].cpu().numpy(), rcm)
@@ -104,18 +106,20 @@ def test_stack_pruned_path_equals_full_path(reuse_self):
     assert_close(pruned[np.asarray(pairs)], ref["score"], SCORE_ATOL, 0.0, "pruned score vs oracle")
 
 
-@pytest.mark.parametrize("reuse_self", [True, False])
-def test_stack_single_layer_pruned_equals_full(reuse_self):
+@pytest.mark.parametrize("reuse_self,split_kv", [(True, False), (True, True), (False, False)])
+def test_stack_single_layer_pruned_equals_full(reuse_self, split_kv):
     # one layer is both the first and the last: the pruned path computes the
     # queries' own rows and each pair's final row only; the scores agree with
     # the path that computes every row, and with the oracle
     idx = 1
     sh = synth.SHAPES[idx]
-    print(f"[case] stack {sh.name} single layer, pruned (reuse_self={reuse_self}) vs full", flush=True)
+    print(f"[case] stack {sh.name} single layer, pruned (reuse_self={reuse_self}, split_kv={split_kv}) vs full",
+          flush=True)
     inp = synth.make_inputs(idx, nan_padding=True)
     b = stack.upload(inp)
+    assert "split_ws" in b.buf  # 100 pairs: the split-KV workspace exists
     full = to_np(stack.step(b, prune=False)[3])
-    pruned = to_np(stack.step(b, prune=True, reuse_self=reuse_self)[3])
+    pruned = to_np(stack.step(b, prune=True, reuse_self=reuse_self, split_kv=split_kv)[3])
     torch.cuda.synchronize()
     assert_close(pruned, full, 1e-3, 0.0, "pruned vs full score")
     pairs = _sample_pairs(inp, 8)

@@ -286,6 +286,7 @@ def test_pair_layout_closed_form():
     assert list(lay["final_row"]) == [2, 5, 6, 7, 11, 15]
     assert list(lay["h0_row"]) == [0, 1, 2, 0, 1, 2, 3, 3, 4, 5, 6, 7, 4, 5, 6, 7]
     assert list(lay["h0_final"]) == [2, 2, 3, 3, 7, 7]
+    assert list(lay["cu_u"]) == [0, 3, 4, 8]
     # the final position's query row is the query row of the pair's final row
     assert list(lay["h0_final"]) == [int(lay["h0_row"][f]) for f in lay["final_row"]]
 
