@@ -83,6 +83,8 @@ def parse():
                     help="compute every row of the first and last layers (no shared / final-row shortcut)")
     ap.add_argument("--no-reuse-self", action="store_true",
                     help="first layer in one merged pass per pair instead of each query's self part once")
+    ap.add_argument("--mlp-dim", type=int, default=None,
+                    help="model-shaped layers (RMSNorm, RoPE, gated-GELU MLP of this width) around the attention")
     ap.add_argument("--split-kv", action="store_true",
                     help="one-layer stacks: each pair's cross keys in shares over several workgroups")
     ap.add_argument("--graph", action="store_true",
@@ -119,6 +121,43 @@ class EventRec:
     def durations_ms(self):
         self.torch.cuda.synchronize()
         return {k: [s.elapsed_time(e) for s, e in v] for k, v in self.ev.items()}
+
+
+def model_work(inp, sh, work, single=False):
+    """Work per launch of the model-shaped layer's extra calls (RMSNorm, RoPE,
+    gated MLP in passes of at most MLP_ROWS rows, final norm)."""
+    from encoder_decoder_document_amd.stack import MLP_ROWS
+    I = int(inp["model"]["mlp_dim"])
+    H, nq, nkv, d = sh.H, sh.nq, sh.nkv, sh.d
+    e = 2 if sh.dtype == "bf16" else 4
+    lq = np.asarray(inp["lq"], dtype=np.int64)
+    U, P = int(lq.sum()), sh.pairs
+    rows = sh.n_docs * U
+
+    def norm(m):
+        return dict(flops=3.0 * m * H, bytes=float(m * H * (4 + e) + H * e))
+
+    def rope(m, heads):
+        return dict(flops=6.0 * m * heads * d, bytes=float(2 * m * heads * d * e))
+
+    def mlp(m, tag):
+        n_pass = -(-m // MLP_ROWS)
+        c = m / n_pass  # rows per pass (average)
+        work.update({
+            "mlp_norm" + tag: norm(c),
+            "mlp_gate_up" + tag: dict(flops=2.0 * c * H * 2 * I, bytes=float(c * H * e + 2 * I * H * e + c * 2 * I * e)),
+            "mlp_act" + tag: dict(flops=8.0 * c * I, bytes=float(c * 3 * I * e)),
+            "mlp_down" + tag: dict(flops=2.0 * c * I * H, bytes=float(c * I * e + H * I * e + c * H * 8)),
+        })
+
+    work.update({"attn_norm": norm(rows), "attn_norm_first": norm(U), "attn_norm_last": norm(P),
+                 "rope_q": rope(rows, nq), "rope_k": rope(rows, nkv), "rope_q_first": rope(U, nq),
+                 "rope_k_first": rope(U, nkv), "rope_q_last": rope(P, nq),
+                 "final_norm": dict(flops=3.0 * P * H, bytes=float(P * H * 8 + H * e))})
+    if not single:
+        mlp(rows, "")
+    mlp(P, "_last")
+    return work
 
 
 def work_model(inp, sh, single=False):
@@ -294,7 +333,7 @@ def main():
     if ops.device_check() != ops.KALM_OK:
         sys.exit(ops.load().kalm_last_error().decode())
     print(f"[bench] generating {sh.name}", file=sys.stderr, flush=True)
-    inp = synth.make_inputs(idx, nan_padding=False, shape=sh)
+    inp = synth.make_inputs(idx, nan_padding=False, shape=sh, mlp_dim=a.mlp_dim)
     b = stack.upload(inp)
     torch.cuda.synchronize()
     print(f"[bench] uploaded: rows={b.rows} pairs={b.P}; warmup {a.warmup}", file=sys.stderr, flush=True)
@@ -330,7 +369,10 @@ def main():
               flush=True)
 
     dur = rec.durations_ms()
-    work = work_model(inp, sh, single=not a.no_prune and sh.n_layers == 1)
+    single = not a.no_prune and sh.n_layers == 1
+    work = work_model(inp, sh, single=single)
+    if inp.get("model"):
+        model_work(inp, sh, work, single=single)
     kernels = {}
     for k, v in dur.items():
         n_per = len(v) / a.steps
@@ -371,6 +413,8 @@ def main():
                    "decoder_rows": b.rows, "pruned_first_last_layer": not a.no_prune,
                    "first_layer_self_once_per_query": not a.no_prune and not a.no_reuse_self,
                    "hip_graph": a.graph, "eager_ms_per_step": eager_ms,
+                   "layer": ("model-shaped (RMSNorm, RoPE, gated-GELU MLP %d)" % a.mlp_dim) if a.mlp_dim
+                   else "merged attention + projections",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "merged_attn": attn_summary(kernels, work, sh),

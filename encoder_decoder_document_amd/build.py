@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(os.path.dirname(PKG), "_build")
 LIB = os.path.join(PKG, "libkalm.so")
-SOURCES = ["kalm_api.hip", "pool.hip", "rows.hip", "gemm.hip", "attn.hip"]
+SOURCES = ["kalm_api.hip", "pool.hip", "rows.hip", "gemm.hip", "attn.hip", "layer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -273,6 +273,60 @@ kalm_status kalm_merged_attn_split(const void* Q, int64_t q_ld, int64_t q_rows, 
                           workspace_bytes);
 }
 
+kalm_status kalm_rms_norm(const void* x, kalm_dtype x_dt, int64_t x_ld, int64_t M, int32_t H, const void* w,
+                          kalm_dtype w_dt, float eps, void* y, kalm_dtype y_dt, int64_t y_ld, void* stream) {
+  kalm::g_err[0] = 0;
+  const bool dts_ok = (x_dt == KALM_F32 || x_dt == KALM_BF16) && (w_dt == KALM_F32 || w_dt == KALM_BF16) &&
+                      (y_dt == KALM_F32 || y_dt == KALM_BF16);
+  KALM_REQUIRE(dts_ok, KALM_ERR_UNSUPPORTED, "kalm_rms_norm: dtype");
+  KALM_REQUIRE(M >= 0 && H >= 4 && H % 4 == 0, KALM_ERR_INVALID_ARG, "kalm_rms_norm: H must be a positive multiple of 4");
+  KALM_REQUIRE(x_ld >= H && y_ld >= H && x_ld % 4 == 0 && y_ld % 4 == 0, KALM_ERR_INVALID_ARG,
+               "kalm_rms_norm: leading dimensions must be >= H and multiples of 4");
+  KALM_REQUIRE(eps >= 0.f, KALM_ERR_INVALID_ARG, "kalm_rms_norm: eps must be >= 0");
+  KALM_REQUIRE(M == 0 || (x && w && y), KALM_ERR_INVALID_ARG, "kalm_rms_norm: null pointer");
+  KALM_REQUIRE(ALIGNED16(x) && ALIGNED16(w) && ALIGNED16(y), KALM_ERR_INVALID_ARG,
+               "kalm_rms_norm: pointers must be 16-byte aligned");
+  KALM_DEVICE_OR_RETURN();
+  kalm::launch_rms_norm(x, x_dt == KALM_BF16, x_ld, M, H, w, w_dt == KALM_BF16, eps, y, y_dt == KALM_BF16, y_ld,
+                        (hipStream_t)stream);
+  return kalm::check_launch("kalm_rms_norm");
+}
+
+kalm_status kalm_rope(void* X, kalm_dtype dt, int64_t ld, int64_t rows, int32_t col0, int32_t n_heads, int32_t d,
+                      const int32_t* cu, int32_t n_seq, int32_t max_len, int32_t row_mode, float theta,
+                      void* stream) {
+  kalm::g_err[0] = 0;
+  KALM_REQUIRE(dt == KALM_F32 || dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "kalm_rope: dtype");
+  KALM_REQUIRE(row_mode == 0 || row_mode == 1, KALM_ERR_INVALID_ARG, "kalm_rope: row_mode %d not in 0..1", row_mode);
+  KALM_REQUIRE(rows >= 0 && n_seq >= 0 && n_heads >= 0 && max_len >= 0 && col0 >= 0, KALM_ERR_INVALID_ARG,
+               "kalm_rope: negative sizes");
+  KALM_REQUIRE(d >= 8 && d % 8 == 0 && col0 % 4 == 0 && ld % 4 == 0 && ld >= col0 + (int64_t)n_heads * d,
+               KALM_ERR_INVALID_ARG, "kalm_rope: d must be a multiple of 8, col0 and ld multiples of 4 covering the heads");
+  KALM_REQUIRE(theta > 1.f, KALM_ERR_INVALID_ARG, "kalm_rope: theta must be > 1");
+  KALM_REQUIRE((int64_t)max_len * n_heads * (d / 8) < (int64_t)65535 * 256, KALM_ERR_UNSUPPORTED,
+               "kalm_rope: too many rows per sequence");
+  KALM_REQUIRE(n_seq == 0 || (X && cu), KALM_ERR_INVALID_ARG, "kalm_rope: null pointer");
+  KALM_REQUIRE(ALIGNED16(X), KALM_ERR_INVALID_ARG, "kalm_rope: X must be 16-byte aligned");
+  KALM_DEVICE_OR_RETURN();
+  kalm::launch_rope(X, dt == KALM_BF16, ld, rows, col0, n_heads, d, cu, n_seq, max_len, row_mode, theta,
+                    (hipStream_t)stream);
+  return kalm::check_launch("kalm_rope");
+}
+
+kalm_status kalm_gated_gelu(const void* Y, kalm_dtype dt, int64_t y_ld, int64_t M, int32_t I, void* A, int64_t a_ld,
+                            void* stream) {
+  kalm::g_err[0] = 0;
+  KALM_REQUIRE(dt == KALM_F32 || dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "kalm_gated_gelu: dtype");
+  KALM_REQUIRE(M >= 0 && I >= 4 && I % 4 == 0, KALM_ERR_INVALID_ARG, "kalm_gated_gelu: I must be a positive multiple of 4");
+  KALM_REQUIRE(y_ld >= 2 * (int64_t)I && a_ld >= I && y_ld % 4 == 0 && a_ld % 4 == 0, KALM_ERR_INVALID_ARG,
+               "kalm_gated_gelu: leading dimensions must cover the columns and be multiples of 4");
+  KALM_REQUIRE(M == 0 || (Y && A), KALM_ERR_INVALID_ARG, "kalm_gated_gelu: null pointer");
+  KALM_REQUIRE(ALIGNED16(Y) && ALIGNED16(A), KALM_ERR_INVALID_ARG, "kalm_gated_gelu: pointers must be 16-byte aligned");
+  KALM_DEVICE_OR_RETURN();
+  kalm::launch_gated_gelu(Y, dt == KALM_BF16, y_ld, M, I, A, a_ld, (hipStream_t)stream);
+  return kalm::check_launch("kalm_gated_gelu");
+}
+
 kalm_status kalm_yesno_score(const void* h, kalm_dtype h_dt, int64_t h_ld, int64_t rows, const int32_t* final_row,
                              int32_t P, int32_t H, const void* w_yesno, kalm_dtype w_dt, float* yes, float* no,
                              float* margin, float* score, void* stream) {

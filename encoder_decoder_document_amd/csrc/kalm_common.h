@@ -150,6 +150,12 @@ void launch_yesno(const void* h, bool h_bf16, int64_t h_ld, int64_t rows, const 
                   hipStream_t s);
 void launch_rank_topn(const float* score, int n_queries, int D, int top_n, int32_t* out_index, float* out_score,
                       hipStream_t s);
+void launch_rms_norm(const void* x, bool x_bf16, int64_t x_ld, int64_t M, int H, const void* w, bool w_bf16, float eps,
+                     void* y, bool y_bf16, int64_t y_ld, hipStream_t s);
+void launch_rope(void* X, bool bf16, int64_t ld, int64_t rows, int col0, int nh, int d, const int32_t* cu, int n_seq,
+                 int max_len, int mode, float theta, hipStream_t s);
+void launch_gated_gelu(const void* Y, bool bf16, int64_t y_ld, int64_t M, int I, void* A, int64_t a_ld,
+                       hipStream_t s);
 void launch_gather_rows(const float* src, const int32_t* idx, int64_t M, int H, int64_t n_src,
                         float* dst, bf16_t* dst_bf16, hipStream_t s);
 }  // namespace kalm

@@ -47,6 +47,9 @@ _SIGS = {
     "kalm_merged_attn_split": (_i32, [_c_p, _i64, _i64, _c_p, _i64, _c_p, _c_p, _i32, _i32, _c_p, _c_p, _i64, _c_p,
                                       _c_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_p, _i64, _i64, _c_p, _i32,
                                       _i32, _c_p, _i64, _c_p]),
+    "kalm_rms_norm": (_i32, [_c_p, _i32, _i64, _i64, _i32, _c_p, _i32, _f32, _c_p, _i32, _i64, _c_p]),
+    "kalm_rope": (_i32, [_c_p, _i32, _i64, _i64, _i32, _i32, _i32, _c_p, _i32, _i32, _i32, _f32, _c_p]),
+    "kalm_gated_gelu": (_i32, [_c_p, _i32, _i64, _i64, _i32, _c_p, _i64, _c_p]),
     "kalm_yesno_score": (_i32, [_c_p, _i32, _i64, _i64, _c_p, _i32, _i32, _c_p, _i32, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "kalm_linear": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _i32, _c_p, _i32, _i32, _c_p, _c_p]),
     "kalm_gather_rows": (_i32, [_c_p, _c_p, _i64, _i32, _i64, _c_p, _c_p, _c_p]),
@@ -299,6 +302,44 @@ def kalm_merged_attn_split(Q: torch.Tensor, o_self: torch.Tensor, lse_self: torc
         _ptr(Kc), _ptr(Vc), Kc.stride(0), _ptr(chunk_mask), _ptr(doc_of_pair), D, Cmax, nq, nkv, d, float(scale),
         _dt(Q), _ptr(out), out.stride(0), o_rows, _ptr(lse), int(row_mode), int(n_split), _ptr(workspace), ws_bytes,
         _stream(stream)))
+    return out
+
+
+def kalm_rms_norm(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, out: Optional[torch.Tensor] = None,
+                  y_dtype: Optional[torch.dtype] = None, stream=None):
+    """y = x / sqrt(mean(x^2) + eps) * w row by row; x [M, H] (row stride >= H), w [H]."""
+    if x.stride(-1) != 1:
+        raise ValueError("unit column stride required")
+    _contig(w)
+    M, H = x.shape
+    if out is None:
+        out = torch.empty(M, H, dtype=y_dtype or x.dtype, device=x.device)
+    _check("kalm_rms_norm", load().kalm_rms_norm(_ptr(x), _dt(x), x.stride(0), M, H, _ptr(w), _dt(w), float(eps),
+                                                _ptr(out), _dt(out), out.stride(0), _stream(stream)))
+    return out
+
+
+def kalm_rope(X: torch.Tensor, col0: int, n_heads: int, d: int, cu: torch.Tensor, max_len: int, row_mode: int = 0,
+              theta: float = 10000.0, stream=None):
+    """Rotary embedding in place on heads [col0, col0 + n_heads*d) of X [rows, ld]."""
+    if X.stride(-1) != 1:
+        raise ValueError("unit column stride required")
+    _contig(cu)
+    _check("kalm_rope", load().kalm_rope(_ptr(X), _dt(X), X.stride(0), X.shape[0], col0, n_heads, d, _ptr(cu),
+                                        cu.numel() - 1, max_len, int(row_mode), float(theta), _stream(stream)))
+    return X
+
+
+def kalm_gated_gelu(Y: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
+    """Y [M, 2I] (gate | up) -> gelu_tanh(gate) * up [M, I]."""
+    if Y.stride(-1) != 1:
+        raise ValueError("unit column stride required")
+    M, I2 = Y.shape
+    I = I2 // 2
+    if out is None:
+        out = torch.empty(M, I, dtype=Y.dtype, device=Y.device)
+    _check("kalm_gated_gelu", load().kalm_gated_gelu(_ptr(Y), _dt(Y), Y.stride(0), M, I, _ptr(out), out.stride(0),
+                                                    _stream(stream)))
     return out
 
 

@@ -73,6 +73,8 @@ class DeviceBatch:
     w_yesno: torch.Tensor
     # buffers written by the step
     buf: Dict[str, torch.Tensor]
+    # model-shaped layer (RMSNorm, RoPE, gated MLP), when the batch carries its weights
+    model: Optional[Dict[str, object]] = None
 
 
 def upload(inputs: Dict[str, object], device="cuda", n_layers: Optional[int] = None) -> DeviceBatch:
@@ -133,11 +135,34 @@ def upload(inputs: Dict[str, object], device="cuda", n_layers: Optional[int] = N
     if dt == torch.bfloat16:
         buf["h0b"] = torch.empty(U, H, dtype=torch.bfloat16, device=device)
         buf["hfb"] = torch.empty(P, H, dtype=torch.bfloat16, device=device)
+    model = None
+    if inputs.get("model"):
+        mi = inputs["model"]
+        I = int(mi["mlp_dim"])
+        ch = min(rows, MLP_ROWS)
+        model = dict(eps=float(mi["eps"]), theta=float(mi["rope_theta"]), I=I,
+                     attn_norm=[dev(W["attn_norm"]) for W in layers], mlp_norm=[dev(W["mlp_norm"]) for W in layers],
+                     Wgu=[dev(np.concatenate([W["Wg"], W["Wu"]], 0)) for W in layers],
+                     Wd=[dev(W["Wd"]) for W in layers],
+                     final_norm=dev(mi["final_norm"]) if mi.get("final_norm") is not None else None)
+        buf.update(
+            xn=torch.empty(rows, H, dtype=dt, device=device),       # normalised layer input, every row
+            xu=torch.empty(U, H, dtype=dt, device=device),          # ... the queries' own rows
+            xf=torch.empty(P, H, dtype=dt, device=device),          # ... the final rows
+            hfn=torch.empty(P, H, dtype=torch.float32, device=device),  # final norm of the final rows
+            m_x=torch.empty(ch, H, dtype=dt, device=device),        # MLP row chunk: normalised input,
+            m_gu=torch.empty(ch, 2 * I, dtype=dt, device=device),   # gate | up projections,
+            m_a=torch.empty(ch, I, dtype=dt, device=device),        # activation
+        )
     return DeviceBatch(
         shape=sh, n_layers=L, dtype=dt, D=D, T=T, H=H, nq=sh.nq, nkv=sh.nkv, d=sh.d, chunk=chunk, Cmax=Cmax,
         n_queries=sh.n_queries, P=P, rows=rows, max_lq=int(lq.max()) if lq.size else 0,
         x=dev(inputs["x"]), token_mask=dev(inputs["token_mask"], torch.uint8), lq=dev(lq, torch.int32),
-        h0=dev(inputs["h0"], torch.float32), Wqkv=Wqkv, Wkvc=Wkvc, Wo=Wo, w_yesno=dev(inputs["w_yesno"]), buf=buf)
+        h0=dev(inputs["h0"], torch.float32), Wqkv=Wqkv, Wkvc=Wkvc, Wo=Wo, w_yesno=dev(inputs["w_yesno"]), buf=buf,
+        model=model)
+
+
+MLP_ROWS = 1 << 16  # rows per gated-MLP pass (bounds the gate/up buffer)
 
 
 def final_row_splits(P: int, nq: int, nkv: int, Cmax: int, cus: int = 256) -> int:
@@ -194,6 +219,8 @@ def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_
     stack with few pairs (off by default: at the one-query Nano shape the
     resumed pass is bound by per-workgroup start-up latency, not by its few
     key tiles, and the extra merge launch costs more than the split saves)."""
+    if b.model is not None:
+        return decoder_model(b, stream, rec, prune, reuse_self, split_kv)
     B = b.buf
     bf = b.dtype == torch.bfloat16
     qd, kv = b.nq * b.d, b.nkv * b.d
@@ -281,8 +308,134 @@ def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_
                             stream=stream)
 
 
+def decoder_model(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_self: bool = True,
+                  split_kv: bool = False):
+    """The model-shaped decoder layer around the merged attention: RMSNorm
+    before the attention and before a gated-GELU MLP, RoPE on the self Q/K
+    (positions 0..Lq-1 of each pair; the cached passage's cross keys carry
+    none), residual adds in fp32.  The same row pruning as the plain stack
+    (shared first layer with its self part once per query, final-row last
+    layer, one-layer stacks on final rows only); the pairs' final rows end in
+    ``hf``, the score reads their final RMSNorm."""
+    B, M = b.buf, b.model
+    qd, kv, eps, theta = b.nq * b.d, b.nkv * b.d, M["eps"], M["theta"]
+    scale = 1.0 / math.sqrt(b.d)
+    single = prune and b.n_layers == 1
+    last_pruned = pruned(b, prune)
+
+    def norm(src, w, dst, name):
+        with rec(name):
+            ops.kalm_rms_norm(src, w, eps, out=dst, stream=stream)
+
+    def rope(X, col0, nh, cu, mode, name):
+        with rec(name):
+            ops.kalm_rope(X, col0, nh, b.d, cu, b.max_lq, mode, theta, stream=stream)
+
+    def mlp(h, l, tag=""):
+        # gated MLP on the fp32 rows h (in place), MLP_ROWS rows per pass
+        for r0 in range(0, h.shape[0], MLP_ROWS):
+            hv = h[r0:r0 + MLP_ROWS]
+            n = hv.shape[0]
+            x, gu, a = B["m_x"][:n], B["m_gu"][:n], B["m_a"][:n]
+            norm(hv, M["mlp_norm"][l], x, "mlp_norm" + tag)
+            with rec("mlp_gate_up" + tag):
+                ops.kalm_linear(x, M["Wgu"][l], Y=gu, stream=stream)
+            with rec("mlp_act" + tag):
+                ops.kalm_gated_gelu(gu, out=a, stream=stream)
+            with rec("mlp_down" + tag):
+                ops.kalm_linear(a, M["Wd"][l], Y=hv, accumulate=True, stream=stream)
+
+    if not single:
+        with rec("gather_rows"):
+            ops.kalm_gather_rows(b.h0, B["h0_row"], dst=B["h"], stream=stream)
+    qkv = B["qkv"]
+    for l in range(b.n_layers):
+        kvc = B["kvc"][l].view(b.D * b.Cmax, 2 * kv)
+        cross = (kvc[:, :kv], kvc[:, kv:], B["chunk_mask"], B["doc_of_pair"], b.nq, b.nkv, b.d)
+        if prune and l == 0:
+            # the queries' own rows: norm, Q/K/V, RoPE once per query row
+            u = B["qkv_u"]
+            norm(b.h0, M["attn_norm"][0], B["xu"], "attn_norm_first")
+            with rec("qkv_linear_first"):
+                ops.kalm_linear(B["xu"], b.Wqkv[0], Y=u, stream=stream)
+            rope(u, 0, b.nq, B["cu_u"], 0, "rope_q_first")
+            rope(u, qd, b.nkv, B["cu_u"], 0, "rope_k_first")
+            rmode, o_rows, o_buf = ((ops.ROWS_SHARED_FINAL, b.P, B["of"]) if single
+                                    else (ops.ROWS_SHARED, b.rows, B["o"]))
+            if reuse_self:
+                with rec("self_attn_first"):
+                    ops.kalm_self_attn_partial(u[:, :qd], u[:, qd:qd + kv], u[:, qd + kv:], B["cu_u"], b.max_lq,
+                                               b.nq, b.nkv, b.d, scale=scale, out=B["o_self"], lse=B["lse_self"],
+                                               stream=stream)
+                if single and split_kv and "split_ws" in B:
+                    with rec("merged_attn_first_split"):
+                        ops.kalm_merged_attn_split(u[:, :qd], B["o_self"], B["lse_self"], B["cu_q"], b.max_lq,
+                                                   *cross, rmode, o_rows, final_row_splits(b.P, b.nq, b.nkv, b.Cmax),
+                                                   workspace=B["split_ws"], scale=scale, out=o_buf, stream=stream)
+                else:
+                    with rec("merged_attn_first_resume"):
+                        ops.kalm_merged_attn_resume(u[:, :qd], B["o_self"], B["lse_self"], B["cu_q"], b.max_lq,
+                                                    *cross, rmode, o_rows, scale=scale, out=o_buf, stream=stream)
+            else:
+                with rec("merged_attn_first"):
+                    ops.kalm_merged_attn_rows(u[:, :qd], u[:, qd:qd + kv], u[:, qd + kv:], B["cu_q"], b.max_lq,
+                                              *cross, rmode, o_rows, scale=scale, out=o_buf, stream=stream)
+            if single:
+                with rec("gather_final_rows"):
+                    ops.kalm_gather_rows(b.h0, B["h0_final"], dst=B["hf"], stream=stream)
+                with rec("o_linear_last"):
+                    ops.kalm_linear(B["of"], b.Wo[0], Y=B["hf"], accumulate=True, stream=stream)
+                mlp(B["hf"], 0, "_last")
+                continue
+        elif last_pruned and l == b.n_layers - 1 and l > 0:
+            # final rows only: normalised K/V (RoPE on K) of every row; norm, Q, RoPE at the
+            # final position, attention, projection and MLP of the final rows
+            norm(B["h"], M["attn_norm"][l], B["xn"], "attn_norm")
+            kvs = qkv.view(-1)[: b.rows * 2 * kv].view(b.rows, 2 * kv)
+            with rec("kv_linear_last"):
+                ops.kalm_linear(B["xn"], b.Wqkv[l][qd:], Y=kvs, stream=stream)
+            rope(kvs, 0, b.nkv, B["cu_q"], 0, "rope_k")
+            with rec("gather_final_rows"):
+                ops.kalm_gather_rows(B["h"], B["final_row"], dst=B["hf"], stream=stream)
+            norm(B["hf"], M["attn_norm"][l], B["xf"], "attn_norm_last")
+            with rec("q_linear_last"):
+                ops.kalm_linear(B["xf"], b.Wqkv[l][:qd], Y=B["qf"], stream=stream)
+            rope(B["qf"], 0, b.nq, B["cu_q"], 1, "rope_q_last")
+            with rec("merged_attn_last"):
+                ops.kalm_merged_attn_rows(B["qf"], kvs[:, :kv], kvs[:, kv:], B["cu_q"], b.max_lq, *cross,
+                                          ops.ROWS_FINAL, b.P, scale=scale, out=B["of"], stream=stream)
+            with rec("o_linear_last"):
+                ops.kalm_linear(B["of"], b.Wo[l], Y=B["hf"], accumulate=True, stream=stream)
+            mlp(B["hf"], l, "_last")
+            continue
+        else:
+            norm(B["h"], M["attn_norm"][l], B["xn"], "attn_norm")
+            with rec("qkv_linear"):
+                ops.kalm_linear(B["xn"], b.Wqkv[l], Y=qkv, stream=stream)
+            rope(qkv, 0, b.nq, B["cu_q"], 0, "rope_q")
+            rope(qkv, qd, b.nkv, B["cu_q"], 0, "rope_k")
+            with rec("merged_attn"):
+                ops.kalm_merged_attn(qkv[:, :qd], qkv[:, qd:qd + kv], qkv[:, qd + kv:], B["cu_q"], b.max_lq,
+                                     *cross[:4], b.nq, b.nkv, b.d, scale=scale, out=B["o"], stream=stream)
+        with rec("o_linear"):
+            ops.kalm_linear(B["o"], b.Wo[l], Y=B["h"], accumulate=True, stream=stream)
+        mlp(B["h"], l)
+    if not last_pruned:
+        with rec("gather_final_rows"):
+            ops.kalm_gather_rows(B["h"], B["final_row"], dst=B["hf"], stream=stream)
+
+
 def score(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True):
     """Row a4: yes/no readout at every pair's final row."""
+    if b.model is not None:
+        # the pairs' final rows are in hf; the readout follows the final RMSNorm when there is one
+        hf = b.buf["hf"]
+        if b.model["final_norm"] is not None:
+            with rec("final_norm"):
+                ops.kalm_rms_norm(hf, b.model["final_norm"], b.model["eps"], out=b.buf["hfn"], stream=stream)
+            hf = b.buf["hfn"]
+        with rec("yesno_score"):
+            return ops.kalm_yesno_score(hf, b.buf["p_idx"], b.w_yesno, stream=stream)
     with rec("yesno_score"):
         if pruned(b, prune):
             return ops.kalm_yesno_score(b.buf["hf"], b.buf["p_idx"], b.w_yesno, stream=stream)

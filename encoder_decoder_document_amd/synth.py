@@ -115,7 +115,8 @@ def _normal(rng: np.random.Generator, shape, std: float, bf16: bool) -> np.ndarr
 
 
 def make_inputs(shape_index: int, seed: Optional[int] = None, nan_padding: bool = True,
-                n_layers: Optional[int] = None, shape: Optional[Shape] = None) -> Dict[str, object]:
+                n_layers: Optional[int] = None, shape: Optional[Shape] = None,
+                mlp_dim: Optional[int] = None) -> Dict[str, object]:
     """Draw one batch for ``SHAPES[shape_index]`` (or an explicit ``shape``).
 
     Returns a dict of host arrays:
@@ -127,6 +128,12 @@ def make_inputs(shape_index: int, seed: Optional[int] = None, nan_padding: bool 
       w_yesno [2,H] (row 0 stands for the "yes" LM-head row, row 1 for "no").
     The seed defaults to 1000 + shape_index.  ``n_layers`` overrides the layer
     count (tests use it to cut long stacks).
+
+    With ``mlp_dim`` = I the batch also carries the weights of a model-shaped
+    layer, drawn from a generator of their own so that every array above is
+    unchanged: per layer attn_norm and mlp_norm [H] (1 + N(0, 0.1^2)), Wg and
+    Wu [I,H] and Wd [H,I] (N(0, 0.02^2)), and ``model`` = dict(rope_theta
+    10000, eps 1e-6, final_norm [H] (1 + N(0, 0.1^2))).
     """
     sh = shape if shape is not None else SHAPES[shape_index]
     if seed is None:
@@ -156,8 +163,22 @@ def make_inputs(shape_index: int, seed: Optional[int] = None, nan_padding: bool 
             Wo=_normal(g_w, (H, sh.nq * sh.d), 0.02, bf16),
         ))
     w_yesno = _normal(g_yn, (2, H), 0.02, bf16)
-    return dict(shape=sh, seed=seed, doc_len=doc_len, token_mask=token_mask, x=x,
-                lq=lq, h0=h0, layers=layers, w_yesno=w_yesno)
+    out = dict(shape=sh, seed=seed, doc_len=doc_len, token_mask=token_mask, x=x,
+               lq=lq, h0=h0, layers=layers, w_yesno=w_yesno)
+    if mlp_dim:
+        g_m = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
+        I = int(mlp_dim)
+        for W in layers:
+            W.update(attn_norm=1.0 + _normal(g_m, (H,), 0.1, bf16), mlp_norm=1.0 + _normal(g_m, (H,), 0.1, bf16),
+                     Wg=_normal(g_m, (I, H), 0.02, bf16), Wu=_normal(g_m, (I, H), 0.02, bf16),
+                     Wd=_normal(g_m, (H, I), 0.02, bf16))
+            if bf16:  # 1 + x must stay bf16-representable
+                W["attn_norm"] = round_to_bf16(W["attn_norm"])
+                W["mlp_norm"] = round_to_bf16(W["mlp_norm"])
+        fn = 1.0 + _normal(g_m, (H,), 0.1, bf16)
+        out["model"] = dict(rope_theta=10000.0, eps=1e-6, final_norm=round_to_bf16(fn) if bf16 else fn,
+                            mlp_dim=I)
+    return out
 
 
 def normal(seed: int, shape, std: float = 1.0, bf16: bool = True) -> np.ndarray:

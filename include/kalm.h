@@ -264,6 +264,48 @@ kalm_status kalm_merged_attn_split(const void* Q, int64_t q_ld, int64_t q_rows, 
                                    int64_t workspace_bytes, void* stream);
 
 /*
+ * Decoder-layer completion (a model-shaped layer around a3).  The pages say the
+ * forward pass reads every dim, head count, layer count and RoPE parameter from
+ * the model's config, RoPE inverse frequencies computed from it ("KaLM-Reranker
+ * -V1-Nano -- MLX (Apple Silicon)", What this is / Derivation); no other layer
+ * internal is given, so these are the standard forms.
+ *
+ * kalm_rms_norm -- y[m] = x[m] / sqrt(mean_j x[m,j]^2 + eps) * w, fp32 sum of
+ * squares, one rounding to y's dtype.  x [M, H] (row stride x_ld), w [H],
+ * y [M, H] (row stride y_ld); dtypes F32 or BF16 each.  Requires H % 4 == 0,
+ * ld values multiples of 4, 16-byte aligned pointers; x and y may not overlap.
+ */
+kalm_status kalm_rms_norm(const void* x, kalm_dtype x_dt, int64_t x_ld, int64_t M, int32_t H,
+                          const void* w, kalm_dtype w_dt, float eps, void* y, kalm_dtype y_dt,
+                          int64_t y_ld, void* stream);
+
+/*
+ * kalm_rope -- rotary position embedding, in place, on n_heads heads of d
+ * columns starting at column col0 of X [rows, *] (row stride ld): for each head
+ * and i < d/2 the pair (x_i, x_{i+d/2}) at position t turns by the angle
+ * t * theta^(-2i/d) ("rotate half" pairing), fp32 arithmetic, one rounding.
+ *   row_mode 0  sequence s owns rows cu[s] .. cu[s+1]-1 at positions 0, 1, ...
+ *               (max_len >= every length; rows past max_len are not touched)
+ *   row_mode 1  one row per sequence: row s at position cu[s+1]-cu[s]-1 (the
+ *               final position)
+ * Rows outside [0, rows) are skipped.  Requires d % 8 == 0, col0 and ld
+ * multiples of 4, theta > 1, X 16-byte aligned.
+ */
+kalm_status kalm_rope(void* X, kalm_dtype dt, int64_t ld, int64_t rows, int32_t col0, int32_t n_heads,
+                      int32_t d, const int32_t* cu, int32_t n_seq, int32_t max_len, int32_t row_mode,
+                      float theta, void* stream);
+
+/*
+ * kalm_gated_gelu -- the gated MLP's activation: A[m, j] = gelu(Y[m, j]) *
+ * Y[m, I + j] for j < I, gelu in its tanh form 0.5 x (1 + tanh(sqrt(2/pi)
+ * (x + 0.044715 x^3))); Y [M, 2I] holds the gate projection then the up
+ * projection.  Requires I % 4 == 0, ld values multiples of 4, 16-byte aligned
+ * pointers.
+ */
+kalm_status kalm_gated_gelu(const void* Y, kalm_dtype dt, int64_t y_ld, int64_t M, int32_t I, void* A,
+                            int64_t a_ld, void* stream);
+
+/*
  * a4 -- yes/no readout ([MLX] What this is: score = softmax([logit_yes,
  * logit_no])[yes] at the decoder's final position; [Q4KM] Score a pair and [Q80]
  * Frozen inference contract: margin = yes - no, score = sigmoid(margin)).

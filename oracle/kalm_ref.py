@@ -285,6 +285,55 @@ def pair_layout(lq: Sequence[int], n_docs: int):
 
 
 # --------------------------------------------------------------------------
+# Decoder-layer completion (a model-shaped layer around a3)
+# --------------------------------------------------------------------------
+def rms_norm(x, w, eps: float = 1e-6):
+    """Root-mean-square normalisation of each row, times a per-column weight.
+
+    The pages name no norm; they say every dim and RoPE parameter comes from
+    the model's config ([MLX] What this is).  READING: the standard form
+    y = x / sqrt(mean(x^2) + eps) * w (a plain weight, eps from config,
+    1e-6 by default).  x [..., H], w [H] -> float64.
+    """
+    x = np.asarray(x, dtype=F64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(w, dtype=F64)
+
+
+def rope(x, positions, theta: float = 10000.0):
+    """Rotary position embedding of x [L, n_heads, d] at ``positions`` [L].
+
+    [MLX] Derivation: the inverse-frequency tables are computed from the
+    config.  READING: inverse frequency theta^(-2i/d) for i < d/2, and the
+    "rotate half" pairing -- dim i turns together with dim i + d/2 by the
+    angle position * theta^(-2i/d).
+    """
+    x = np.asarray(x, dtype=F64)
+    d = x.shape[-1]
+    half = d // 2
+    inv_freq = float(theta) ** (-2.0 * np.arange(half) / d)
+    ang = np.asarray(positions, dtype=F64)[:, None] * inv_freq[None, :]   # [L, d/2]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def gelu_tanh(x):
+    """GELU in its tanh form, 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).
+
+    READING: the gated MLP's activation (the pages name none; the tanh form is
+    the one used by the Gemma family that T5-Gemma builds on).
+    """
+    x = np.asarray(x, dtype=F64)
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def gated_gelu(g, u):
+    """The gated MLP's activation: gelu_tanh(gate) * up, elementwise."""
+    return gelu_tanh(g) * np.asarray(u, dtype=F64)
+
+
+# --------------------------------------------------------------------------
 # a5: the decoder stack glue (one pair)
 # --------------------------------------------------------------------------
 def _store_fn(mode: str, dtype: str) -> Callable:
@@ -297,7 +346,7 @@ def _store_fn(mode: str, dtype: str) -> Callable:
 
 def decoder_stack(h0, pooled_doc, chunk_mask_doc, layers: List[Dict[str, np.ndarray]], w_yesno,
                   nq: int, nkv: int, d: int, mode: str = "mirror", dtype: str = "bf16",
-                  return_hidden: bool = False):
+                  return_hidden: bool = False, model: Optional[Dict[str, object]] = None):
     """Run one (query, passage) pair through the merged-attention stack.
 
     READING (the pages give only the layer counts and the merged attention
@@ -310,6 +359,16 @@ def decoder_stack(h0, pooled_doc, chunk_mask_doc, layers: List[Dict[str, np.ndar
     rounds to the storage dtype in mirror mode and is the identity in pure
     mode; h itself is rounded to fp32 after each layer in mirror mode.
 
+    With ``model`` (dict rope_theta, eps, final_norm [H] or None) each layer
+    is the model-shaped reading (pre-norm, RoPE on the self Q/K, gated MLP):
+        hb = store(rms_norm(h, attn_norm))
+        Q, Ks = store(rope(store(hb Wq^T))), store(rope(store(hb Wk^T)))  at
+                positions 0..Lq-1; Vs, Kc, Vc as above (no RoPE on cross keys)
+        h = h + store(merged_attn(...)) Wo^T
+        x = store(rms_norm(h, mlp_norm))
+        h = h + store(gated_gelu(store(x Wg^T), store(x Wu^T))) Wd^T
+    and the score reads rms_norm(h_last, final_norm) when final_norm is given.
+
     h0 [Lq,H], pooled_doc [C,H] (already in storage precision), chunk_mask_doc
     [C] -> dict as ``yesno_score`` (+ ``h`` [Lq,H] when return_hidden).
     """
@@ -318,18 +377,31 @@ def decoder_stack(h0, pooled_doc, chunk_mask_doc, layers: List[Dict[str, np.ndar
     h = np.asarray(h0, dtype=F64).copy()
     Lq = h.shape[0]
     pooled_doc = np.asarray(pooled_doc, dtype=F64)
+    eps = float(model["eps"]) if model else 0.0
     for W in layers:
-        hb = st(h)
+        hb = st(rms_norm(h, W["attn_norm"], eps)) if model else st(h)
         Qm = st(hb @ np.asarray(W["Wq"], F64).T).reshape(Lq, nq, d)
         Ks = st(hb @ np.asarray(W["Wk"], F64).T).reshape(Lq, nkv, d)
         Vs = st(hb @ np.asarray(W["Wv"], F64).T).reshape(Lq, nkv, d)
+        if model:
+            pos = np.arange(Lq)
+            Qm = st(rope(Qm, pos, model["rope_theta"]))
+            Ks = st(rope(Ks, pos, model["rope_theta"]))
         Kc, Vc = cross_kv(pooled_doc, W["Wkc"], W["Wvc"])
         Kc = st(Kc).reshape(-1, nkv, d)
         Vc = st(Vc).reshape(-1, nkv, d)
         O, _ = merged_attn(Qm, Ks, Vs, Kc, Vc, chunk_mask_doc)
         O = st(O).reshape(Lq, nq * d)
         h = keep_f32(h + O @ np.asarray(W["Wo"], F64).T)
-    out = yesno_score(h[Lq - 1], w_yesno)
+        if model:
+            x = st(rms_norm(h, W["mlp_norm"], eps))
+            g = st(x @ np.asarray(W["Wg"], F64).T)
+            u = st(x @ np.asarray(W["Wu"], F64).T)
+            h = keep_f32(h + st(gated_gelu(g, u)) @ np.asarray(W["Wd"], F64).T)
+    last = h[Lq - 1]
+    if model and model.get("final_norm") is not None:
+        last = keep_f32(rms_norm(last, model["final_norm"], eps))
+    out = yesno_score(last, w_yesno)
     if return_hidden:
         out["h"] = h
     return out
@@ -361,7 +433,7 @@ def stack_scores(inputs: Dict[str, object], pairs: Optional[Iterable[int]] = Non
         pooled_doc, cm_doc = pooled_cache[dd]
         h0 = inputs["h0"][q_start[q]:q_start[q + 1]]
         out = decoder_stack(h0, pooled_doc, cm_doc, layers, inputs["w_yesno"],
-                            sh.nq, sh.nkv, sh.d, mode=mode, dtype=sh.dtype)
+                            sh.nq, sh.nkv, sh.d, mode=mode, dtype=sh.dtype, model=inputs.get("model"))
         for k in res:
             res[k].append(float(out[k]))
     res = {k: np.asarray(v, dtype=F64) for k, v in res.items()}

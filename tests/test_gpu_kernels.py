@@ -579,6 +579,60 @@ def test_merged_attn_resume_bad_doc_gives_nan_rows():
     assert np.isfinite(g[:20]).all() and np.isnan(g[20:]).all()
 
 
+# ------------------------------------------------------------------ model-shaped layer parts
+@pytest.mark.parametrize("M,H,xdt,ydt", [(1000, 1152, "f32", "bf16"), (37, 640, "f32", "f32"), (5, 64, "bf16", "bf16"),
+                                         (300, 2560, "bf16", "f32")])
+def test_rms_norm_parity(M, H, xdt, ydt):
+    _announce(f"rms_norm M={M} H={H} {xdt}->{ydt}")
+    t = {"f32": torch.float32, "bf16": torch.bfloat16}
+    x = synth.normal(61, (M, H), 1.5, xdt == "bf16")
+    x[3 % M] *= 40.0  # one large row
+    if xdt == "bf16":
+        x = synth.round_to_bf16(x)  # the device input is exactly what the oracle sees
+    w = 1.0 + synth.normal(62, (H,), 0.1, ydt == "bf16")
+    w = synth.round_to_bf16(w) if ydt == "bf16" else w
+    y = ops.kalm_rms_norm(to_dev(x, t[xdt]), to_dev(w, t[ydt]), 1e-6, y_dtype=t[ydt])
+    torch.cuda.synchronize()
+    ref = oracle.rms_norm(x, w, 1e-6)
+    assert_close(to_np(y), ref, *(BF16_TOL if ydt == "bf16" else F32_TOL), "rms_norm")
+
+
+@pytest.mark.parametrize("bf16,mode", [(True, 0), (False, 0), (True, 1), (False, 1)])
+def test_rope_parity(bf16, mode):
+    _announce(f"rope bf16={bf16} mode={mode}")
+    nq, nkv, d = 4, 2, 256 if bf16 else 64
+    lens = np.array([1, 31, 130, 512, 7], np.int64)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rows = int(lens.sum()) if mode == 0 else len(lens)
+    ld = (nq + 2 * nkv) * d
+    X = synth.normal(63, (rows, ld), 1.0, bf16)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    Xd = to_dev(X, dt)
+    ops.kalm_rope(Xd, 0, nq, d, to_dev(cu, torch.int32), int(lens.max()), mode, 10000.0)
+    ops.kalm_rope(Xd, nq * d, nkv, d, to_dev(cu, torch.int32), int(lens.max()), mode, 10000.0)
+    torch.cuda.synchronize()
+    pos = np.concatenate([np.arange(n) for n in lens]) if mode == 0 else lens - 1
+    ref = X.astype(np.float64).copy()
+    ref[:, :nq * d] = oracle.rope(X[:, :nq * d].reshape(rows, nq, d), pos, 10000.0).reshape(rows, -1)
+    ref[:, nq * d:(nq + nkv) * d] = oracle.rope(X[:, nq * d:(nq + nkv) * d].reshape(rows, nkv, d), pos,
+                                                10000.0).reshape(rows, -1)
+    got = to_np(Xd)
+    assert_close(got, ref, *(BF16_TOL if bf16 else F32_TOL), "rope")
+    # the V columns are not touched
+    assert np.array_equal(got[:, (nq + nkv) * d:], X[:, (nq + nkv) * d:].astype(np.float64))
+
+
+@pytest.mark.parametrize("M,I,bf16", [(1000, 1536, True), (33, 64, False), (7, 4, True)])
+def test_gated_gelu_parity(M, I, bf16):
+    _announce(f"gated_gelu M={M} I={I} bf16={bf16}")
+    Y = synth.normal(64, (M, 2 * I), 2.0, bf16)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    A = ops.kalm_gated_gelu(to_dev(Y, dt))
+    torch.cuda.synchronize()
+    ref = oracle.gated_gelu(Y[:, :I], Y[:, I:])
+    assert_close(to_np(A), ref, *(BF16_TOL if bf16 else F32_TOL), "gated_gelu")
+
+
 # ------------------------------------------------------------------ a4 score
 @pytest.mark.parametrize("H,hb,wb", [(640, False, True), (1152, True, True), (64, False, False)])
 def test_yesno_score_parity(H, hb, wb):

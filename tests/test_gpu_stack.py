@@ -148,6 +148,30 @@ def test_step_graph_replays_equal_eager(idx, n_layers):
         assert np.array_equal(again, eager[3], equal_nan=True)
 
 
+@pytest.mark.parametrize("idx,n_layers,mlp_dim,n_sample", [(0, 2, 96, None), (1, None, 1536, 8), (2, 3, 1536, 8)])
+def test_model_shaped_stack_parity(idx, n_layers, mlp_dim, n_sample):
+    # the model-shaped layer (RMSNorm, RoPE on the self Q/K, gated-GELU MLP,
+    # final norm) through the pruned path, against the oracle
+    sh = synth.SHAPES[idx]
+    print(f"[case] model-shaped stack {sh.name} layers={n_layers} mlp={mlp_dim}", flush=True)
+    inp = synth.make_inputs(idx, nan_padding=True, n_layers=n_layers, mlp_dim=mlp_dim)
+    b, got = _run(inp)
+    pairs = list(range(sh.pairs)) if n_sample is None else _sample_pairs(inp, n_sample)
+    _check(inp, b, got, pairs)
+
+
+def test_model_shaped_pruned_equals_full():
+    idx = 2
+    sh = synth.SHAPES[idx]
+    print(f"[case] model-shaped stack {sh.name} 3 layers, pruned vs full", flush=True)
+    inp = synth.make_inputs(idx, nan_padding=True, n_layers=3, mlp_dim=1536)
+    b = stack.upload(inp)
+    full = to_np(stack.step(b, prune=False)[3])
+    pruned = to_np(stack.step(b, prune=True)[3])
+    torch.cuda.synchronize()
+    assert_close(pruned, full, 1e-3, 0.0, "pruned vs full score (model-shaped)")
+
+
 @pytest.mark.parametrize("chunk", [1, 2, 8, 16])
 def test_stack_matryoshka_chunk_sizes(chunk):
     # the pooling granularity is a parameter of the path: every chunk size

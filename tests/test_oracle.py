@@ -6,6 +6,7 @@ or brute-force loops on tiny inputs, chosen so that a plausible mistake (a
 dropped term, a wrong index or sign, a transposed operand, a wrong divisor)
 fails at least one of them.  CPU only.
 """
+import dataclasses
 import json
 import math
 import os
@@ -391,6 +392,139 @@ def test_stack_mirror_close_to_pure_on_bf16_shape():
     mirror = oracle.stack_scores(inp, mode="mirror")
     d = np.abs(pure["score"] - mirror["score"])
     assert d.max() < 5e-3 and d.max() > 0
+
+
+# ------------------------------------------------------------------ model-shaped layer parts
+def test_rms_norm_worked_example_library_and_scale_invariance():
+    y = oracle.rms_norm(np.array([[3.0, 4.0]]), np.array([1.0, 2.0]), eps=0.0)
+    r = math.sqrt((9 + 16) / 2)
+    np.testing.assert_allclose(y, [[3 / r, 8 / r]], rtol=1e-15)
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((7, 48))
+    w = 1 + 0.1 * rng.standard_normal(48)
+    ref = torch.nn.functional.rms_norm(torch.as_tensor(x), (48,), torch.as_tensor(w), eps=1e-6).numpy()
+    np.testing.assert_allclose(oracle.rms_norm(x, w, 1e-6), ref, rtol=1e-12, atol=1e-14)
+    # without eps the output ignores the row's scale, and with unit weight its mean square is 1
+    np.testing.assert_allclose(oracle.rms_norm(5 * x, w, 0.0), oracle.rms_norm(x, w, 0.0), rtol=1e-13)
+    np.testing.assert_allclose(np.mean(oracle.rms_norm(x, np.ones(48), 0.0) ** 2, axis=1), 1.0, rtol=1e-13)
+
+
+def test_rope_pairing_frequencies_and_relative_position():
+    # rotate-half pairing: dim 0 turns with dim d/2 = 2 at frequency theta^0 = 1,
+    # dim 1 with dim 3 at theta^(-2/4) = 0.01 (theta = 10^4)
+    e0 = oracle.rope(np.array([[[1.0, 0.0, 0.0, 0.0]]]), [1], 1e4)[0, 0]
+    np.testing.assert_allclose(e0, [math.cos(1), 0, math.sin(1), 0], atol=1e-15)
+    e1 = oracle.rope(np.array([[[0.0, 1.0, 0.0, 0.0]]]), [1], 1e4)[0, 0]
+    np.testing.assert_allclose(e1, [0, math.cos(0.01), 0, math.sin(0.01)], atol=1e-15)
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 3, 16))
+    k = rng.standard_normal((1, 3, 16))
+    # position 0 is the identity; every rotation keeps the norm
+    np.testing.assert_array_equal(oracle.rope(q, [0], 500.0), q)
+    np.testing.assert_allclose(np.linalg.norm(oracle.rope(q, [37], 500.0), axis=-1), np.linalg.norm(q, axis=-1),
+                               rtol=1e-13)
+    # the score of a rotated query and key depends on the positions only through their difference
+    for m, n in [(5, 2), (40, 33), (7, 7), (3, 9)]:
+        a = np.sum(oracle.rope(q, [m], 500.0) * oracle.rope(k, [n], 500.0), axis=-1)
+        b = np.sum(oracle.rope(q, [m - n], 500.0) * k, axis=-1)
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+    # the same rotation written as complex multiplication of (x_i + i x_{i+d/2})
+    pos = np.array([0, 1, 4, 11])
+    x = rng.standard_normal((4, 2, 8))
+    z = torch.complex(torch.as_tensor(x[..., :4]), torch.as_tensor(x[..., 4:]))
+    ang = torch.as_tensor(pos, dtype=torch.float64)[:, None] * (1e4 ** (-torch.arange(0, 8, 2, dtype=torch.float64)
+                                                                        / 8))[None]
+    zr = z * torch.polar(torch.ones_like(ang), ang)[:, None, :]
+    ref = torch.cat([zr.real, zr.imag], -1).numpy()
+    np.testing.assert_allclose(oracle.rope(x, pos, 1e4), ref, rtol=1e-12, atol=1e-14)
+
+
+def test_gelu_tanh_library_odd_identity_and_exact_gelu():
+    x = np.linspace(-8, 8, 2001)
+    ref = torch.nn.functional.gelu(torch.as_tensor(x), approximate="tanh").numpy()
+    np.testing.assert_allclose(oracle.gelu_tanh(x), ref, rtol=1e-12, atol=1e-15)
+    # gelu(x) - gelu(-x) = x holds exactly for the tanh form
+    np.testing.assert_allclose(oracle.gelu_tanh(x) - oracle.gelu_tanh(-x), x, atol=1e-13)
+    # and it stays within 1e-3 of the exact x * Phi(x)
+    exact = x * 0.5 * (1 + scipy.special.erf(x / math.sqrt(2)))
+    assert np.max(np.abs(oracle.gelu_tanh(x) - exact)) < 1e-3
+    np.testing.assert_allclose(oracle.gated_gelu(x, 3.0), 3.0 * ref, rtol=1e-12, atol=1e-14)
+
+
+def _model_inputs(n_layers=2, seed=21, mlp_dim=48):
+    sh = synth.Shape("mini_model_f32", 1, 3, 16, 32, 4, 2, 8, n_layers, "f32", ("loguniform", 4, 16),
+                     ("const", 6, 6))
+    return synth.make_inputs(0, seed=seed, shape=sh, mlp_dim=mlp_dim)
+
+
+def _torch_model_stack_one_pair(h0, x_doc, mask_doc, layers, model, w_yesno, nq, nkv, d):
+    """Independent fp64 formulation of the model-shaped layer with torch
+    library routines: rms_norm, complex-multiplication RoPE, SDPA over the
+    concatenated KV, tanh-GELU."""
+    F = torch.nn.functional
+    T, H = x_doc.shape
+    m = torch.as_tensor(mask_doc, dtype=torch.float64)
+    xs = torch.where(m[:, None] > 0, torch.as_tensor(np.nan_to_num(x_doc), dtype=torch.float64), 0.0)
+    cnt = m.view(-1, 4).sum(1)
+    pooled = xs.view(-1, 4, H).sum(1) / cnt.clamp(min=1)[:, None]
+    cvalid = cnt > 0
+    h = torch.as_tensor(h0, dtype=torch.float64)
+    Lq = h.shape[0]
+    eps = model["eps"]
+    ang = torch.arange(Lq, dtype=torch.float64)[:, None] * (
+        model["rope_theta"] ** (-torch.arange(0, d, 2, dtype=torch.float64) / d))[None]
+    rot = torch.polar(torch.ones_like(ang), ang)[:, None, :]
+
+    def rope(t):
+        z = torch.complex(t[..., : d // 2], t[..., d // 2:]) * rot
+        return torch.cat([z.real, z.imag], -1)
+
+    for W in layers:
+        t = {k: torch.as_tensor(v, dtype=torch.float64) for k, v in W.items()}
+        x = F.rms_norm(h, (H,), t["attn_norm"], eps=eps)
+        q = rope((x @ t["Wq"].T).view(Lq, nq, d))
+        ks = rope((x @ t["Wk"].T).view(Lq, nkv, d))
+        k = torch.cat([ks, (pooled @ t["Wkc"].T).view(-1, nkv, d)], 0)
+        v = torch.cat([(x @ t["Wv"].T).view(Lq, nkv, d), (pooled @ t["Wvc"].T).view(-1, nkv, d)], 0)
+        k = k.repeat_interleave(nq // nkv, 1).transpose(0, 1)
+        v = v.repeat_interleave(nq // nkv, 1).transpose(0, 1)
+        allow = torch.cat([torch.ones(Lq, Lq, dtype=torch.bool).tril(), cvalid[None].expand(Lq, -1)], 1)
+        o = F.scaled_dot_product_attention(q.transpose(0, 1), k, v, attn_mask=allow)
+        h = h + o.transpose(0, 1).reshape(Lq, nq * d) @ t["Wo"].T
+        x2 = F.rms_norm(h, (H,), t["mlp_norm"], eps=eps)
+        h = h + (F.gelu(x2 @ t["Wg"].T, approximate="tanh") * (x2 @ t["Wu"].T)) @ t["Wd"].T
+    last = F.rms_norm(h[-1], (H,), torch.as_tensor(model["final_norm"], dtype=torch.float64), eps=eps)
+    w = torch.as_tensor(w_yesno, dtype=torch.float64)
+    return float(last @ (w[0] - w[1]))
+
+
+def test_model_stack_pure_matches_independent_torch_formulation():
+    inp = _model_inputs()
+    sh = inp["shape"]
+    res = oracle.stack_scores(inp, mode="pure")
+    for p in range(sh.pairs):
+        dd = p % sh.n_docs
+        mg = _torch_model_stack_one_pair(inp["h0"], inp["x"][dd], inp["token_mask"][dd], inp["layers"],
+                                         inp["model"], inp["w_yesno"], sh.nq, sh.nkv, sh.d)
+        assert math.isclose(res["margin"][p], mg, rel_tol=1e-10, abs_tol=1e-12)
+
+
+def test_model_layer_reduces_to_plain_layer():
+    # one decoder position (RoPE at position 0 is the identity), unit-rms input,
+    # unit norm weights, no eps, a zero down projection and no final norm: the
+    # model-shaped layer is the plain one
+    inp = _model_inputs(n_layers=1, seed=5)
+    sh = dataclasses.replace(inp["shape"], lq=("const", 1, 1))
+    inp = synth.make_inputs(0, seed=5, shape=sh, mlp_dim=48)
+    h0 = inp["h0"].astype(np.float64)
+    inp["h0"] = h0 / np.sqrt(np.mean(h0 * h0, axis=1, keepdims=True))
+    for W in inp["layers"]:
+        W["attn_norm"] = np.ones_like(W["attn_norm"])
+        W["Wd"] = np.zeros_like(W["Wd"])
+    model = dict(inp["model"], eps=0.0, final_norm=None)
+    plain = oracle.stack_scores(dict(inp, model=None), mode="pure")
+    shaped = oracle.stack_scores(dict(inp, model=model), mode="pure")
+    np.testing.assert_allclose(shaped["margin"], plain["margin"], rtol=1e-12, atol=1e-14)
 
 
 # ------------------------------------------------------------------ ranking
