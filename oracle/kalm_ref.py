@@ -16,6 +16,10 @@ Sources (web pages; cited by title and section):
   [PAPER] "KaLM-Reranker-V1: Fast but Not Late Interaction for Compressed
           Document Reranking", abstract (encoder pre-encodes passages with
           Matryoshka pooling; decoder cross-attends to them).
+  The optional model-shaped layer parts (rms_norm, rope, gelu_tanh,
+  gated_gelu) follow [MLX] "What this is" / "Derivation" (every dim and RoPE
+  parameter read from the config, RoPE inverse frequencies computed from it)
+  in their standard forms, each marked READING.
 
 Every function computes in float64 on the exact values it is handed.  Where a
 page leaves a step open the plainest reading is taken; each such reading is
