@@ -46,11 +46,11 @@ FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 MEASURED_TRAFFIC = {
     # profiles/hbm_traffic_small_stack26_bf16.md
     "o_linear": {"src": "1ac37431fbadf90a7420ae28adc0c318d18297856aeb8e2bbeac68bd819470da",
-                 "fetch_kib": 3107738.0, "write_kib": 6443285.0},
+                 "fetch_kib": 3108700.0, "write_kib": 6443199.0},
     "qkv_linear": {"src": "1ac37431fbadf90a7420ae28adc0c318d18297856aeb8e2bbeac68bd819470da",
-                   "fetch_kib": 2385666.0, "write_kib": 2616612.0},
-    "merged_attn": {"src": "c6c79ac4186c8f138fef4c9840b2afca7f4919d640011c5b16bba3f476e7413a",
-                    "fetch_kib": 1483483.0, "write_kib": 1792200.0},
+                   "fetch_kib": 2368201.0, "write_kib": 2616645.0},
+    "merged_attn": {"src": "e4398fb95f38317814949013ab059bd39c8d78cf15179276fb16da0351d1715c",
+                    "fetch_kib": 1483712.0, "write_kib": 1792200.0},
 }
 KERNEL_SRC = {"o_linear": "gemm.hip", "qkv_linear": "gemm.hip", "cross_kv": "gemm.hip",
               "merged_attn": "attn_bf16.h", "chunk_pool": "pool.hip", "gather_rows": "rows.hip"}
