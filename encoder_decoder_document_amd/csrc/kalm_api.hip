@@ -51,7 +51,7 @@ kalm_status check_launch(const char* what) {
 
 extern "C" {
 
-int32_t kalm_version(void) { return 100; }
+int32_t kalm_version(void) { return 200; }
 
 const char* kalm_last_error(void) { return kalm::g_err; }
 

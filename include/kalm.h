@@ -5,7 +5,10 @@
  * interaction" reranker: chunk pooling of passage encoder states, the cross
  * K/V projection of the pooled vectors, the merged self+cross attention of
  * the decoder and the yes/no relevance score, plus the linear layers and row
- * layout that chain them into a decoder stack.
+ * layout that chain them into a decoder stack, the ranking of the scores, the
+ * split forms of the merged attention (self part once, cross part resumed or
+ * in split-KV shares) and the optional parts of a model-shaped layer (RMSNorm,
+ * RoPE, gated GELU).
  *
  * Page citations (by page title and section):
  *   [MLX]  "KaLM-Reranker-V1-Nano -- MLX (Apple Silicon)": What this is, Speed.
@@ -28,7 +31,8 @@
  *  - There is no CPU fallback.  Without a usable GPU every call returns
  *    KALM_ERR_NO_DEVICE (the same stance as the --require-gpu guard in [Q4KM]
  *    Troubleshooting and [Q80] Score one query-passage pair).
- *  - Every output element is written, padded positions included, so results are
+ *  - Every output element is written, padded positions included (except the rows
+ *    of pairs an entry point documents as skipped), so results are
  *    deterministic run to run (no atomics in any reduction).
  *  - Calls keep no state between them and may be made from several host threads.
  */
@@ -51,7 +55,8 @@ typedef enum {
 
 typedef enum { KALM_F32 = 0, KALM_BF16 = 1 } kalm_dtype;
 
-/* Library version, major*10000 + minor*100 + patch. */
+/* Library version, major*10000 + minor*100 + patch (0.2.0: split attention,
+ * one-layer final rows, layer parts). */
 int32_t kalm_version(void);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */

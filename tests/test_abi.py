@@ -48,7 +48,7 @@ def test_binding_covers_every_declared_symbol():
 def test_invalid_arguments_rejected_before_launch():
     from encoder_decoder_document_amd import ops
     lib = ops.load()
-    assert lib.kalm_version() == 100
+    assert lib.kalm_version() == 200
     # chunk = 0
     st = lib.kalm_chunk_pool(None, None, 1, 8, 64, 0, ops.KALM_BF16, None, None, None, None)
     assert st == ops.KALM_ERR_INVALID_ARG and b"chunk" in lib.kalm_last_error()
