@@ -230,6 +230,8 @@ def work_model(inp, sh, single=False):
         "q_linear_last": linear(P, H, qd, P * qd * e),
         # residual update: read and write the fp32 stream, write its bf16 copy
         "o_linear": linear(rows, qd, H, rows * H * (4 + 4 + (2 if e == 2 else 0))),
+        # first layer: the residual source is each query's first hidden rows, read once
+        "o_linear_first": linear(rows, qd, H, U * H * 4 + rows * H * (4 + (2 if e == 2 else 0))),
         "o_linear_last": linear(P, qd, H, P * H * 8),
         "cross_kv": dict(flops=2.0 * int(C.sum()) * H * 2 * kv, bytes=float(D * Cmax * (H + 2 * kv) * e)),
         "chunk_pool": dict(flops=0.0, bytes=float(int(dl.sum()) * H * e + D * Cmax * H * e + D * T + D * Cmax + 4 * D)),

@@ -134,10 +134,11 @@ __device__ __forceinline__ void zero_k_tail(bf16_t* tile, int k0, int K, int tid
 // into registers while the last k-tile is copied and multiplied, so their
 // memory latency is hidden instead of being paid after the k-loop.
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int OCC, bool PF_Y = false,
-          bool STREAM_X = GEMM_STREAM_X>
+          bool STREAM_X = GEMM_STREAM_X, bool RES = false>
 __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, int M, int K, int N,
-    void* __restrict__ Y, int epi, bf16_t* __restrict__ Ybf, const uint8_t* __restrict__ rmask) {
+    void* __restrict__ Y, int epi, bf16_t* __restrict__ Ybf, const uint8_t* __restrict__ rmask,
+    const float* __restrict__ Rsrc, const int32_t* __restrict__ Rrow, int64_t Rrows) {
   constexpr int NW = WM * WN;
   constexpr int CPS = DmaPlan<BM, NW, BK, true>::PER + DmaPlan<BN, NW, BK, false>::PER;  // copies per thread per k-tile
   static_assert(STAGES >= 2 && STAGES <= 5, "wait_dma_ktile handles at most three later k-tiles in flight");
@@ -204,6 +205,20 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
   constexpr int RPI = 64 / LPR;
   constexpr int NY = FM * (32 / RPI);  // 16-byte pieces of the fp32 stream per lane (PF_Y)
   const int prow = lane / LPR, pcol = (lane % LPR) * 4;
+  // the fp32 values the accumulate epilogue adds to: Y itself, or row Rrow[m]
+  // (row m when Rrow is null) of a separate [Rrows, N] source -- the residual
+  // stream started from a gathered row; an index outside [0, Rrows) gives NaN
+  // (RES: a separate instantiation, so the plain update keeps its loads unconditional)
+  auto res_at = [&](int m, int n) -> f32x4_t {
+    if constexpr (!RES) {
+      return ld_out((const f32x4_t*)((const float*)Y + (int64_t)m * N + n));
+    } else {
+      const int64_t src = Rrow ? (int64_t)Rrow[m] : (int64_t)m;
+      if (src < 0 || src >= Rrows)
+        return f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      return *(const f32x4_t*)(Rsrc + src * N + n);
+    }
+  };
   f32x4_t yold[PF_Y ? NY : 1];
   auto load_yold = [&]() {
 #pragma unroll
@@ -211,8 +226,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
 #pragma unroll
       for (int rr = 0; rr < 32; rr += RPI) {
         const int m = m0 + wm * WTM + j * 32 + rr + prow, n = n0 + wn * WTN + pcol;
-        yold[j * (32 / RPI) + rr / RPI] =
-            (m < M && n < N) ? ld_out((const f32x4_t*)((const float*)Y + (int64_t)m * N + n)) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        yold[j * (32 / RPI) + rr / RPI] = (m < M && n < N) ? res_at(m, n) : f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
   };
   for (int kt = 0; kt < STAGES - 1 && kt < nk; ++kt) issue(kt);
@@ -308,7 +322,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
           st_out((u32x2_t*)((bf16_t*)Y + off), u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
         } else {
           f32x4_t* yp = (f32x4_t*)((float*)Y + off);
-          if (epi == EPI_F32_ACC) v += PF_Y ? yold[j * (32 / RPI) + rr / RPI] : ld_out(yp);
+          if (epi == EPI_F32_ACC) v += PF_Y ? yold[j * (32 / RPI) + rr / RPI] : res_at(m, n);
           st_out(yp, v);
           if (Ybf) st_out((u32x2_t*)(Ybf + off), u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
         }
@@ -494,7 +508,9 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_persistent(
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ X,
                                                        const float* __restrict__ W, int M, int K,
                                                        int N, float* __restrict__ Y, int accumulate,
-                                                       const uint8_t* __restrict__ rmask) {
+                                                       const uint8_t* __restrict__ rmask,
+                                                       const float* __restrict__ Rsrc,
+                                                       const int32_t* __restrict__ Rrow, int64_t Rrows) {
   __shared__ float Xs[16][64 + 1];
   __shared__ float Ws[16][64 + 1];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
@@ -527,13 +543,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
     const int m = m0 + ty * 4 + i;
     if (m >= M) continue;
     const bool row_ok = rmask ? rmask[m] != 0 : true;
+    const int64_t src = Rrow ? (int64_t)Rrow[m] : (int64_t)m;
+    const bool src_ok = !Rsrc || (src >= 0 && src < Rrows);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + tx * 4 + j;
       if (n >= N) continue;
       float v = row_ok ? acc[i][j] : 0.f;
       float* yp = Y + (int64_t)m * N + n;
-      if (accumulate) v += *yp;
+      if (accumulate) v += !Rsrc ? *yp : (src_ok ? Rsrc[src * N + n] : __builtin_nanf(""));
       *yp = v;
     }
   }
@@ -544,16 +562,21 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 namespace kalm {
 
 void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, void* Y, bool y_f32,
-                        bool accumulate, bf16_t* Y_bf16, const uint8_t* rmask, hipStream_t s) {
+                        bool accumulate, bf16_t* Y_bf16, const uint8_t* rmask, hipStream_t s, const float* Rsrc,
+                        const int32_t* Rrow, int64_t Rrows) {
   const int epi = !y_f32 ? EPI_BF16 : (accumulate ? EPI_F32_ACC : EPI_F32);
   const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles >= 512 && epi == EPI_F32_ACC) {
     // residual update (reads and writes the fp32 stream): 128 x 128 tiles,
     // two workgroups per CU, so one's epilogue traffic overlaps the other's k-loop
     const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 64, 2, 4, GEMM_PF_Y>), dim3(tiles), dim3(512), 0, s, X, W, M,
-                       K, N, Y, epi, Y_bf16, rmask);
-  } else if (big_tiles >= 512 && GEMM_PERSIST) {
+    if (Rsrc)
+      hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 64, 2, 4, GEMM_PF_Y, GEMM_STREAM_X, true>), dim3(tiles),
+                         dim3(512), 0, s, X, W, M, K, N, Y, epi, Y_bf16, rmask, Rsrc, Rrow, Rrows);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 64, 2, 4, GEMM_PF_Y>), dim3(tiles), dim3(512), 0, s, X, W,
+                         M, K, N, Y, epi, Y_bf16, rmask, Rsrc, Rrow, Rrows);
+  } else if (big_tiles >= 512 && GEMM_PERSIST) {  // never EPI_F32_ACC: no residual source here
     // persistent 256 x 256 tiles, one workgroup per CU
     const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
     const int grid = tiles < 256 ? ((tiles + 7) / 8) * 8 : 256;
@@ -564,22 +587,27 @@ void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, v
     const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
 #ifdef GEMM_W16
     hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 4, 4, 64, 2, 4>), dim3(tiles), dim3(1024), 0, s, X, W, M, K, N,
-                       Y, epi, Y_bf16, rmask);
+                       Y, epi, Y_bf16, rmask, Rsrc, Rrow, Rrows);
 #else
     hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 64, 2, 1>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y,
-                       epi, Y_bf16, rmask);
+                       epi, Y_bf16, rmask, Rsrc, Rrow, Rrows);
 #endif
   } else {  // small problems: more, smaller tiles to fill the 256 CUs
     const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 32, 4, 1>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y,
-                       epi, Y_bf16, rmask);
+    if (Rsrc)
+      hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 32, 4, 1, false, GEMM_STREAM_X, true>), dim3(tiles),
+                         dim3(512), 0, s, X, W, M, K, N, Y, epi, Y_bf16, rmask, Rsrc, Rrow, Rrows);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 32, 4, 1>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y,
+                         epi, Y_bf16, rmask, Rsrc, Rrow, Rrows);
   }
 }
 
 void launch_linear_f32(const float* X, const float* W, int M, int K, int N, float* Y, bool accumulate,
-                       const uint8_t* rmask, hipStream_t s) {
+                       const uint8_t* rmask, hipStream_t s, const float* Rsrc, const int32_t* Rrow, int64_t Rrows) {
   const dim3 grid((N + 63) / 64, (M + 63) / 64);
-  hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, X, W, M, K, N, Y, accumulate ? 1 : 0, rmask);
+  hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, X, W, M, K, N, Y, accumulate ? 1 : 0, rmask, Rsrc, Rrow,
+                     Rrows);
 }
 
 }  // namespace kalm

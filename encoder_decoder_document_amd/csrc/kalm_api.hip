@@ -90,32 +90,55 @@ kalm_status kalm_chunk_pool(const void* x, const uint8_t* token_mask, int32_t D,
   return kalm::check_launch("kalm_chunk_pool");
 }
 
+static kalm_status linear_impl(const char* fn, const void* X, const void* W, int32_t M, int32_t K, int32_t N,
+                               kalm_dtype dt, void* Y, kalm_dtype y_dt, int32_t accumulate, void* Y_bf16,
+                               void* stream, const float* R = nullptr, const int32_t* r_row = nullptr,
+                               int64_t r_rows = 0);
+
 kalm_status kalm_linear(const void* X, const void* W, int32_t M, int32_t K, int32_t N, kalm_dtype dt,
                         void* Y, kalm_dtype y_dt, int32_t accumulate, void* Y_bf16, void* stream) {
+  return linear_impl("kalm_linear", X, W, M, K, N, dt, Y, y_dt, accumulate, Y_bf16, stream);
+}
+
+kalm_status kalm_linear_residual(const void* X, const void* W, int32_t M, int32_t K, int32_t N, kalm_dtype dt,
+                                 const float* R, const int32_t* r_row, int64_t r_rows, float* Y, void* Y_bf16,
+                                 void* stream) {
   kalm::g_err[0] = 0;
-  KALM_REQUIRE(dt == KALM_F32 || dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "kalm_linear: dtype %d", (int)dt);
-  KALM_REQUIRE(y_dt == KALM_F32 || y_dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "kalm_linear: y dtype %d", (int)y_dt);
-  KALM_REQUIRE(M >= 0 && K >= 1 && N >= 1, KALM_ERR_INVALID_ARG, "kalm_linear: bad sizes M=%d K=%d N=%d", M, K, N);
-  KALM_REQUIRE(M == 0 || (X && W && Y), KALM_ERR_INVALID_ARG, "kalm_linear: null pointer");
-  KALM_REQUIRE(!accumulate || y_dt == KALM_F32, KALM_ERR_UNSUPPORTED, "kalm_linear: accumulate needs an F32 Y");
-  KALM_REQUIRE(!Y_bf16 || y_dt == KALM_F32, KALM_ERR_UNSUPPORTED, "kalm_linear: Y_bf16 copy needs an F32 Y");
+  KALM_REQUIRE(M == 0 || R, KALM_ERR_INVALID_ARG, "kalm_linear_residual: null residual source");
+  KALM_REQUIRE(r_rows >= 0 && (r_row || r_rows >= M), KALM_ERR_INVALID_ARG,
+               "kalm_linear_residual: without r_row the source needs M rows");
+  KALM_REQUIRE(ALIGNED16(R), KALM_ERR_INVALID_ARG, "kalm_linear_residual: R must be 16-byte aligned");
+  return linear_impl("kalm_linear_residual", X, W, M, K, N, dt, Y, KALM_F32, 1, Y_bf16, stream, R, r_row,
+                     r_row ? r_rows : M);
+}
+
+static kalm_status linear_impl(const char* fn, const void* X, const void* W, int32_t M, int32_t K, int32_t N,
+                               kalm_dtype dt, void* Y, kalm_dtype y_dt, int32_t accumulate, void* Y_bf16,
+                               void* stream, const float* R, const int32_t* r_row, int64_t r_rows) {
+  kalm::g_err[0] = 0;
+  KALM_REQUIRE(dt == KALM_F32 || dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)dt);
+  KALM_REQUIRE(y_dt == KALM_F32 || y_dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "%s: y dtype %d", fn, (int)y_dt);
+  KALM_REQUIRE(M >= 0 && K >= 1 && N >= 1, KALM_ERR_INVALID_ARG, "%s: bad sizes M=%d K=%d N=%d", fn, M, K, N);
+  KALM_REQUIRE(M == 0 || (X && W && Y), KALM_ERR_INVALID_ARG, "%s: null pointer", fn);
+  KALM_REQUIRE(!accumulate || y_dt == KALM_F32, KALM_ERR_UNSUPPORTED, "%s: accumulate needs an F32 Y", fn);
+  KALM_REQUIRE(!Y_bf16 || y_dt == KALM_F32, KALM_ERR_UNSUPPORTED, "%s: Y_bf16 copy needs an F32 Y", fn);
   KALM_REQUIRE(ALIGNED16(X) && ALIGNED16(W) && ALIGNED16(Y) && ALIGNED16(Y_bf16), KALM_ERR_INVALID_ARG,
-               "kalm_linear: pointers must be 16-byte aligned");
+               "%s: pointers must be 16-byte aligned", fn);
   if (dt == KALM_BF16) {
-    KALM_REQUIRE(K % 8 == 0 && N % 8 == 0, KALM_ERR_UNSUPPORTED, "kalm_linear: bf16 needs K%%8==0 and N%%8==0 (K=%d N=%d)", K, N);
+    KALM_REQUIRE(K % 8 == 0 && N % 8 == 0, KALM_ERR_UNSUPPORTED, "%s: bf16 needs K%%8==0 and N%%8==0 (K=%d N=%d)", fn, K, N);
   } else {
-    KALM_REQUIRE(y_dt == KALM_F32 && !Y_bf16, KALM_ERR_UNSUPPORTED, "kalm_linear: F32 inputs need an F32 Y and no bf16 copy");
-    KALM_REQUIRE(K % 4 == 0 && N % 4 == 0, KALM_ERR_UNSUPPORTED, "kalm_linear: f32 needs K%%4==0 and N%%4==0");
+    KALM_REQUIRE(y_dt == KALM_F32 && !Y_bf16, KALM_ERR_UNSUPPORTED, "%s: F32 inputs need an F32 Y and no bf16 copy", fn);
+    KALM_REQUIRE(K % 4 == 0 && N % 4 == 0, KALM_ERR_UNSUPPORTED, "%s: f32 needs K%%4==0 and N%%4==0", fn);
   }
   KALM_DEVICE_OR_RETURN();
   if (M == 0) return KALM_OK;
   if (dt == KALM_BF16)
     kalm::launch_linear_bf16((const bf16_t*)X, (const bf16_t*)W, M, K, N, Y, y_dt == KALM_F32, accumulate != 0,
-                             (bf16_t*)Y_bf16, nullptr, (hipStream_t)stream);
+                             (bf16_t*)Y_bf16, nullptr, (hipStream_t)stream, R, r_row, r_rows);
   else
     kalm::launch_linear_f32((const float*)X, (const float*)W, M, K, N, (float*)Y, accumulate != 0, nullptr,
-                            (hipStream_t)stream);
-  return kalm::check_launch("kalm_linear");
+                            (hipStream_t)stream, R, r_row, r_rows);
+  return kalm::check_launch(fn);
 }
 
 kalm_status kalm_cross_kv(const void* pooled, const uint8_t* chunk_mask, int32_t D, int32_t Cmax, int32_t H,

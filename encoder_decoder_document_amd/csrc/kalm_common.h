@@ -121,10 +121,14 @@ void launch_chunk_pool(const void* x, const uint8_t* mask, int D, int T, int H, 
 void launch_pair_layout(const int32_t* lq, int nQ, int nD, int32_t* cu_q, int32_t* doc_of_pair,
                         int32_t* final_row, int32_t* h0_row, int64_t rows, int32_t* h0_final, int32_t* cu_u,
                         hipStream_t s);
+// Linear layers.  With accumulate, Y (fp32) += X W^T, or -- given Rsrc -- Y = R + X W^T where row m of R is
+// Rsrc[Rrow[m]] (Rsrc[m] when Rrow is null), an index outside [0, Rrows) giving NaN.
 void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, void* Y, bool y_f32,
-                        bool accumulate, bf16_t* Y_bf16, const uint8_t* row_mask, hipStream_t s);
+                        bool accumulate, bf16_t* Y_bf16, const uint8_t* row_mask, hipStream_t s,
+                        const float* Rsrc = nullptr, const int32_t* Rrow = nullptr, int64_t Rrows = 0);
 void launch_linear_f32(const float* X, const float* W, int M, int K, int N, float* Y, bool accumulate,
-                       const uint8_t* row_mask, hipStream_t s);
+                       const uint8_t* row_mask, hipStream_t s, const float* Rsrc = nullptr,
+                       const int32_t* Rrow = nullptr, int64_t Rrows = 0);
 void launch_merged_attn_bf16(const bf16_t* Q, int64_t q_ld, const bf16_t* Ks, const bf16_t* Vs,
                              int64_t kv_ld, const int32_t* cu_q, int P, int64_t q_rows, int64_t kv_rows,
                              int64_t o_rows, int mode, int max_lq, const bf16_t* Kc, const bf16_t* Vc,

@@ -52,6 +52,7 @@ _SIGS = {
     "kalm_gated_gelu": (_i32, [_c_p, _i32, _i64, _i64, _i32, _c_p, _i64, _c_p]),
     "kalm_yesno_score": (_i32, [_c_p, _i32, _i64, _i64, _c_p, _i32, _i32, _c_p, _i32, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "kalm_linear": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _i32, _c_p, _i32, _i32, _c_p, _c_p]),
+    "kalm_linear_residual": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _i32, _c_p, _c_p, _i64, _c_p, _c_p, _c_p]),
     "kalm_gather_rows": (_i32, [_c_p, _c_p, _i64, _i32, _i64, _c_p, _c_p, _c_p]),
     "kalm_rank_topn": (_i32, [_c_p, _i32, _i32, _i32, _c_p, _c_p, _c_p]),
 }
@@ -364,6 +365,20 @@ def kalm_linear(X: torch.Tensor, W: torch.Tensor, Y: Optional[torch.Tensor] = No
         Y = torch.empty(M, N, dtype=y_dtype or X.dtype, device=X.device)
     _check("kalm_linear", load().kalm_linear(_ptr(X), _ptr(W), M, K, N, _dt(X), _ptr(Y), _dt(Y),
                                             1 if accumulate else 0, _ptr(Y_bf16), _stream(stream)))
+    return Y
+
+
+def kalm_linear_residual(X: torch.Tensor, W: torch.Tensor, R: torch.Tensor, r_row: Optional[torch.Tensor],
+                         Y: Optional[torch.Tensor] = None, Y_bf16: Optional[torch.Tensor] = None, stream=None):
+    """Y = R[r_row] + X W^T (fp32; R row m when r_row is None); optional bf16 copy."""
+    _contig(X, W, R, r_row, Y, Y_bf16)
+    M, K = X.shape
+    N = W.shape[0]
+    if Y is None:
+        Y = torch.empty(M, N, dtype=torch.float32, device=X.device)
+    _check("kalm_linear_residual", load().kalm_linear_residual(
+        _ptr(X), _ptr(W), M, K, N, _dt(X), _ptr(R), _ptr(r_row), R.shape[0], _ptr(Y), _ptr(Y_bf16),
+        _stream(stream)))
     return Y
 
 

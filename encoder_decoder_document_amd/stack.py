@@ -8,7 +8,9 @@ itself only enqueues libkalm calls on the current stream:
   every query) -> kalm_gather_rows (each pair's residual stream starts from its
   query's first hidden state) -> per layer: kalm_linear (fused Q/K/V), kalm_merged_attn,
   kalm_linear (output projection added to the fp32 residual, bf16 copy for the
-  next layer) -> kalm_yesno_score.
+  next layer) -> kalm_yesno_score.  With ``prune`` the residual start is fused
+  into the first layer's output projection (kalm_linear_residual adds it to the
+  gathered first hidden states).
 
 With ``prune`` (the default) two layers do less work for the same result:
   * layer 1: every passage of a query still holds the query's own first hidden
@@ -227,7 +229,9 @@ def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_
     # one pruned layer is both the first and the last: only the queries' own
     # rows and the pairs' final rows are ever computed
     single = prune and b.n_layers == 1
-    if not single:
+    if not prune:
+        # residual start: every pair row from its query's first hidden state (the
+        # pruned first layer instead adds its projection to those rows directly)
         with rec("gather_rows"):
             ops.kalm_gather_rows(b.h0, B["h0_row"], dst=B["h"], dst_bf16=B["hb"] if bf else None, stream=stream)
     qkv = B["qkv"]
@@ -303,6 +307,12 @@ def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_
             with rec("merged_attn"):
                 ops.kalm_merged_attn(Q, Ks, Vs, B["cu_q"], b.max_lq, kvc[:, :kv], kvc[:, kv:], B["chunk_mask"],
                                      B["doc_of_pair"], b.nq, b.nkv, b.d, scale=scale, out=B["o"], stream=stream)
+        if prune and l == 0:
+            # residual start fused: h = h0[query row of each pair row] + O Wo^T
+            with rec("o_linear_first"):
+                ops.kalm_linear_residual(B["o"], b.Wo[l], b.h0, B["h0_row"], Y=B["h"],
+                                         Y_bf16=B["hb"] if bf else None, stream=stream)
+            continue
         with rec("o_linear"):
             ops.kalm_linear(B["o"], b.Wo[l], Y=B["h"], accumulate=True, Y_bf16=B["hb"] if bf else None,
                             stream=stream)
@@ -345,7 +355,7 @@ def decoder_model(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, 
             with rec("mlp_down" + tag):
                 ops.kalm_linear(a, M["Wd"][l], Y=hv, accumulate=True, stream=stream)
 
-    if not single:
+    if not prune:
         with rec("gather_rows"):
             ops.kalm_gather_rows(b.h0, B["h0_row"], dst=B["h"], stream=stream)
     qkv = B["qkv"]
@@ -417,8 +427,13 @@ def decoder_model(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, 
             with rec("merged_attn"):
                 ops.kalm_merged_attn(qkv[:, :qd], qkv[:, qd:qd + kv], qkv[:, qd + kv:], B["cu_q"], b.max_lq,
                                      *cross[:4], b.nq, b.nkv, b.d, scale=scale, out=B["o"], stream=stream)
-        with rec("o_linear"):
-            ops.kalm_linear(B["o"], b.Wo[l], Y=B["h"], accumulate=True, stream=stream)
+        if prune and l == 0:
+            # residual start fused: h = h0[query row of each pair row] + O Wo^T
+            with rec("o_linear_first"):
+                ops.kalm_linear_residual(B["o"], b.Wo[l], b.h0, B["h0_row"], Y=B["h"], stream=stream)
+        else:
+            with rec("o_linear"):
+                ops.kalm_linear(B["o"], b.Wo[l], Y=B["h"], accumulate=True, stream=stream)
         mlp(B["h"], l)
     if not last_pruned:
         with rec("gather_final_rows"):

@@ -345,6 +345,24 @@ kalm_status kalm_linear(const void* X, const void* W, int32_t M, int32_t K, int3
                         void* stream);
 
 /*
+ * kalm_linear_residual -- the residual update of a layer whose residual stream
+ * starts from gathered rows: Y[m] = R[r_row[m]] + X[m] . W^T (fp32; R[m] when
+ * r_row is NULL), with the optional bf16 copy Y_bf16 of Y.  The first decoder
+ * layer of a batch in which every passage of a query starts from the query's
+ * own first hidden states ([MLX] What this is: the decoder models the query;
+ * [MLX] Speed: one passage set, many queries) adds its output projection to
+ * those rows directly, with no materialised copy of them per pair.
+ *   R      [r_rows, N] float, contiguous; r_row [M] int32 (nullable; without
+ *          it R needs M rows); an index outside [0, r_rows) gives NaN in that
+ *          row of Y
+ *   Y      [M, N] float out; must not overlap R unless r_row is NULL and R == Y
+ * Other arguments as kalm_linear (accumulate into an F32 Y).
+ */
+kalm_status kalm_linear_residual(const void* X, const void* W, int32_t M, int32_t K, int32_t N,
+                                 kalm_dtype dt, const float* R, const int32_t* r_row, int64_t r_rows,
+                                 float* Y, void* Y_bf16, void* stream);
+
+/*
  * a5 -- row gather that starts the residual stream of every pair from its
  * query's first-layer hidden state (all passages of a query share it).
  *   dst[m] = src[idx[m]]   for m < M   (float rows of length H)

@@ -106,6 +106,11 @@ def test_invalid_arguments_rejected_before_launch():
     assert st == ops.KALM_ERR_INVALID_ARG and b"n_split" in lib.kalm_last_error()
     st = lib.kalm_merged_attn_split(*args[:20], ops.KALM_F32, *args[21:], 2, 16, need, None)
     assert st == ops.KALM_ERR_UNSUPPORTED
+    # gathered residual: no source; without an index the source needs M rows
+    st = lib.kalm_linear_residual(16, 16, 10, 64, 64, ops.KALM_BF16, None, None, 10, 16, None, None)
+    assert st == ops.KALM_ERR_INVALID_ARG and b"residual source" in lib.kalm_last_error()
+    st = lib.kalm_linear_residual(16, 16, 10, 64, 64, ops.KALM_BF16, 16, None, 9, 16, None, None)
+    assert st == ops.KALM_ERR_INVALID_ARG and b"M rows" in lib.kalm_last_error()
     # ranking: top_n larger than the passages; too many passages for one workgroup
     st = lib.kalm_rank_topn(None, 1, 10, 11, None, None, None)
     assert st == ops.KALM_ERR_INVALID_ARG and b"top_n" in lib.kalm_last_error()

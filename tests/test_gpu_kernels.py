@@ -153,6 +153,39 @@ def test_linear_parity(M, K, N, mode):
         assert_close(got, ref, *F32_TOL, "Y f32 path")
 
 
+@pytest.mark.parametrize("M,K,N,bf,indexed", [(300, 1024, 1152, True, True), (40003, 1024, 1152, True, True),
+                                               (22093, 1024, 1152, True, False), (33, 36, 20, False, True)])
+def test_linear_residual_parity(M, K, N, bf, indexed):
+    """Y = R[r_row] + X W^T: the residual update starting from gathered rows
+    (big and small tile paths, fp32 path); out-of-range indices give NaN rows."""
+    _announce(f"linear_residual M={M} K={K} N={N} bf16={bf} indexed={indexed}")
+    X = synth.normal(40 + M, (M, K), 1.0, bf)
+    W = synth.normal(41 + M, (N, K), 0.02, bf)
+    dt = torch.bfloat16 if bf else torch.float32
+    rows = 97 if indexed else M
+    R = synth.normal(42 + M, (rows, N), 1.0, False)
+    idx = synth.integers(43 + M, 0, rows - 1, M) if indexed else None
+    if indexed:
+        idx[[1, M // 2]] = [rows, -1]  # out of range: NaN rows
+    Yb = torch.empty(M, N, dtype=torch.bfloat16, device="cuda") if bf else None
+    Y = ops.kalm_linear_residual(to_dev(X, dt), to_dev(W, dt), to_dev(R, torch.float32),
+                                 to_dev(idx, torch.int32) if indexed else None, Y_bf16=Yb)
+    torch.cuda.synchronize()
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    base = R[np.clip(idx, 0, rows - 1)] if indexed else R
+    ref = ref + base
+    got = to_np(Y)
+    if indexed:
+        bad = np.zeros(M, bool)
+        bad[[1, M // 2]] = True
+        assert np.isnan(got[bad]).all()
+        got, ref = got[~bad], ref[~bad]
+    assert_close(got, ref, *((1e-3, 1e-4) if bf else (1e-4, 1e-4)), "Y = R[idx] + XW^T")
+    if Yb is not None:  # NaN rows included
+        assert np.array_equal(to_np(Yb), to_np(Y.to(torch.bfloat16)), equal_nan=True), \
+            "bf16 copy is RNE of the fp32 result"
+
+
 # ------------------------------------------------------------------ a3 merged attention
 def _attn_case(seed, lqs, docs_c, Cmax, nq, nkv, d, bf16, std=0.7, general=False):
     P = len(lqs)
