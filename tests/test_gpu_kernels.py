@@ -666,6 +666,51 @@ def test_gated_gelu_parity(M, I, bf16):
     assert_close(to_np(A), ref, *(BF16_TOL if bf16 else F32_TOL), "gated_gelu")
 
 
+# ------------------------------------------------------------------ empty inputs
+def test_zero_sized_calls_are_valid_noops():
+    """Every entry point accepts an empty batch (no pairs, rows, passages or
+    sequences) and returns OK without touching its outputs."""
+    _announce("zero-sized calls")
+    dev = "cuda"
+    bf, f, i32, u8 = torch.bfloat16, torch.float32, torch.int32, torch.uint8
+    lay = ops.kalm_pair_layout(torch.zeros(0, dtype=i32, device=dev), 5, rows=0)
+    torch.cuda.synchronize()
+    assert lay["cu_q"].cpu().tolist() == [0] and lay["cu_u"].cpu().tolist() == [0]
+    pooled, cm, nc = ops.kalm_chunk_pool(torch.zeros(0, 8, 64, dtype=bf, device=dev),
+                                         torch.zeros(0, 8, dtype=u8, device=dev))
+    assert pooled.shape[0] == 0
+    W = torch.zeros(512, 64, dtype=bf, device=dev)
+    assert ops.kalm_cross_kv(pooled, cm, W).shape[0] == 0
+    X = torch.zeros(0, 64, dtype=bf, device=dev)
+    assert ops.kalm_linear(X, W).shape[0] == 0
+    Yf = torch.full((4, 512), 7.0, dtype=f, device=dev)
+    ops.kalm_linear_residual(X, W, Yf, None, Y=Yf[:0])
+    Q = torch.zeros(0, 1024, dtype=bf, device=dev)
+    KV = torch.zeros(0, 256, dtype=bf, device=dev)
+    Kc = torch.zeros(4 * 16, 256, dtype=bf, device=dev)
+    cm4 = torch.ones(4, 16, dtype=u8, device=dev)
+    cu0 = torch.zeros(1, dtype=i32, device=dev)
+    dop0 = torch.zeros(0, dtype=i32, device=dev)
+    assert ops.kalm_merged_attn(Q, KV, KV, cu0, 0, Kc, Kc, cm4, dop0, 4, 1, 256).shape[0] == 0
+    o_s, l_s = ops.kalm_self_attn_partial(Q, KV, KV, cu0, 0, 4, 1, 256)
+    assert o_s.shape[0] == 0
+    assert ops.kalm_merged_attn_resume(Q, o_s, l_s, cu0, 0, Kc, Kc, cm4, dop0, 4, 1, 256, ops.ROWS_ALL,
+                                       0).shape[0] == 0
+    assert ops.kalm_merged_attn_split(Q, o_s, l_s, cu0, 0, Kc, Kc, cm4, dop0, 4, 1, 256, ops.ROWS_ALL, 0,
+                                      4).shape[0] == 0
+    outs = ops.kalm_yesno_score(torch.zeros(3, 64, dtype=f, device=dev), dop0, torch.zeros(2, 64, dtype=f, device=dev))
+    assert all(o.numel() == 0 for o in outs)
+    idx, sc = ops.kalm_rank_topn(torch.zeros(0, 10, dtype=f, device=dev), 3)
+    assert idx.shape == (0, 3)
+    assert ops.kalm_gather_rows(torch.zeros(3, 64, dtype=f, device=dev), dop0).shape[0] == 0
+    assert ops.kalm_rms_norm(torch.zeros(0, 64, dtype=f, device=dev), torch.ones(64, dtype=f, device=dev)).shape[0] == 0
+    Xr = torch.full((2, 64), 3.0, dtype=f, device=dev)
+    ops.kalm_rope(Xr, 0, 2, 32, cu0, 0)
+    assert ops.kalm_gated_gelu(torch.zeros(0, 64, dtype=bf, device=dev)).shape[0] == 0
+    torch.cuda.synchronize()
+    assert (Yf == 7.0).all() and (Xr == 3.0).all()
+
+
 # ------------------------------------------------------------------ a4 score
 @pytest.mark.parametrize("H,hb,wb", [(640, False, True), (1152, True, True), (64, False, False)])
 def test_yesno_score_parity(H, hb, wb):
