@@ -314,7 +314,7 @@ def pool_long(torch, ops, reps=20):
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its own "
+        print("bench.py measures one GPU: the library has no multi-GPU path (each GPU would run its own "
               "passage shard independently); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
