@@ -312,6 +312,41 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   // multiplies a finite value.
   auto issue = [&](int v, bool is_k) {
     const bool self = v < n_st;
+    if constexpr (RPW == 8) {
+      // the four copies of a wave (4-wave workgroups), branch-free: row offsets
+      // grow by two rows per copy (clamped to the last self key, or the donor
+      // chunk for masked cross rows), the swizzled chunk of row key0 + 2j added
+      // per lane, and one M0 save/restore for the four (3.5% faster than a
+      // copy at a time with per-row branches at the Small shape)
+      const uint32_t so = (is_k ? klds0 + (uint32_t)((v % KR) * TILE_B) : vlds0 + (uint32_t)((v % VR) * TILE_B)) +
+                          dslab;
+      int key0 = dkey0;
+      asm volatile("" : "+v"(key0));
+      const uint32_t c4 = (uint32_t)(__lane_id() & 31) << 4;
+      uint32_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t kj = (uint32_t)(key0 + 2 * j);
+        o[j] = is_k ? (c4 ^ ((kj & 15u) << 4)) : (c4 ^ ((kj & 3u) << 6));
+      }
+      uint64_t base;
+      if (self) {
+        base = is_k ? ks_base : vs_base;
+        const uint32_t r0 = (uint32_t)(v * BKV + key0) * kv_ld2, rmax = (uint32_t)(Lq - 1) * kv_ld2;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] += min(r0 + (uint32_t)(2 * j) * kv_ld2, rmax);
+      } else {
+        base = is_k ? kc_base : vc_base;
+        const int t = v - n_st + ct0;
+        const uint32_t bits = cm_word(t);
+        const uint32_t r0 = (uint32_t)(t * BKV + key0) * c_ld2, rd = (uint32_t)donor * c_ld2;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[j] += ((bits >> (key0 + 2 * j)) & 1u) ? r0 + (uint32_t)(2 * j) * c_ld2 : rd;
+      }
+      dma16x4(base, o[0], o[1], o[2], o[3], so);
+      return;
+    }
     const int kb = self ? v * BKV : (v - n_st + ct0) * BKV;
     const uint32_t ld2 = self ? kv_ld2 : c_ld2;
     const uint64_t base = is_k ? (self ? ks_base : kc_base) : (self ? vs_base : vc_base);

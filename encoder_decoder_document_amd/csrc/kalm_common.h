@@ -81,6 +81,28 @@ __device__ __forceinline__ void dma16(uint64_t sbase, uint32_t voff, uint32_t ld
         : "memory");
 }
 
+// Four direct-to-LDS copies into LDS bases lds, lds + 1024, lds + 2048 and
+// lds + 3072 (16 bytes per lane each), with one save and restore of M0.
+__device__ __forceinline__ void dma16x4(uint64_t sbase, uint32_t o0, uint32_t o1, uint32_t o2, uint32_t o3,
+                                        uint32_t lds) {
+  uint32_t saved;
+  const uint32_t l1 = lds + 1024u, l2 = lds + 2048u, l3 = lds + 3072u;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "global_load_lds_dwordx4 %1, %9\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "global_load_lds_dwordx4 %2, %9\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "global_load_lds_dwordx4 %3, %9\n\t"
+      "s_mov_b32 m0, %8\n\t"
+      "global_load_lds_dwordx4 %4, %9\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(o0), "v"(o1), "v"(o2), "v"(o3), "s"(lds), "s"(l1), "s"(l2), "s"(l3), "s"(sbase)
+      : "memory");
+}
+
 // Wait until the copies of the oldest in-flight k-tile are done: at most
 // `later` k-tiles (CPS copies each) issued after it may still be outstanding.
 template <int CPS>
