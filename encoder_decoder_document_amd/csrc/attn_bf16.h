@@ -77,6 +77,21 @@ __device__ __forceinline__ u32x2_t lds_tr_at(uint32_t addr) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
+// The two halves of a wave exchanged (gfx950 v_permlane32_swap): for every
+// lane, {a, b} holds the value of lane l and of lane l ^ 32, in some order --
+// enough for a symmetric combination such as a max or a sum, without the LDS
+// crossbar a general lane shuffle goes through.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
 // 16-byte LDS read at a byte address.
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 __device__ __forceinline__ bf16x8_t lds_read16(uint32_t addr) { return *(const lds_bf16x8_t*)(size_t)addr; }
@@ -483,7 +498,7 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
       float tmax = sacc[u][0];
 #pragma unroll
       for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, sacc[u][e]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;  // scale > 0 commutes with max
+      tmax = max_xor32(tmax) * scale_log2;  // the row's two halves; scale > 0 commutes with max
       // lazy rescale: the running max moves only when some row's tile max
       // exceeds it by more than LAZY (log2 units); the first tile (m_run =
       // -inf, accumulator 0) always takes this branch with alpha = 0.  Tile 0
@@ -545,7 +560,7 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   }
 #pragma unroll
   for (int u = 0; u < RT; ++u) {
-    const float l_tot = l_run[u] + __shfl_xor(l_run[u], 32, 64);
+    const float l_tot = sum_xor32(l_run[u]);
     // an empty share of the cross keys (PART 3 only: every other walk has a
     // visible key) is the zero partial o = 0, lse = -inf
     const float inv = bad_doc ? __builtin_nanf("") : (PART == 3 && l_tot == 0.f) ? 0.f : 1.f / l_tot;
