@@ -321,63 +321,76 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   const int dkey0 = RPW * wave + (lane >> 5);
   const uint32_t dslab = __builtin_amdgcn_readfirstlane(wave * RPW * (HD * 2));
 
-  // copy the K (or V) rows of tile v into ring slot v % KR (v % VR).  Key rows
-  // that do not exist (past the pair / the passage) or are masked are fetched
-  // from a valid row instead: their logits are masked to -inf, so p = 0
-  // multiplies a finite value.
-  auto issue = [&](int v, bool is_k) {
+  // copy the K and V rows of tile v into ring slot v % KR.  Key rows that do
+  // not exist (past the pair / the passage) or are masked are fetched from a
+  // valid row instead: their logits are masked to -inf, so p = 0 multiplies a
+  // finite value.
+  static_assert(KR == VR, "K and V tiles are copied together");
+  auto issue_kv = [&](int v) {
     const bool self = v < n_st;
+    const uint32_t so = klds0 + (uint32_t)((v % KR) * TILE_B) + dslab;  // the V slab is KR tiles further
     if constexpr (RPW == 8) {
-      // the four copies of a wave (4-wave workgroups), branch-free: row offsets
-      // grow by two rows per copy (clamped to the last self key, or the donor
-      // chunk for masked cross rows), the swizzled chunk of row key0 + 2j added
-      // per lane, and one M0 save/restore for the four (3.5% faster than a
-      // copy at a time with per-row branches at the Small shape)
-      const uint32_t so = (is_k ? klds0 + (uint32_t)((v % KR) * TILE_B) : vlds0 + (uint32_t)((v % VR) * TILE_B)) +
-                          dslab;
+      // the eight copies of a wave (4-wave workgroups), branch-free on full
+      // tiles: copy j takes key row key0 + 2j, whose swizzled chunk is, with
+      // key0 = 8 wave + g (bits 1..2 clear), ck0 ^ 32 j in K and cv0 ^ 128 (j & 1)
+      // in V; one M0 save/restore for the eight
       int key0 = dkey0;
-      asm volatile("" : "+v"(key0));
+      asm volatile("" : "+v"(key0));  // recompute the per-lane parts here instead of holding them
       const uint32_t c4 = (uint32_t)(__lane_id() & 31) << 4;
-      uint32_t o[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t kj = (uint32_t)(key0 + 2 * j);
-        o[j] = is_k ? (c4 ^ ((kj & 15u) << 4)) : (c4 ^ ((kj & 3u) << 6));
-      }
-      uint64_t base;
+      const uint32_t ck0 = c4 ^ ((uint32_t)(key0 & 15) << 4), cv0 = c4 ^ ((uint32_t)(key0 & 3) << 6);
+      uint32_t row[4];
+      uint64_t kb, vb;
       if (self) {
-        base = is_k ? ks_base : vs_base;
-        const uint32_t r0 = (uint32_t)(v * BKV + key0) * kv_ld2, rmax = (uint32_t)(Lq - 1) * kv_ld2;
+        kb = ks_base;
+        vb = vs_base;
+        const uint32_t r0 = (uint32_t)(v * BKV + key0) * kv_ld2;
+        if (v * BKV + BKV <= Lq) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] += min(r0 + (uint32_t)(2 * j) * kv_ld2, rmax);
+          for (int j = 0; j < 4; ++j) row[j] = r0 + (uint32_t)(2 * j) * kv_ld2;
+        } else {  // the ragged last self tile: rows past the pair clamped to its last key
+          const uint32_t rmax = (uint32_t)(Lq - 1) * kv_ld2;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) row[j] = min(r0 + (uint32_t)(2 * j) * kv_ld2, rmax);
+        }
       } else {
-        base = is_k ? kc_base : vc_base;
+        kb = kc_base;
+        vb = vc_base;
         const int t = v - n_st + ct0;
         const uint32_t bits = cm_word(t);
-        const uint32_t r0 = (uint32_t)(t * BKV + key0) * c_ld2, rd = (uint32_t)donor * c_ld2;
+        const uint32_t r0 = (uint32_t)(t * BKV + key0) * c_ld2;
+        if (bits == 0xffffffffu) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          o[j] += ((bits >> (key0 + 2 * j)) & 1u) ? r0 + (uint32_t)(2 * j) * c_ld2 : rd;
+          for (int j = 0; j < 4; ++j) row[j] = r0 + (uint32_t)(2 * j) * c_ld2;
+        } else {  // masked chunk rows fetched from the donor chunk
+          const uint32_t rd = (uint32_t)donor * c_ld2, bl = bits >> key0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) row[j] = ((bl >> (2 * j)) & 1u) ? r0 + (uint32_t)(2 * j) * c_ld2 : rd;
+        }
       }
-      dma16x4(base, o[0], o[1], o[2], o[3], so);
+      dma16x8<(uint32_t)(KR * TILE_B)>(kb, row[0] + ck0, row[1] + (ck0 ^ 32u), row[2] + (ck0 ^ 64u),
+                                       row[3] + (ck0 ^ 96u), vb, row[0] + cv0, row[1] + (cv0 ^ 128u), row[2] + cv0,
+                                       row[3] + (cv0 ^ 128u), so);
       return;
     }
     const int kb = self ? v * BKV : (v - n_st + ct0) * BKV;
     const uint32_t ld2 = self ? kv_ld2 : c_ld2;
-    const uint64_t base = is_k ? (self ? ks_base : kc_base) : (self ? vs_base : vc_base);
     const uint32_t bits = self ? 0u : cm_word(v - n_st + ct0);
-    const uint32_t so = (is_k ? klds0 + (uint32_t)((v % KR) * TILE_B) : vlds0 + (uint32_t)((v % VR) * TILE_B)) + dslab;
     int key0 = dkey0;
     asm volatile("" : "+v"(key0));  // recompute the per-row offsets here instead of holding them
 #pragma unroll
-    for (int j = 0; j < RPW / 2; ++j) {
-      const int key = key0 + 2 * j;
-      int row;
-      if (self) row = min(kb + key, Lq - 1);
-      else row = ((bits >> key) & 1u) ? kb + key : donor;
-      const uint32_t ro = (uint32_t)row * ld2;
-      const int c = __lane_id() & 31;
-      dma16(base, ro + (uint32_t)((is_k ? k_swz(key, c) : v_swz(key, c)) << 4), so + j * 1024);
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint64_t base = kv == 0 ? (self ? ks_base : kc_base) : (self ? vs_base : vc_base);
+#pragma unroll
+      for (int j = 0; j < RPW / 2; ++j) {
+        const int key = key0 + 2 * j;
+        int row;
+        if (self) row = min(kb + key, Lq - 1);
+        else row = ((bits >> key) & 1u) ? kb + key : donor;
+        const uint32_t ro = (uint32_t)row * ld2;
+        const int c = __lane_id() & 31;
+        dma16(base, ro + (uint32_t)((kv == 0 ? k_swz(key, c) : v_swz(key, c)) << 4),
+              so + (uint32_t)(kv * KR * TILE_B) + j * 1024);
+      }
     }
   };
 
@@ -399,16 +412,11 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   const uint32_t vx = vlds0 + vkey * (HD * 2) + 64 * (vkey & 3) + 16 * (vdim0 >> 3) +
                       2 * (vdim0 & 7);
 
-  // Copy schedule (per wave, in issue order): V(0), K(0) .. K(KR-2), then at
-  // tile v: V(v + VR - 1), K(v + KR - 1).  When tile v starts, the copies
-  // still allowed in flight are the K tiles issued after V(v): K(v+1) ..
-  // K(v+KR-VR) -- none when the rings are equally deep.
+  // Copy schedule (per wave): tiles 0 .. KR-2 before the loop, then at tile
+  // v the K and V rows of tile v + KR - 1.  When tile v starts, the copies
+  // still allowed in flight are those of the tiles issued after it.
   constexpr int CPT = RPW / 2;  // copy instructions per wave per K (or V) tile
-  for (int v = 0; v < VR - 1 && v < n_tiles; ++v) {
-    issue(v, false);
-    issue(v, true);
-  }
-  for (int v = VR - 1; v < KR - 1 && v < n_tiles; ++v) issue(v, true);
+  for (int v = 0; v < KR - 1 && v < n_tiles; ++v) issue_kv(v);
   // Make the Q loads complete here, visibly to the compiler: its wait-count
   // pass does not see the asm copies, and would otherwise keep waiting for
   // "the Q loads" inside the tile loop with vmcnt values that, on the
@@ -427,11 +435,9 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
     }
   }
   for (int v = 0; v < n_tiles; ++v) {
-    if (KR == VR) wait_dma_ktile<2 * CPT>(min(n_tiles - 1 - v, VR - 2));
-    else wait_dma_ktile<CPT>(min(n_tiles - 1 - v, KR - VR));  // K(v+1) may still be in flight
+    wait_dma_ktile<2 * CPT>(min(n_tiles - 1 - v, KR - 2));
     __syncthreads();  // tile v visible; the slots of tile v-1 are free
-    if (v + VR - 1 < n_tiles) issue(v + VR - 1, false);
-    if (v + KR - 1 < n_tiles) issue(v + KR - 1, true);
+    if (v + KR - 1 < n_tiles) issue_kv(v + KR - 1);
     const bool self = v < n_st;
     const int kb = self ? v * BKV : (v - n_st + ct0) * BKV;
     // nothing to do: no valid rows in this wave, or a causal tile entirely
@@ -501,19 +507,22 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
       tmax = max_xor32(tmax) * scale_log2;  // the row's two halves; scale > 0 commutes with max
       // lazy rescale: the running max moves only when some row's tile max
       // exceeds it by more than LAZY (log2 units); the first tile (m_run =
-      // -inf, accumulator 0) always takes this branch with alpha = 0.  Tile 0
+      // -inf, accumulator 0) always takes this branch and only sets m.  Tile 0
       // holds key 0, visible to every row, so tmax is finite there (a resumed
       // walk starts from a finite m).  (A row tile whose rows all lie above a
       // causal tile sees only -inf: no change.)
       if (__ballot(tmax > m_run[u] + LAZY)) {
         const float m_new = fmaxf(m_run[u], tmax);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);  // exp2(-inf) = 0
+        // before the first tile every row has m = -inf and a zero state: nothing to scale
+        if (__ballot(m_run[u] != -INFINITY)) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);  // exp2(-inf) = 0
+          l_run[u] *= alpha;
+#pragma unroll
+          for (int i = 0; i < HD / 32; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[u][i][e] *= alpha;
+        }
         m_run[u] = m_new;
-        l_run[u] *= alpha;
-#pragma unroll
-        for (int i = 0; i < HD / 32; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[u][i][e] *= alpha;
       }
       const float nm = -m_run[u];
 #pragma unroll

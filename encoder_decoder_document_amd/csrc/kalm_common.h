@@ -103,6 +103,38 @@ __device__ __forceinline__ void dma16x4(uint64_t sbase, uint32_t o0, uint32_t o1
       : "memory");
 }
 
+// Eight direct-to-LDS copies with one save and restore of M0: four from
+// sa + a0..a3 into LDS bases lds + 1024 j and four from sb + b0..b3 into
+// lds + BOFS + 1024 j (16 bytes per lane each).
+template <uint32_t BOFS>
+__device__ __forceinline__ void dma16x8(uint64_t sa, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint64_t sb,
+                                        uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %9\n\t"
+      "global_load_lds_dwordx4 %1, %10\n\t"
+      "s_add_u32 m0, %9, 0x400\n\t"
+      "global_load_lds_dwordx4 %2, %10\n\t"
+      "s_add_u32 m0, %9, 0x800\n\t"
+      "global_load_lds_dwordx4 %3, %10\n\t"
+      "s_add_u32 m0, %9, 0xc00\n\t"
+      "global_load_lds_dwordx4 %4, %10\n\t"
+      "s_add_u32 m0, %9, %12\n\t"
+      "global_load_lds_dwordx4 %5, %11\n\t"
+      "s_add_u32 m0, %9, %13\n\t"
+      "global_load_lds_dwordx4 %6, %11\n\t"
+      "s_add_u32 m0, %9, %14\n\t"
+      "global_load_lds_dwordx4 %7, %11\n\t"
+      "s_add_u32 m0, %9, %15\n\t"
+      "global_load_lds_dwordx4 %8, %11\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1), "v"(b2), "v"(b3), "s"(lds), "s"(sa), "s"(sb),
+        "n"(BOFS), "n"(BOFS + 1024u), "n"(BOFS + 2048u), "n"(BOFS + 3072u)
+      : "memory", "scc");
+}
+
 // Wait until the copies of the oldest in-flight k-tile are done: at most
 // `later` k-tiles (CPS copies each) issued after it may still be outstanding.
 template <int CPS>
