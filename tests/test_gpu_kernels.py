@@ -233,6 +233,9 @@ def _attn_ref(Q, Ks, Vs, Kc, Vc, cm, doc_of_pair, cu_q, nq, nkv, d):
     ("g8", [40, 97], [33, 64], 64, 8, 1, 0.7, False),
     ("g4_sharp_logits", [150, 80], [90, 40], 96, 4, 1, 3.0, False),
     ("g4_long", [512], [256], 256, 4, 1, 0.7, False),
+    # the largest passage the bf16 path takes (128 key tiles: both validity words)
+    ("g4_max_cmax", [40, 3], [4096, 2049], 4096, 4, 1, 0.7, False),
+    ("g4_max_cmax_general_mask", [20], [0], 4096, 4, 1, 0.7, True),
 ])
 def test_merged_attn_bf16_parity(name, lqs, docs_c, Cmax, nq, nkv, std, general):
     _announce(f"merged_attn bf16 {name}")
