@@ -50,8 +50,8 @@ MEASURED_TRAFFIC = {
                  "fetch_kib": 3108541.0, "write_kib": 6443840.0},
     "qkv_linear": {"src": "f0a62fe46c2f68f091aa05fcc4c97262966cd10ab20d23789b656d7bb9f2b016",
                    "fetch_kib": 2356818.0, "write_kib": 2688301.0},
-    "merged_attn": {"src": "a60c371bcadc2bbd25ebf3908ff6ab4de49225fc667ea9d7987d592e07b35e9f",
-                    "fetch_kib": 1483928.0, "write_kib": 1792200.0},
+    "merged_attn": {"src": "e75c709e951ed1b3cd401d912373085e7b4460edeb3baa8ad756d0a4575c8a2c",
+                    "fetch_kib": 1484152.0, "write_kib": 1792200.0},
 }
 KERNEL_SRC = {"o_linear": "gemm.hip", "qkv_linear": "gemm.hip", "cross_kv": "gemm.hip",
               "merged_attn": "attn_bf16.h", "chunk_pool": "pool.hip", "gather_rows": "rows.hip"}
