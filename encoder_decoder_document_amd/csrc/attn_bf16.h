@@ -379,7 +379,7 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
     asm volatile("" : "+v"(key0));  // recompute the per-row offsets here instead of holding them
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
-      const uint64_t base = kv == 0 ? (self ? ks_base : kc_base) : (self ? vs_base : vc_base);
+      const uint64_t base = uniform64(kv == 0 ? (self ? ks_base : kc_base) : (self ? vs_base : vc_base));
 #pragma unroll
       for (int j = 0; j < RPW / 2; ++j) {
         const int key = key0 + 2 * j;
