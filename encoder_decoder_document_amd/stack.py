@@ -465,6 +465,19 @@ def step(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_sel
     return score(b, stream, rec, prune)
 
 
+def score_pairs(inputs: Dict[str, object], device="cuda", n_layers: Optional[int] = None, prune: bool = True,
+                reuse_self: bool = True) -> Dict[str, torch.Tensor]:
+    """Score every (query, passage) pair of one batch of host inputs, end to end on
+    the device: the per-pair fields of the pages' scoring CLI -- the yes and no
+    logits, their margin and score = sigmoid(margin) ("KaLM-Reranker-V1-Small
+    Q4_K_M GGUF", Score a pair) -- each a device tensor [n_queries * n_docs] in
+    pair order q * n_docs + d.  Larger margins rank first (``rerank.rerank``
+    orders them on the device)."""
+    b = upload(inputs, device, n_layers)
+    yes, no, margin, sc = step(b, prune=prune, reuse_self=reuse_self)
+    return {"yes_logit": yes, "no_logit": no, "margin": margin, "score": sc}
+
+
 class StepGraph:
     """One step captured as a HIP graph (torch.cuda.CUDAGraph records the
     libkalm launches of ``step`` on its capture stream), so that a replay

@@ -76,6 +76,27 @@ def test_stack_parity(idx, n_sample):
     torch.cuda.empty_cache()
 
 
+def test_score_pairs_fields_and_ranking():
+    # the one-call API: the per-pair fields of the scoring CLI, equal to the
+    # step's outputs, and the ranking above it ordered by margin (= by score)
+    sh = synth.SHAPES[1]
+    print(f"[case] score_pairs {sh.name}", flush=True)
+    inp = synth.make_inputs(1, nan_padding=True)
+    out = stack.score_pairs(inp)
+    assert set(out) == {"yes_logit", "no_logit", "margin", "score"}
+    got = {k: to_np(v) for k, v in out.items()}
+    ref = oracle.stack_scores(inp, pairs=list(range(sh.pairs)), mode="mirror")
+    assert_close(got["score"], ref["score"], SCORE_ATOL, 0.0, "score")
+    assert_close(got["margin"], ref["margin"], 2e-2, 1e-2, "margin")
+    assert np.allclose(got["margin"], got["yes_logit"] - got["no_logit"], rtol=0, atol=1e-5)
+    from encoder_decoder_document_amd import rerank
+    recs = rerank.rerank(out["score"], sh.n_docs, 5)
+    assert len(recs) == sh.n_queries and all(len(r) == 5 for r in recs)
+    for q, r in enumerate(recs):
+        s = got["score"][q * sh.n_docs:(q + 1) * sh.n_docs]
+        assert [x["index"] for x in r] == list(np.argsort(-s, kind="stable")[:5])
+
+
 def test_stack_edge_empty_and_one_token_passages():
     # a passage with no valid token leaves pure causal self-attention; a 1-token
     # passage pools to that token; queries of length 1 read their only row
