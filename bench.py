@@ -50,7 +50,7 @@ MEASURED_TRAFFIC = {
                  "fetch_kib": 3108541.0, "write_kib": 6443840.0},
     "qkv_linear": {"src": "f0a62fe46c2f68f091aa05fcc4c97262966cd10ab20d23789b656d7bb9f2b016",
                    "fetch_kib": 2356818.0, "write_kib": 2688301.0},
-    "merged_attn": {"src": "e75c709e951ed1b3cd401d912373085e7b4460edeb3baa8ad756d0a4575c8a2c",
+    "merged_attn": {"src": "d023e09b64933b7bdcf470d8636c772140c73148c65c5983dee392dacce3f01f",
                     "fetch_kib": 1484152.0, "write_kib": 1792200.0},
 }
 KERNEL_SRC = {"o_linear": "gemm.hip", "qkv_linear": "gemm.hip", "cross_kv": "gemm.hip",
