@@ -149,6 +149,9 @@ def model_work(inp, sh, work, single=False):
             "mlp_gate_up" + tag: dict(flops=2.0 * c * H * 2 * I, bytes=float(c * H * e + 2 * I * H * e + c * 2 * I * e)),
             "mlp_act" + tag: dict(flops=8.0 * c * I, bytes=float(c * 3 * I * e)),
             "mlp_down" + tag: dict(flops=2.0 * c * I * H, bytes=float(c * I * e + H * I * e + c * H * 8)),
+            # fused gate/up projection and activation: only the activation leaves the CU
+            "mlp_gate_up_act" + tag: dict(flops=2.0 * c * H * 2 * I + 8.0 * c * I,
+                                          bytes=float(c * H * e + 2 * I * H * e + c * I * e)),
         })
 
     work.update({"attn_norm": norm(rows), "attn_norm_first": norm(U), "attn_norm_last": norm(P),

@@ -340,10 +340,17 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
 // on a cold pipeline.  The epilogue parks each wave's fp32 accumulator in the
 // ring slot just consumed (32 rows x WTN, 16-byte chunks XOR-swizzled by row),
 // which the in-flight copy does not touch.
-template <int BM, int BN, int WM, int WN, int BK, int OCC>
+//
+// GELU (gated MLP): W holds the gate rows and Wu the up rows of an MLP of width
+// I = N / 2.  Output tile t covers BN / 2 gate columns and the BN / 2 up
+// columns of the same units (the first half of the tile's weight rows come
+// from W, the second from Wu), so the epilogue pairs each gate value with its
+// up value and writes A[m, j] = gelu(x_m . wg_j) * (x_m . wu_j) as bf16 into Y
+// ([M, I]); the fp32 products never leave the CU.
+template <int BM, int BN, int WM, int WN, int BK, int OCC, bool GELU = false>
 __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_persistent(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, int M, int K, int N, void* __restrict__ Y, int epi,
-    bf16_t* __restrict__ Ybf) {
+    bf16_t* __restrict__ Ybf, const bf16_t* __restrict__ Wu = nullptr) {
   constexpr int STAGES = 2;
   constexpr int NW = WM * WN;
   constexpr int NT = NW * 64;
@@ -355,6 +362,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_persistent(
   constexpr int CPS = PER_A + PER_B;             // copies per thread per k-tile
   static_assert(NW * 32 * WTN * 4 <= STAGE_ELEMS * 2, "a wave's parked rows fit one ring slot");
   static_assert(WTN % 64 == 0, "park swizzle: rows of 16 or 32 chunks");
+  static_assert(!GELU || (WN % 2 == 0 && (BN / 2) % WTN == 0), "GELU: gate and up halves of a tile on separate waves");
 
   __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGES * STAGE_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -378,18 +386,23 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_persistent(
     const int rr = lane / CPR;
     const int k0 = kk * BK;
     const uint64_t xa = uniform64((uint64_t)(uintptr_t)(X + (int64_t)m0 * K));
-    const uint64_t wa = uniform64((uint64_t)(uintptr_t)(W + (int64_t)n0 * K));
+    // GELU: rows [0, BN/2) of the weight tile are gate units n0/2.., rows [BN/2, BN) the same up units
+    const int g0 = n0 / 2, nu = N / 2;
+    const uint64_t wa = uniform64((uint64_t)(uintptr_t)(W + (int64_t)(GELU ? g0 : n0) * K));
+    const uint64_t wua = GELU ? uniform64((uint64_t)(uintptr_t)(Wu + (int64_t)g0 * K)) : 0;
 #pragma unroll
     for (int j = 0; j < PER_A + PER_B; ++j) {
       const bool isA = j < PER_A;
       const int jj = isA ? j : j - PER_A;
       const int R0 = RPI_D * (wave * (isA ? PER_A : PER_B) + jj);
-      const int row = isA ? min(m0 + R0 + rr, M - 1) - m0 : min(n0 + R0 + rr, N - 1) - n0;
+      const bool up = GELU && !isA && R0 >= BN / 2;  // wave-uniform
+      const int row = isA ? min(m0 + R0 + rr, M - 1) - m0
+                          : (GELU ? min(g0 + (up ? R0 - BN / 2 : R0) + rr, nu - 1) - g0 : min(n0 + R0 + rr, N - 1) - n0);
       int kk8 = k0 + swz<BK>(R0 + rr, lane % CPR) * 8;
       if (kk8 >= K) kk8 = 0;  // in-bounds dummy; zeroed in LDS by zero_k_tail
       const uint32_t off = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)kk8 * 2u;
       const uint32_t dst = b + (isA ? 0u : (uint32_t)(BM * BK * 2)) + (uint32_t)__builtin_amdgcn_readfirstlane(R0 * BK * 2);
-      dma16(isA ? xa : wa, off, dst);
+      dma16(GELU && !isA ? uniform64(up ? wua : wa) : (isA ? xa : wa), off, dst);
     }
   };
 
@@ -478,6 +491,31 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_persistent(
           *(f32x4_t*)(park + r * WTN + ch * 4) =
               f32x4_t{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         }
+      if constexpr (GELU) {
+        // a gate wave (wn < WN/2) and its up partner (wave + WM WN/2) park the
+        // same units; each of the two writes the activation of half of them
+        // (the gate wave the first WTN/2 columns); parks are reused next round
+        __syncthreads();
+        constexpr int HL = WTN / 8;  // lanes per row over half the columns
+        const bool is_up = wn >= WN / 2;
+        const float* pg = is_up ? park - (WN / 2) * WM * (32 * WTN) : park;
+        const float* pu = pg + (WN / 2) * WM * (32 * WTN);
+        const int c = (is_up ? HL : 0) + lane % HL;  // 16-byte chunk of the 64-column block
+        const int nu = N / 2, n = n0 / 2 + (wn % (WN / 2)) * WTN + c * 4;
+#pragma unroll
+        for (int rr = 0; rr < 32; rr += 64 / HL) {
+          const int prr = rr + lane / HL;
+          const int m = m0 + wm * WTM + j * 32 + prr;
+          const int o = prr * WTN + ((c ^ (prr & 15)) * 4);
+          const f32x4_t gv = *(const f32x4_t*)(pg + o), uv = *(const f32x4_t*)(pu + o);
+          if (m < M && n < nu)
+            st_out((u32x2_t*)((bf16_t*)Y + (int64_t)m * nu + n),
+                   u32x2_t{pack_bf16x2(gated_gelu_tanh(gv[0], uv[0]), gated_gelu_tanh(gv[1], uv[1])),
+                           pack_bf16x2(gated_gelu_tanh(gv[2], uv[2]), gated_gelu_tanh(gv[3], uv[3]))});
+        }
+        __syncthreads();
+        continue;
+      }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -601,6 +639,16 @@ void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, v
       hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 32, 4, 1>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y,
                          epi, Y_bf16, rmask, Rsrc, Rrow, Rrows);
   }
+}
+
+void launch_linear_gelu_bf16(const bf16_t* X, const bf16_t* Wg, const bf16_t* Wu, int M, int K, int I, bf16_t* A,
+                             hipStream_t s) {
+  // output tiles of 128 gate + 128 up units (I % 128 == 0, checked by the caller)
+  const int tiles = ((M + 255) / 256) * ((2 * I) / 256);
+  if (tiles == 0) return;
+  const int grid = tiles < 256 ? ((tiles + 7) / 8) * 8 : 256;
+  hipLaunchKernelGGL((gemm_bf16_persistent<256, 256, 2, 4, 64, 1, true>), dim3(grid), dim3(512), 0, s, X, Wg, M, K,
+                     2 * I, (void*)A, (int)EPI_BF16, (bf16_t*)nullptr, Wu);
 }
 
 void launch_linear_f32(const float* X, const float* W, int M, int K, int N, float* Y, bool accumulate,

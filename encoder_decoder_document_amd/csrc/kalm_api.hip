@@ -51,7 +51,7 @@ kalm_status check_launch(const char* what) {
 
 extern "C" {
 
-int32_t kalm_version(void) { return 200; }
+int32_t kalm_version(void) { return 300; }
 
 const char* kalm_last_error(void) { return kalm::g_err; }
 
@@ -348,6 +348,23 @@ kalm_status kalm_gated_gelu(const void* Y, kalm_dtype dt, int64_t y_ld, int64_t 
   KALM_DEVICE_OR_RETURN();
   kalm::launch_gated_gelu(Y, dt == KALM_BF16, y_ld, M, I, A, a_ld, (hipStream_t)stream);
   return kalm::check_launch("kalm_gated_gelu");
+}
+
+kalm_status kalm_linear_gated_gelu(const void* X, const void* Wg, const void* Wu, int32_t M, int32_t K, int32_t I,
+                                   void* A, void* stream) {
+  kalm::g_err[0] = 0;
+  KALM_REQUIRE(M >= 0 && K >= 1 && I >= 1, KALM_ERR_INVALID_ARG, "kalm_linear_gated_gelu: bad sizes M=%d K=%d I=%d",
+               M, K, I);
+  KALM_REQUIRE(K % 8 == 0 && I % 128 == 0, KALM_ERR_UNSUPPORTED,
+               "kalm_linear_gated_gelu: needs K %% 8 == 0 and I %% 128 == 0 (K=%d I=%d)", K, I);
+  KALM_REQUIRE((int64_t)I * K < (1LL << 30), KALM_ERR_UNSUPPORTED, "kalm_linear_gated_gelu: weights too large");
+  KALM_REQUIRE(M == 0 || (X && Wg && Wu && A), KALM_ERR_INVALID_ARG, "kalm_linear_gated_gelu: null pointer");
+  KALM_REQUIRE(ALIGNED16(X) && ALIGNED16(Wg) && ALIGNED16(Wu) && ALIGNED16(A), KALM_ERR_INVALID_ARG,
+               "kalm_linear_gated_gelu: pointers must be 16-byte aligned");
+  KALM_DEVICE_OR_RETURN();
+  kalm::launch_linear_gelu_bf16((const bf16_t*)X, (const bf16_t*)Wg, (const bf16_t*)Wu, M, K, I, (bf16_t*)A,
+                                (hipStream_t)stream);
+  return kalm::check_launch("kalm_linear_gated_gelu");
 }
 
 kalm_status kalm_yesno_score(const void* h, kalm_dtype h_dt, int64_t h_ld, int64_t rows, const int32_t* final_row,

@@ -18,6 +18,17 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // float -> bf16, round to nearest even (the hardware v_cvt_pk_bf16_f32 path on gfx950).
 __device__ __forceinline__ bf16_t to_bf16(float f) { return (bf16_t)f; }
+
+// GELU in its tanh form, 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), times
+// the gate's partner value u (the activation of a gated MLP).  Evaluated as
+// x / (1 + exp(-2 y)) with y the tanh argument -- the same function, since
+// (1 + tanh y) / 2 is the logistic function of 2 y -- with one hardware
+// exp2 and one reciprocal: large |y| give exp2(+inf) = inf (-> 0) or 0 (-> x).
+__device__ __forceinline__ float gated_gelu_tanh(float x, float u) {
+  const float y = 0.7978845608028654f * fmaf(0.044715f * x * x, x, x);
+  const float e = __builtin_amdgcn_exp2f(-2.f * 1.4426950408889634f * y);
+  return x * __builtin_amdgcn_rcpf(1.f + e) * u;
+}
 __device__ __forceinline__ float from_bf16(bf16_t b) { return (float)b; }
 
 // Pack two floats into one dword of two bf16 (lo = a, hi = b).
@@ -212,6 +223,8 @@ void launch_rms_norm(const void* x, bool x_bf16, int64_t x_ld, int64_t M, int H,
                      void* y, bool y_bf16, int64_t y_ld, hipStream_t s);
 void launch_rope(void* X, bool bf16, int64_t ld, int64_t rows, int col0, int nh, int d, const int32_t* cu, int n_seq,
                  int max_len, int mode, float theta, hipStream_t s);
+void launch_linear_gelu_bf16(const bf16_t* X, const bf16_t* Wg, const bf16_t* Wu, int M, int K, int I, bf16_t* A,
+                             hipStream_t s);
 void launch_gated_gelu(const void* Y, bool bf16, int64_t y_ld, int64_t M, int I, void* A, int64_t a_ld,
                        hipStream_t s);
 void launch_gather_rows(const float* src, const int32_t* idx, int64_t M, int H, int64_t n_src,

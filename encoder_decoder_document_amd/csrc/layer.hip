@@ -116,9 +116,7 @@ __global__ __launch_bounds__(256) void gated_gelu_kernel(const T* __restrict__ Y
   f32x4_t o;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float x = g[k];
-    const float inner = 0.7978845608028654f * fmaf(0.044715f * x * x, x, x);
-    o[k] = 0.5f * x * (1.f + tanhf(inner)) * u[k];
+    o[k] = gated_gelu_tanh(g[k], u[k]);
   }
   st4(A + m * a_ld + j, o);
 }

@@ -50,6 +50,7 @@ _SIGS = {
     "kalm_rms_norm": (_i32, [_c_p, _i32, _i64, _i64, _i32, _c_p, _i32, _f32, _c_p, _i32, _i64, _c_p]),
     "kalm_rope": (_i32, [_c_p, _i32, _i64, _i64, _i32, _i32, _i32, _c_p, _i32, _i32, _i32, _f32, _c_p]),
     "kalm_gated_gelu": (_i32, [_c_p, _i32, _i64, _i64, _i32, _c_p, _i64, _c_p]),
+    "kalm_linear_gated_gelu": (_i32, [_c_p, _c_p, _c_p, _i32, _i32, _i32, _c_p, _c_p]),
     "kalm_yesno_score": (_i32, [_c_p, _i32, _i64, _i64, _c_p, _i32, _i32, _c_p, _i32, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "kalm_linear": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _i32, _c_p, _i32, _i32, _c_p, _c_p]),
     "kalm_linear_residual": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _i32, _c_p, _c_p, _i64, _c_p, _c_p, _c_p]),
@@ -341,6 +342,21 @@ def kalm_gated_gelu(Y: torch.Tensor, out: Optional[torch.Tensor] = None, stream=
         out = torch.empty(M, I, dtype=Y.dtype, device=Y.device)
     _check("kalm_gated_gelu", load().kalm_gated_gelu(_ptr(Y), _dt(Y), Y.stride(0), M, I, _ptr(out), out.stride(0),
                                                     _stream(stream)))
+    return out
+
+
+def kalm_linear_gated_gelu(X: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, out: Optional[torch.Tensor] = None,
+                           stream=None):
+    """X [M, K], Wg, Wu [I, K] (bf16) -> gelu_tanh(X Wg^T) * (X Wu^T) [M, I] bf16, fused."""
+    _contig(X, Wg, Wu, out)
+    M, K = X.shape
+    I = Wg.shape[0]
+    if Wu.shape != Wg.shape or Wg.shape[1] != K:
+        raise ValueError("Wg and Wu must both be [I, K]")
+    if out is None:
+        out = torch.empty(M, I, dtype=X.dtype, device=X.device)
+    _check("kalm_linear_gated_gelu", load().kalm_linear_gated_gelu(_ptr(X), _ptr(Wg), _ptr(Wu), M, K, I, _ptr(out),
+                                                                  _stream(stream)))
     return out
 
 

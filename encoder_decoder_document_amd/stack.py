@@ -153,7 +153,8 @@ def upload(inputs: Dict[str, object], device="cuda", n_layers: Optional[int] = N
             xf=torch.empty(P, H, dtype=dt, device=device),          # ... the final rows
             hfn=torch.empty(P, H, dtype=torch.float32, device=device),  # final norm of the final rows
             m_x=torch.empty(ch, H, dtype=dt, device=device),        # MLP row chunk: normalised input,
-            m_gu=torch.empty(ch, 2 * I, dtype=dt, device=device),   # gate | up projections,
+            # gate | up projections (not needed when the fused kernel takes the width)
+            m_gu=torch.empty(0 if dt == torch.bfloat16 and I % 128 == 0 else ch, 2 * I, dtype=dt, device=device),
             m_a=torch.empty(ch, I, dtype=dt, device=device),        # activation
         )
     return DeviceBatch(
@@ -332,6 +333,9 @@ def decoder_model(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, 
     scale = 1.0 / math.sqrt(b.d)
     single = prune and b.n_layers == 1
     last_pruned = pruned(b, prune)
+    I = M["I"]
+    # the fused gate/up + activation kernel takes bf16 widths in blocks of 128 units
+    fused_mlp = M["Wgu"][0].dtype == torch.bfloat16 and I % 128 == 0
 
     def norm(src, w, dst, name):
         with rec(name):
@@ -348,10 +352,16 @@ def decoder_model(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, 
             n = hv.shape[0]
             x, gu, a = B["m_x"][:n], B["m_gu"][:n], B["m_a"][:n]
             norm(hv, M["mlp_norm"][l], x, "mlp_norm" + tag)
-            with rec("mlp_gate_up" + tag):
-                ops.kalm_linear(x, M["Wgu"][l], Y=gu, stream=stream)
-            with rec("mlp_act" + tag):
-                ops.kalm_gated_gelu(gu, out=a, stream=stream)
+            if fused_mlp:
+                # gate/up projection and activation in one kernel: the [n, 2I]
+                # projections never reach HBM
+                with rec("mlp_gate_up_act" + tag):
+                    ops.kalm_linear_gated_gelu(x, M["Wgu"][l][:I], M["Wgu"][l][I:], out=a, stream=stream)
+            else:
+                with rec("mlp_gate_up" + tag):
+                    ops.kalm_linear(x, M["Wgu"][l], Y=gu, stream=stream)
+                with rec("mlp_act" + tag):
+                    ops.kalm_gated_gelu(gu, out=a, stream=stream)
             with rec("mlp_down" + tag):
                 ops.kalm_linear(a, M["Wd"][l], Y=hv, accumulate=True, stream=stream)
 

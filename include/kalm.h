@@ -56,7 +56,8 @@ typedef enum {
 typedef enum { KALM_F32 = 0, KALM_BF16 = 1 } kalm_dtype;
 
 /* Library version, major*10000 + minor*100 + patch (0.2.0: split attention,
- * one-layer final rows, layer parts). */
+ * one-layer final rows, layer parts; 0.3.0: fused gate/up projection and
+ * activation). */
 int32_t kalm_version(void);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
@@ -309,6 +310,21 @@ kalm_status kalm_rope(void* X, kalm_dtype dt, int64_t ld, int64_t rows, int32_t 
  */
 kalm_status kalm_gated_gelu(const void* Y, kalm_dtype dt, int64_t y_ld, int64_t M, int32_t I, void* A,
                             int64_t a_ld, void* stream);
+
+/*
+ * kalm_linear_gated_gelu -- the gated MLP's gate and up projections fused with
+ * its activation: A[m, j] = gelu(X[m] . Wg[j]) * (X[m] . Wu[j]), the same
+ * tanh-form gelu as kalm_gated_gelu, fp32 products (not rounded to bf16
+ * between the projection and the activation), one rounding to bf16.
+ *   X   [M, K] bf16, row-major (K contiguous)
+ *   Wg  [I, K] bf16 gate rows, Wu [I, K] bf16 up rows (PyTorch [out, in])
+ *   A   [M, I] bf16 out, row-major
+ * BF16 only.  Requires K % 8 == 0, I % 128 == 0 (an output tile holds 128 gate
+ * and the matching 128 up units), 16-byte aligned pointers; X, Wg, Wu and A
+ * must not overlap.
+ */
+kalm_status kalm_linear_gated_gelu(const void* X, const void* Wg, const void* Wu, int32_t M, int32_t K, int32_t I,
+                                   void* A, void* stream);
 
 /*
  * a4 -- yes/no readout ([MLX] What this is: score = softmax([logit_yes,

@@ -48,7 +48,7 @@ def test_binding_covers_every_declared_symbol():
 def test_invalid_arguments_rejected_before_launch():
     from encoder_decoder_document_amd import ops
     lib = ops.load()
-    assert lib.kalm_version() == 200
+    assert lib.kalm_version() == 300
     # chunk = 0
     st = lib.kalm_chunk_pool(None, None, 1, 8, 64, 0, ops.KALM_BF16, None, None, None, None)
     assert st == ops.KALM_ERR_INVALID_ARG and b"chunk" in lib.kalm_last_error()
@@ -116,6 +116,13 @@ def test_invalid_arguments_rejected_before_launch():
     assert st == ops.KALM_ERR_INVALID_ARG and b"top_n" in lib.kalm_last_error()
     st = lib.kalm_rank_topn(None, 1, 5000, 10, None, None, None)
     assert st == ops.KALM_ERR_UNSUPPORTED
+    # fused gate/up + activation: width not a multiple of 128; K not a multiple of 8; missing up weights
+    st = lib.kalm_linear_gated_gelu(16, 16, 16, 10, 64, 100, 16, None)
+    assert st == ops.KALM_ERR_UNSUPPORTED and b"I % 128" in lib.kalm_last_error()
+    st = lib.kalm_linear_gated_gelu(16, 16, 16, 10, 60, 128, 16, None)
+    assert st == ops.KALM_ERR_UNSUPPORTED
+    st = lib.kalm_linear_gated_gelu(16, 16, None, 10, 64, 128, 16, None)
+    assert st == ops.KALM_ERR_INVALID_ARG and b"null" in lib.kalm_last_error()
 
 
 @needs_lib

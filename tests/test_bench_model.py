@@ -74,10 +74,16 @@ def test_single_layer_model_counts_final_rows_only():
 
 
 def test_counter_traffic_goes_stale_with_the_source(monkeypatch):
+    import hashlib
     for k, m in bench.MEASURED_TRAFFIC.items():
         t = bench.traffic_bytes(k)
-        # the stored figures belong to the committed source, scaled by the copy calibration
-        assert t == m["fetch_kib"] * 1024 * bench.FETCH_FACTOR + m["write_kib"] * 1024 * bench.WRITE_FACTOR
+        path = os.path.join(ROOT, "encoder_decoder_document_amd", "csrc", bench.KERNEL_SRC[k])
+        current = hashlib.sha256(open(path, "rb").read()).hexdigest() == m["src"]
+        # figures taken on this source, scaled by the copy calibration; none once the source changed
+        if current:
+            assert t == m["fetch_kib"] * 1024 * bench.FETCH_FACTOR + m["write_kib"] * 1024 * bench.WRITE_FACTOR
+        else:
+            assert t is None
     stale = {k: dict(v, src="0" * 64) for k, v in bench.MEASURED_TRAFFIC.items()}
     monkeypatch.setattr(bench, "MEASURED_TRAFFIC", stale)
     assert all(bench.traffic_bytes(k) is None for k in stale)

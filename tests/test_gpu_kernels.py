@@ -669,6 +669,22 @@ def test_gated_gelu_parity(M, I, bf16):
     assert_close(to_np(A), ref, *(BF16_TOL if bf16 else F32_TOL), "gated_gelu")
 
 
+@pytest.mark.parametrize("M,K,I", [(300, 200, 128), (513, 640, 384), (1, 64, 256), (1100, 1152, 768)])
+def test_linear_gated_gelu_parity(M, K, I):
+    # the fused gate/up projection + activation against fp64 products of the
+    # same bf16 operands: ragged M, a K tail (K % 64 != 0), several 128-unit blocks
+    _announce(f"linear_gated_gelu M={M} K={K} I={I}")
+    X = synth.normal(70, (M, K), 1.0, True)
+    Wg = synth.normal(71, (I, K), 1.0 / np.sqrt(K), True)
+    Wu = synth.normal(72, (I, K), 1.0 / np.sqrt(K), True)
+    bf = torch.bfloat16
+    A = ops.kalm_linear_gated_gelu(to_dev(X, bf), to_dev(Wg, bf), to_dev(Wu, bf))
+    torch.cuda.synchronize()
+    Xd = X.astype(np.float64)
+    ref = oracle.gated_gelu(Xd @ Wg.astype(np.float64).T, Xd @ Wu.astype(np.float64).T)
+    assert_close(to_np(A), ref, *BF16_TOL, "linear_gated_gelu")
+
+
 # ------------------------------------------------------------------ empty inputs
 def test_zero_sized_calls_are_valid_noops():
     """Every entry point accepts an empty batch (no pairs, rows, passages or
@@ -710,6 +726,8 @@ def test_zero_sized_calls_are_valid_noops():
     Xr = torch.full((2, 64), 3.0, dtype=f, device=dev)
     ops.kalm_rope(Xr, 0, 2, 32, cu0, 0)
     assert ops.kalm_gated_gelu(torch.zeros(0, 64, dtype=bf, device=dev)).shape[0] == 0
+    wgu = torch.zeros(128, 64, dtype=bf, device=dev)
+    assert ops.kalm_linear_gated_gelu(torch.zeros(0, 64, dtype=bf, device=dev), wgu, wgu).shape == (0, 128)
     torch.cuda.synchronize()
     assert (Yf == 7.0).all() and (Xr == 3.0).all()
 
