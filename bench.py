@@ -46,12 +46,12 @@ FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 MEASURED_TRAFFIC = {
     # profiles/hbm_traffic_small_stack26_bf16.md (the QKV figures are the mean over the
     # 24 full-height QKV launches only; the same kernel symbol also runs the last layer's K/V)
-    "o_linear": {"src": "f0a62fe46c2f68f091aa05fcc4c97262966cd10ab20d23789b656d7bb9f2b016",
-                 "fetch_kib": 3108541.0, "write_kib": 6443840.0},
-    "qkv_linear": {"src": "f0a62fe46c2f68f091aa05fcc4c97262966cd10ab20d23789b656d7bb9f2b016",
-                   "fetch_kib": 2356818.0, "write_kib": 2688301.0},
+    "o_linear": {"src": "95f47cf4a369cef446fc2112c5041b1b93466c75131691b14ec6e212b260da7d",
+                 "fetch_kib": 3108944.8, "write_kib": 6443341.3},
+    "qkv_linear": {"src": "95f47cf4a369cef446fc2112c5041b1b93466c75131691b14ec6e212b260da7d",
+                   "fetch_kib": 2499455.5, "write_kib": 2688300.7},
     "merged_attn": {"src": "d023e09b64933b7bdcf470d8636c772140c73148c65c5983dee392dacce3f01f",
-                    "fetch_kib": 1484152.0, "write_kib": 1792200.0},
+                    "fetch_kib": 1484128.2, "write_kib": 1792200.0},
 }
 KERNEL_SRC = {"o_linear": "gemm.hip", "qkv_linear": "gemm.hip", "cross_kv": "gemm.hip",
               "merged_attn": "attn_bf16.h", "chunk_pool": "pool.hip", "gather_rows": "rows.hip"}
