@@ -1,0 +1,86 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake -- a wrong divisor, an off-by-one window, a
+dropped or transposed term, a wrong sign or index -- in a copy of the oracle
+written to a temporary tree, runs the pin tests (tests/test_oracle.py) against
+that copy in a separate process, and requires them to fail.  The unmodified
+copy must pass, so a failure is the planted mistake's doing.  The product
+code is never touched: the mistakes live only in the temporary copy.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ORACLE = os.path.join(ROOT, "oracle", "kalm_ref.py")
+
+# (what the mistake is, exact text in the oracle, replacement)
+MUTATIONS = [
+    ("pool: divide by the chunk size, not the valid count",
+     "pooled[d, c] = rows.sum(axis=0) / cnt", "pooled[d, c] = rows.sum(axis=0) / chunk"),
+    ("pool: window shifted by one token",
+     "t0, t1 = c * chunk, min(T, (c + 1) * chunk)", "t0, t1 = c * chunk + 1, min(T, (c + 1) * chunk + 1)"),
+    ("attention: a row does not see its own key",
+     "causal = np.tril(np.ones((Lq, Lq), dtype=bool))",
+     "causal = np.tril(np.ones((Lq, Lq), dtype=bool), -1) | np.eye(Lq, dtype=bool) * (np.arange(Lq) == 0)"),
+    ("attention: wrong KV head for a query head", "g = h // group", "g = h % nkv"),
+    ("attention: 1/d instead of 1/sqrt(d)", "scale = 1.0 / math.sqrt(d)", "scale = 1.0 / d"),
+    ("attention: normalised by the largest row sum", "O[:, h] = (e / tot) @ v", "O[:, h] = (e / tot.max()) @ v"),
+    ("score: margin with the wrong sign", "m = y - n", "m = n - y"),
+    ("stack: residual dropped", "h = keep_f32(h + O @ np.asarray(W[\"Wo\"], F64).T)",
+     "h = keep_f32(O @ np.asarray(W[\"Wo\"], F64).T)"),
+    ("stack: cross values projected with the key weights",
+     "Kc, Vc = cross_kv(pooled_doc, W[\"Wkc\"], W[\"Wvc\"])", "Kc, Vc = cross_kv(pooled_doc, W[\"Wkc\"], W[\"Wkc\"])"),
+    ("bf16 rounding: truncation instead of round-half-even",
+     "m = np.rint(m * 256.0) / 256.0", "m = np.floor(m * 256.0) / 256.0"),
+    ("layout: final row one past the pair", "final_row.append(cu_q[-1] + n - 1)", "final_row.append(cu_q[-1] + n)"),
+    ("layout: residual start from the wrong query row", "h0_final.append(q_start[q] + n - 1)",
+     "h0_final.append(q_start[q] + n)"),
+    ("rank: ties broken by the higher index",
+     "0.0 if math.isnan(s[q, j]) else -s[q, j], j))", "0.0 if math.isnan(s[q, j]) else -s[q, j], -j))"),
+    ("RMSNorm: mean of |x| instead of mean of x^2", "ms = np.mean(x * x, axis=-1, keepdims=True)",
+     "ms = np.mean(np.abs(x), axis=-1, keepdims=True)"),
+    ("RoPE: frequencies over the half dimension", "inv_freq = float(theta) ** (-2.0 * np.arange(half) / d)",
+     "inv_freq = float(theta) ** (-2.0 * np.arange(half) / half)"),
+    ("RoPE: rotation sense flipped", "return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)",
+     "return np.concatenate([a * c + b * s, b * c - a * s], axis=-1)"),
+    ("GELU: cubic coefficient dropped", "(x + 0.044715 * x ** 3)", "(x)"),
+]
+
+
+def _tree(tmp_path, src):
+    """A minimal copy of the repository whose oracle is ``src``."""
+    root = tmp_path / "repo"
+    shutil.copytree(os.path.join(ROOT, "tests"), root / "tests",
+                    ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutations.py"))
+    pkg = root / "encoder_decoder_document_amd"
+    pkg.mkdir()
+    for f in os.listdir(os.path.join(ROOT, "encoder_decoder_document_amd")):
+        if f.endswith(".py"):
+            shutil.copy(os.path.join(ROOT, "encoder_decoder_document_amd", f), pkg / f)
+    (root / "oracle").mkdir()
+    shutil.copy(os.path.join(ROOT, "oracle", "__init__.py"), root / "oracle" / "__init__.py")
+    (root / "oracle" / "kalm_ref.py").write_text(src)
+    return root
+
+
+def _pins(root):
+    env = dict(os.environ, PYTHONPATH=str(root), PYTHONDONTWRITEBYTECODE="1")
+    return subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle.py", "-x", "-q", "-m", "not gpu",
+                           "-p", "no:cacheprovider"], cwd=root, env=env, capture_output=True, text=True, timeout=600)
+
+
+def test_unmodified_copy_passes_the_pins(tmp_path):
+    r = _pins(_tree(tmp_path, open(ORACLE).read()))
+    assert r.returncode == 0, r.stdout[-2000:]
+
+
+@pytest.mark.parametrize("what,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_a_planted_mistake(tmp_path, what, old, new):
+    src = open(ORACLE).read()
+    assert src.count(old) == 1, f"mutation target not found once: {old!r}"
+    r = _pins(_tree(tmp_path, src.replace(old, new)))
+    assert r.returncode == 1, f"pins did not catch: {what}\n{r.stdout[-1500:]}"
