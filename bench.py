@@ -46,9 +46,9 @@ FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 MEASURED_TRAFFIC = {
     # profiles/hbm_traffic_small_stack26_bf16.md (the QKV figures are the mean over the
     # 24 full-height QKV launches only; the same kernel symbol also runs the last layer's K/V)
-    "o_linear": {"src": "95f47cf4a369cef446fc2112c5041b1b93466c75131691b14ec6e212b260da7d",
+    "o_linear": {"src": "fa920d3086110191496affc9dbd53c74b65ac665467d78862e3bae729afcb7b2",
                  "fetch_kib": 3108944.8, "write_kib": 6443341.3},
-    "qkv_linear": {"src": "95f47cf4a369cef446fc2112c5041b1b93466c75131691b14ec6e212b260da7d",
+    "qkv_linear": {"src": "fa920d3086110191496affc9dbd53c74b65ac665467d78862e3bae729afcb7b2",
                    "fetch_kib": 2499455.5, "write_kib": 2688300.7},
     "merged_attn": {"src": "d023e09b64933b7bdcf470d8636c772140c73148c65c5983dee392dacce3f01f",
                     "fetch_kib": 1484128.2, "write_kib": 1792200.0},

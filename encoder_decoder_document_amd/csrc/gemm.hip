@@ -14,12 +14,14 @@
 // global memory straight into LDS with the gfx950 global_load_lds_dwordx4 copy
 // (no staging registers) through an LDS ring of STAGES k-tiles, one barrier
 // per k-tile.  With BK = 64 every copied row is one whole 128-byte line, which
-// halves the L1 -> L2 requests per byte (the k-loop is bound by the requests
-// in flight per CU, not by L2 bandwidth).  16-byte k-chunks are stored XOR-swizzled
+// halves the L1 -> L2 requests per byte.  The k-loop is bound by that per-k-tile
+// rendezvous -- every wave waits for the slowest copy of the workgroup -- more
+// than by L2 bandwidth or by the ring's depth.  16-byte k-chunks are stored XOR-swizzled
 // (see swz), chosen through the address each lane fetches, so the fragment
 // reads of 32 consecutive rows are bank-conflict free.  Workgroups are
 // remapped so that each XCD walks a contiguous range of output tiles (the
-// tiles sharing activation rows stay in one L2).
+// tiles sharing activation rows stay in one L2).  The persistent kernel also
+// serves a gated MLP's gate/up projection fused with its activation (GELU).
 #include "kalm_common.h"
 
 namespace {
