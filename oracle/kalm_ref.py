@@ -47,15 +47,20 @@ F64 = np.float64
 # storage rounding (used only by the mirror mode)
 # --------------------------------------------------------------------------
 def round_bf16(a) -> np.ndarray:
-    """Nearest bf16 value (8 significant bits, ties to even), as float64.
+    """Nearest bf16 value (ties to even), as float64.
 
-    bf16 shares float32's exponent range, so for the normal-range values
-    handled here rounding the significand to 8 bits is the whole conversion.
+    bf16 has float32's sign and 8-bit exponent and 7 stored significand
+    bits.  A value in [2^(e-1), 2^e) at or above 2^-126 keeps 8 significant
+    bits (its quantum is 2^(e-8)); below 2^-126 the representable values are
+    the multiples of 2^-133 (subnormals); a value that rounds to 2^128 or
+    beyond is +-inf.  Rounding to a multiple of the quantum with ties to even
+    is ties-to-even on the stored significand.  NaN stays NaN.
     """
     a = np.asarray(a, dtype=F64)
-    m, e = np.frexp(a)                       # a = m * 2**e, 0.5 <= |m| < 1
-    m = np.rint(m * 256.0) / 256.0           # np.rint rounds half to even
-    return np.ldexp(m, e)
+    _, e = np.frexp(a)                          # |a| in [2^(e-1), 2^e)
+    q = np.maximum(e - 8, -133)                 # exponent of the quantum
+    r = np.ldexp(np.rint(np.ldexp(a, -q)), q)   # np.rint rounds half to even
+    return np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, a), r)
 
 
 def round_f32(a) -> np.ndarray:
@@ -412,13 +417,15 @@ def decoder_stack(h0, pooled_doc, chunk_mask_doc, layers: List[Dict[str, np.ndar
 
 
 def stack_scores(inputs: Dict[str, object], pairs: Optional[Iterable[int]] = None,
-                 mode: str = "mirror", n_layers: Optional[int] = None):
+                 mode: str = "mirror", n_layers: Optional[int] = None, return_hidden: bool = False):
     """Score the pairs of a synthetic batch (all pairs by default).
 
     Pools every passage that a chosen pair needs (then rounds the pooled
     vectors to the storage dtype in mirror mode), and runs
     ``decoder_stack`` per pair.  Returns dict of float64 arrays yes, no,
-    margin, score over the chosen pairs, plus ``pairs``.
+    margin, score over the chosen pairs, plus ``pairs``; with
+    ``return_hidden`` also ``h_final`` [pairs, H], each pair's hidden state
+    at its final position after the last layer (before any final norm).
     """
     sh = inputs["shape"]
     D = sh.n_docs
@@ -429,6 +436,7 @@ def stack_scores(inputs: Dict[str, object], pairs: Optional[Iterable[int]] = Non
     st = _store_fn(mode, sh.dtype)
     pooled_cache: Dict[int, tuple] = {}
     res = {k: [] for k in ("yes", "no", "margin", "score")}
+    h_final = []
     for p in pairs:
         q, dd = p // D, p % D
         if dd not in pooled_cache:
@@ -437,9 +445,14 @@ def stack_scores(inputs: Dict[str, object], pairs: Optional[Iterable[int]] = Non
         pooled_doc, cm_doc = pooled_cache[dd]
         h0 = inputs["h0"][q_start[q]:q_start[q + 1]]
         out = decoder_stack(h0, pooled_doc, cm_doc, layers, inputs["w_yesno"],
-                            sh.nq, sh.nkv, sh.d, mode=mode, dtype=sh.dtype, model=inputs.get("model"))
+                            sh.nq, sh.nkv, sh.d, mode=mode, dtype=sh.dtype, return_hidden=return_hidden,
+                            model=inputs.get("model"))
         for k in res:
             res[k].append(float(out[k]))
+        if return_hidden:
+            h_final.append(out["h"][-1])
     res = {k: np.asarray(v, dtype=F64) for k, v in res.items()}
     res["pairs"] = np.asarray(pairs, dtype=np.int64)
+    if return_hidden:
+        res["h_final"] = np.asarray(h_final, dtype=F64).reshape(len(pairs), inputs["shape"].H)
     return res

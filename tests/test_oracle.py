@@ -312,6 +312,161 @@ def test_round_bf16_against_bit_truncation_definition():
                                   torch.as_tensor(a32).to(torch.bfloat16).to(torch.float64).numpy())
 
 
+# Every finite non-negative bf16 value, in increasing order: the upper 16
+# bits of a float32 (0x0000 .. 0x7F7F), each pattern read as a number.
+_BF16_BITS = np.arange(0, 0x7F80, dtype=np.uint32)
+_BF16_VALS = (_BF16_BITS << 16).view(np.float32).astype(np.float64)
+
+
+def _bf16_nearest_by_table(a):
+    """Nearest bf16 value by search over the table of all bf16 values: the
+    closer neighbour, the one with an even bit pattern on a tie, +-inf past
+    the midpoint between the largest finite value and 2^128."""
+    a = np.asarray(a, dtype=np.float64)
+    x = np.abs(a)
+    j = np.clip(np.searchsorted(_BF16_VALS, x), 1, len(_BF16_VALS) - 1)
+    lo, hi = _BF16_VALS[j - 1], _BF16_VALS[j]
+    dlo, dhi = x - lo, hi - x
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (_BF16_BITS[j] % 2 == 0))
+    r = np.where(pick_hi, hi, lo)
+    r = np.where(x == 0, 0.0, r)
+    top = _BF16_VALS[-1]
+    mid_inf = top + (top - _BF16_VALS[-2]) / 2          # halfway to 2^128; ties go to 2^128 (even) = inf
+    r = np.where(x >= mid_inf, np.inf, np.where(x > top, top, r))
+    return np.where(np.isnan(a), np.nan, np.copysign(r, a))
+
+
+def test_round_bf16_full_range_against_the_table_of_all_values():
+    # normal, subnormal (below 2^-126: multiples of 2^-133) and overflowing
+    # inputs, and exact midpoints between neighbouring bf16 values
+    rng = np.random.default_rng(12)
+    a = rng.standard_normal(40000) * 10.0 ** rng.uniform(-45, 38.6, 40000)
+    k = rng.integers(0, len(_BF16_VALS) - 1, 4000)
+    mids = (_BF16_VALS[k] + _BF16_VALS[k + 1]) / 2
+    sub = rng.integers(0, 1 << 8, 2000) * 2.0 ** -134          # subnormal grid and its midpoints
+    top = _BF16_VALS[-1]
+    special = np.array([0.0, -0.0, top, -top, top + (top - _BF16_VALS[-2]) / 2, 2.0 ** 128, 1e39, -1e39,
+                        2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -134, 2.0 ** -126, 2.0 ** -126 - 2.0 ** -134,
+                        np.inf, -np.inf])
+    a = np.concatenate([a, mids, -mids, sub, -sub, special])
+    got = oracle.round_bf16(a)
+    ref = _bf16_nearest_by_table(a)
+    np.testing.assert_array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+    assert np.isnan(oracle.round_bf16(np.nan))
+
+
+# ------------------------------------------------------------------ stack: mirror-mode storage points
+# One pair, one layer, one head (nq = nkv = 1, d = H), weights chosen so the
+# attention reduces to a closed form: one visible key (its value), uniform
+# weights (Wq = 0: the mean of the visible values) or two keys (a logistic
+# weight).  Storage rounding is applied with the table search above, fp32
+# storage with a float32 cast; the oracle's mirror mode must match exactly.
+def _bf(a):
+    return _bf16_nearest_by_table(a)
+
+
+def _f32(a):
+    return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def _one_pair(h0, x_doc, mask_doc, W):
+    Lq, H = h0.shape
+    T = x_doc.shape[0]
+    sh = synth.Shape("closed_form", 1, 1, T, H, 1, 1, H, 1, "bf16", ("list", [int(mask_doc.sum())], 0),
+                     ("list", [Lq], 0))
+    inp = dict(shape=sh, x=x_doc[None].astype(np.float32), token_mask=mask_doc[None].astype(np.uint8),
+               lq=np.array([Lq], np.int32), h0=h0.astype(np.float32), layers=[W],
+               w_yesno=np.ones((2, H), np.float32))
+    return oracle.stack_scores(inp, mode="mirror", return_hidden=True)["h_final"][0]
+
+
+def _layer_weights(H, rng, wq=0.0, wk=0.0, wv=1.0 / 3.0, wkc=0.0, wvc=1.0 / 3.0, wo=0.75):
+    eye = np.eye(H)
+    return dict(Wq=wq * eye, Wk=wk * eye, Wv=wv * eye, Wkc=wkc * eye, Wvc=wvc * eye, Wo=wo * eye)
+
+
+def _h0(rng, Lq, H):
+    return rng.standard_normal((Lq, H)).astype(np.float32).astype(np.float64)   # not bf16-representable
+
+
+def test_mirror_one_visible_key_rounds_the_layer_input_and_keeps_fp32_residual():
+    # one position, empty passage: the output is the single value row
+    # V = bf16(bf16(h) Wv^T); the residual is stored in fp32
+    rng = np.random.default_rng(31)
+    H = 64
+    h0 = _h0(rng, 1, H)
+    W = _layer_weights(H, rng, wq=0.5, wk=0.25)
+    x = np.full((4, H), np.nan)
+    got = _one_pair(h0, x, np.zeros(4), W)
+    V = _bf(_bf(h0) / 3.0)
+    np.testing.assert_array_equal(got, _f32(h0 + V * 0.75)[-1])
+
+
+def test_mirror_uniform_weights_round_values_and_output():
+    # Wq = 0: every logit is 0, so row 1's output is bf16((V0 + V1) / 2)
+    rng = np.random.default_rng(32)
+    H, Lq = 64, 2
+    h0 = _h0(rng, Lq, H)
+    W = _layer_weights(H, rng, wk=0.5)
+    got = _one_pair(h0, np.full((4, H), np.nan), np.zeros(4), W)
+    V = _bf(_bf(h0) / 3.0)
+    O1 = _bf((V[0] + V[1]) / 2)
+    np.testing.assert_array_equal(got, _f32(h0[1] + O1 * 0.75))
+
+
+def test_mirror_two_keys_round_queries_and_keys():
+    # row 1 of two positions: weights sigma(s1 - s0), sigma(s0 - s1) with
+    # s_j = bf16(0.3 bf16(h1)) . bf16(0.7 bf16(h_j)) / sqrt(d)
+    rng = np.random.default_rng(33)
+    H, Lq = 64, 2
+    h0 = _h0(rng, Lq, H) * 0.5
+    W = _layer_weights(H, rng, wq=0.3, wk=0.7)
+    got = _one_pair(h0, np.full((4, H), np.nan), np.zeros(4), W)
+    hb = _bf(h0)
+    q1, K, V = _bf(0.3 * hb[1]), _bf(0.7 * hb), _bf(hb / 3.0)
+    s = (K @ q1) / math.sqrt(H)
+    p1 = 1.0 / (1.0 + math.exp(s[0] - s[1]))
+    O1 = _bf((1.0 - p1) * V[0] + p1 * V[1])
+    np.testing.assert_allclose(got, _f32(h0[1] + O1 * 0.75), rtol=0, atol=1e-12)
+
+
+def test_mirror_cross_chunk_rounds_pooled_and_cross_values():
+    # one position, a passage of 3 valid tokens in one chunk, Wq = 0: the
+    # output is bf16((V0 + Vc) / 2), Vc = bf16(bf16(mean of the tokens) / 3)
+    rng = np.random.default_rng(34)
+    H = 64
+    h0 = _h0(rng, 1, H)
+    x = rng.standard_normal((4, H)).astype(np.float32).astype(np.float64)
+    mask = np.array([1, 1, 1, 0])
+    x[3] = np.nan
+    W = _layer_weights(H, rng, wk=0.5, wkc=0.5)
+    got = _one_pair(h0, x, mask, W)
+    V0 = _bf(_bf(h0[0]) / 3.0)
+    Vc = _bf(_bf(x[:3].mean(axis=0)) / 3.0)
+    np.testing.assert_array_equal(got, _f32(h0[0] + _bf((V0 + Vc) / 2) * 0.75))
+
+
+def test_mirror_cross_chunk_key_rounding():
+    # one position and one chunk with a real query: the logistic weight of
+    # the cross key uses kc = bf16(0.9 bf16(pooled))
+    rng = np.random.default_rng(35)
+    H = 64
+    h0 = _h0(rng, 1, H) * 0.5
+    x = rng.standard_normal((4, H)).astype(np.float32).astype(np.float64)
+    mask = np.array([1, 1, 0, 0])
+    x[2:] = np.nan
+    W = _layer_weights(H, rng, wq=0.3, wk=0.7, wkc=0.9)
+    got = _one_pair(h0, x, mask, W)
+    hb = _bf(h0[0])
+    pooled = _bf(x[:2].mean(axis=0))
+    q, k0, kc = _bf(0.3 * hb), _bf(0.7 * hb), _bf(0.9 * pooled)
+    V0, Vc = _bf(hb / 3.0), _bf(pooled / 3.0)
+    pc = 1.0 / (1.0 + math.exp((q @ k0 - q @ kc) / math.sqrt(H)))
+    O = _bf((1.0 - pc) * V0 + pc * Vc)
+    np.testing.assert_allclose(got, _f32(h0[0] + O * 0.75), rtol=0, atol=1e-12)
+
+
 # ------------------------------------------------------------------ stack
 def _tiny_inputs(n_layers=2, seed=5, shape=None):
     return synth.make_inputs(0, seed=seed, n_layers=n_layers, shape=shape)

@@ -35,7 +35,30 @@ MUTATIONS = [
     ("stack: cross values projected with the key weights",
      "Kc, Vc = cross_kv(pooled_doc, W[\"Wkc\"], W[\"Wvc\"])", "Kc, Vc = cross_kv(pooled_doc, W[\"Wkc\"], W[\"Wkc\"])"),
     ("bf16 rounding: truncation instead of round-half-even",
-     "m = np.rint(m * 256.0) / 256.0", "m = np.floor(m * 256.0) / 256.0"),
+     "r = np.ldexp(np.rint(np.ldexp(a, -q)), q)", "r = np.ldexp(np.floor(np.ldexp(a, -q)), q)"),
+    ("bf16 rounding: 8 significant bits kept below 2^-126 (no subnormal grid)",
+     "q = np.maximum(e - 8, -133)", "q = e - 8"),
+    ("bf16 rounding: no overflow to inf", "return np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, a), r)",
+     "return r"),
+    # mirror mode: each storage rounding dropped in turn
+    ("mirror: layer input not rounded", "hb = st(rms_norm(h, W[\"attn_norm\"], eps)) if model else st(h)",
+     "hb = st(rms_norm(h, W[\"attn_norm\"], eps)) if model else h"),
+    ("mirror: queries not rounded", "Qm = st(hb @ np.asarray(W[\"Wq\"], F64).T)",
+     "Qm = (hb @ np.asarray(W[\"Wq\"], F64).T)"),
+    ("mirror: self keys not rounded", "Ks = st(hb @ np.asarray(W[\"Wk\"], F64).T)",
+     "Ks = (hb @ np.asarray(W[\"Wk\"], F64).T)"),
+    ("mirror: self values not rounded", "Vs = st(hb @ np.asarray(W[\"Wv\"], F64).T)",
+     "Vs = (hb @ np.asarray(W[\"Wv\"], F64).T)"),
+    ("mirror: cross keys not rounded", "Kc = st(Kc).reshape(-1, nkv, d)", "Kc = Kc.reshape(-1, nkv, d)"),
+    ("mirror: cross values not rounded", "Vc = st(Vc).reshape(-1, nkv, d)", "Vc = Vc.reshape(-1, nkv, d)"),
+    ("mirror: attention output not rounded", "O = st(O).reshape(Lq, nq * d)", "O = O.reshape(Lq, nq * d)"),
+    ("mirror: attention output rounded after the projection instead of before",
+     "O = st(O).reshape(Lq, nq * d)\n        h = keep_f32(h + O @ np.asarray(W[\"Wo\"], F64).T)",
+     "O = O.reshape(Lq, nq * d)\n        h = keep_f32(h + st(O @ np.asarray(W[\"Wo\"], F64).T))"),
+    ("mirror: residual not stored in fp32", "h = keep_f32(h + O @ np.asarray(W[\"Wo\"], F64).T)",
+     "h = h + O @ np.asarray(W[\"Wo\"], F64).T"),
+    ("mirror: pooled vectors not rounded", "pooled_cache[dd] = (st(pooled[0]), cm[0])",
+     "pooled_cache[dd] = (pooled[0], cm[0])"),
     ("layout: final row one past the pair", "final_row.append(cu_q[-1] + n - 1)", "final_row.append(cu_q[-1] + n)"),
     ("layout: residual start from the wrong query row", "h0_final.append(q_start[q] + n - 1)",
      "h0_final.append(q_start[q] + n)"),
