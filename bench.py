@@ -191,6 +191,13 @@ def work_model(inp, sh, single=False):
     def linear(M, K, N, out_bytes):
         return dict(flops=2.0 * M * K * N, bytes=float(M * K * e + N * K * e + out_bytes))
 
+    # every layer's cross K/V in one launch: the valid chunk rows of all
+    # passages projected by each layer's weights; pooled rows read once, the
+    # stacked weights once, every output row (padded ones written as 0) once
+    L = len(inp["layers"])
+    cross_kv = dict(flops=2.0 * L * int(C.sum()) * H * 2 * kv,
+                    bytes=float(D * Cmax * H * e + L * 2 * kv * H * e + D * Cmax * L * 2 * kv * e))
+
     if single:
         # one pruned layer: the queries' own rows and every pair's final row only
         nQ = len(lq)
@@ -208,7 +215,7 @@ def work_model(inp, sh, single=False):
                                             bytes=float(nQ * qd * e + nQ * (qd + nq) * 4 + cross_bytes
                                                         + P * qd * e)),
             "o_linear_last": linear(P, qd, H, P * H * 8),
-            "cross_kv": dict(flops=2.0 * int(C.sum()) * H * 2 * kv, bytes=float(D * Cmax * (H + 2 * kv) * e)),
+            "cross_kv": cross_kv,
             "chunk_pool": dict(flops=0.0, bytes=float(int(dl.sum()) * H * e + D * Cmax * H * e + D * T + D * Cmax
                                                       + 4 * D)),
             "gather_query_rows": dict(flops=0.0, bytes=float(U * H * (4 + 4 + 2))),
@@ -237,7 +244,7 @@ def work_model(inp, sh, single=False):
         # first layer: the residual source is each query's first hidden rows, read once
         "o_linear_first": linear(rows, qd, H, U * H * 4 + rows * H * (4 + (2 if e == 2 else 0))),
         "o_linear_last": linear(P, qd, H, P * H * 8),
-        "cross_kv": dict(flops=2.0 * int(C.sum()) * H * 2 * kv, bytes=float(D * Cmax * (H + 2 * kv) * e)),
+        "cross_kv": cross_kv,
         "chunk_pool": dict(flops=0.0, bytes=float(int(dl.sum()) * H * e + D * Cmax * H * e + D * T + D * Cmax + 4 * D)),
         # residual start: the queries' first hidden states read once, every pair row written fp32 + bf16
         "gather_rows": dict(flops=0.0, bytes=float(U * H * 4 + rows * H * (4 + (2 if e == 2 else 0)))),

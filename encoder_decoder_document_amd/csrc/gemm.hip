@@ -221,15 +221,44 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
       return *(const f32x4_t*)(Rsrc + src * N + n);
     }
   };
+  // PF_Y: piece i = j (32 / RPI) + rr / RPI of this lane's share of the fp32
+  // stream is row m0 + wm WTM + 32 j + rr + prow, columns n .. n + 3.  All NY
+  // pieces are loaded unconditionally, from the clamped in-range row and column
+  // (pieces outside the output are loaded but never stored), so that exactly NY
+  // vector loads follow the last k-tile's copies -- the wait at the last k-tile
+  // counts on that -- and no branch around them makes the compiler drain the
+  // copies first.  RES: each piece's source row is read in the prologue (the
+  // first k-tile's wait completes it), so the pieces' loads do not wait for an
+  // index load inside the k-loop; a source row outside [0, Rrows) is loaded
+  // from Y's own row instead and replaced by NaN in the epilogue (bit i of sbad).
   f32x4_t yold[PF_Y ? NY : 1];
+  int32_t srow[PF_Y && RES ? NY : 1];
+  uint32_t sbad = 0;
+  auto piece_row = [&](int i) { return m0 + wm * WTM + (i / (32 / RPI)) * 32 + (i % (32 / RPI)) * RPI + prow; };
+  if constexpr (PF_Y && RES) {
+    if (Rrow) {
+#pragma unroll
+      for (int i = 0; i < NY; ++i) srow[i] = Rrow[min(piece_row(i), M - 1)];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NY; ++i) srow[i] = min(piece_row(i), M - 1);
+    }
+  }
   auto load_yold = [&]() {
+    const int nc = min(n0 + wn * WTN + pcol, N - 4);
 #pragma unroll
-    for (int j = 0; j < FM; ++j)
-#pragma unroll
-      for (int rr = 0; rr < 32; rr += RPI) {
-        const int m = m0 + wm * WTM + j * 32 + rr + prow, n = n0 + wn * WTN + pcol;
-        yold[j * (32 / RPI) + rr / RPI] = (m < M && n < N) ? res_at(m, n) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NY; ++i) {
+      const int mc = min(piece_row(i), M - 1);
+      const float* yrow = (const float*)Y + (int64_t)mc * N + nc;
+      if constexpr (!RES) {
+        yold[i] = ld_out((const f32x4_t*)yrow);
+      } else {
+        const int64_t src = srow[i];
+        const bool bad = src < 0 || src >= Rrows;
+        sbad |= (uint32_t)bad << i;
+        yold[i] = *(const f32x4_t*)(bad ? yrow : Rsrc + src * N + nc);
       }
+    }
   };
   for (int kt = 0; kt < STAGES - 1 && kt < nk; ++kt) issue(kt);
   for (int kt = 0; kt < nk; ++kt) {
@@ -245,6 +274,14 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
       zero_k_tail<BM, BK>(cur, kidx(kt) * BK, K, tid, NT);
       zero_k_tail<BN, BK>(cur + BM * BK, kidx(kt) * BK, K, tid, NT);
       __syncthreads();
+    }
+    if constexpr (PF_Y && RES) {
+      // the source rows (read in the prologue) are complete at the first
+      // k-tile's wait: take them here, before more copies are in flight
+      if (kt == 0) {
+#pragma unroll
+        for (int i = 0; i < NY; ++i) asm volatile("" ::"v"(srow[i]));
+      }
     }
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
     if (PF_Y && kt == max(nk - 1 - GEMM_PF_DIST, 0)) load_yold();
@@ -287,6 +324,8 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
     }
   }
 
+  if (PF_Y && nk == 0) load_yold();  // a tile with no k-step (all rows masked) still adds to the stream
+
   // Epilogue through LDS: each wave parks 32 rows x WTN columns of its fp32
   // accumulator at a time (row stride padded by 16 bytes: conflict-free for
   // both the column-wise writes and the row-wise reads), then streams them out
@@ -324,7 +363,16 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
           st_out((u32x2_t*)((bf16_t*)Y + off), u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
         } else {
           f32x4_t* yp = (f32x4_t*)((float*)Y + off);
-          if (epi == EPI_F32_ACC) v += PF_Y ? yold[j * (32 / RPI) + rr / RPI] : res_at(m, n);
+          if (epi == EPI_F32_ACC) {
+            if constexpr (PF_Y) {
+              const int i = j * (32 / RPI) + rr / RPI;
+              v += yold[i];
+              if (RES && ((sbad >> i) & 1u))
+                v = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+            } else {
+              v += res_at(m, n);
+            }
+          }
           st_out(yp, v);
           if (Ybf) st_out((u32x2_t*)(Ybf + off), u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
         }
@@ -616,7 +664,14 @@ void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, v
     else
       hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 64, 2, 4, GEMM_PF_Y>), dim3(tiles), dim3(512), 0, s, X, W,
                          M, K, N, Y, epi, Y_bf16, rmask, Rsrc, Rrow, Rrows);
-  } else if (big_tiles >= 512 && GEMM_PERSIST) {  // never EPI_F32_ACC: no residual source here
+  } else if (big_tiles >= 512 && rmask) {
+    // rows with a zero mask byte (padded chunks of the cross projection) are
+    // written as 0: 128 x 128 tiles, a tile whose rows are all masked skips its
+    // k-loop (the persistent kernel below takes no mask)
+    const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 64, 2, 4>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y,
+                       epi, Y_bf16, rmask, Rsrc, Rrow, Rrows);
+  } else if (big_tiles >= 512 && GEMM_PERSIST) {  // never EPI_F32_ACC, never masked rows
     // persistent 256 x 256 tiles, one workgroup per CU
     const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
     const int grid = tiles < 256 ? ((tiles + 7) / 8) * 8 : 256;

@@ -51,7 +51,7 @@ kalm_status check_launch(const char* what) {
 
 extern "C" {
 
-int32_t kalm_version(void) { return 300; }
+int32_t kalm_version(void) { return 400; }
 
 const char* kalm_last_error(void) { return kalm::g_err; }
 
@@ -141,27 +141,44 @@ static kalm_status linear_impl(const char* fn, const void* X, const void* W, int
   return kalm::check_launch(fn);
 }
 
-kalm_status kalm_cross_kv(const void* pooled, const uint8_t* chunk_mask, int32_t D, int32_t Cmax, int32_t H,
-                          const void* Wkv, int32_t kv_dim, kalm_dtype dt, void* KVc, void* stream) {
+static kalm_status cross_kv_impl(const char* fn, const void* pooled, const uint8_t* chunk_mask, int32_t D,
+                                 int32_t Cmax, int32_t H, const void* Wkv, int32_t kv_dim, int32_t n_layers,
+                                 kalm_dtype dt, void* KVc, void* stream) {
   kalm::g_err[0] = 0;
-  KALM_REQUIRE(dt == KALM_F32 || dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "kalm_cross_kv: dtype %d", (int)dt);
-  KALM_REQUIRE(D >= 0 && Cmax >= 1 && H >= 1 && kv_dim >= 1, KALM_ERR_INVALID_ARG, "kalm_cross_kv: bad sizes");
-  KALM_REQUIRE((int64_t)D * Cmax < (1LL << 31), KALM_ERR_UNSUPPORTED, "kalm_cross_kv: too many rows");
-  KALM_REQUIRE(D == 0 || (pooled && Wkv && KVc), KALM_ERR_INVALID_ARG, "kalm_cross_kv: null pointer");
+  KALM_REQUIRE(dt == KALM_F32 || dt == KALM_BF16, KALM_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)dt);
+  KALM_REQUIRE(D >= 0 && Cmax >= 1 && H >= 1 && kv_dim >= 1 && n_layers >= 1, KALM_ERR_INVALID_ARG,
+               "%s: bad sizes", fn);
+  KALM_REQUIRE((int64_t)D * Cmax < (1LL << 31), KALM_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  KALM_REQUIRE((int64_t)2 * kv_dim * n_layers < (1LL << 31), KALM_ERR_UNSUPPORTED, "%s: too many columns", fn);
+  KALM_REQUIRE(D == 0 || (pooled && Wkv && KVc), KALM_ERR_INVALID_ARG, "%s: null pointer", fn);
   KALM_REQUIRE(ALIGNED16(pooled) && ALIGNED16(Wkv) && ALIGNED16(KVc), KALM_ERR_INVALID_ARG,
-               "kalm_cross_kv: pointers must be 16-byte aligned");
+               "%s: pointers must be 16-byte aligned", fn);
   KALM_REQUIRE(H % (dt == KALM_BF16 ? 8 : 4) == 0 && kv_dim % 4 == 0, KALM_ERR_UNSUPPORTED,
-               "kalm_cross_kv: H=%d / kv_dim=%d not aligned to the vector width", H, kv_dim);
+               "%s: H=%d / kv_dim=%d not aligned to the vector width", fn, H, kv_dim);
   KALM_DEVICE_OR_RETURN();
   if (D == 0) return KALM_OK;
-  const int M = D * Cmax, N = 2 * kv_dim;
+  // one GEMM over every layer's stacked weights: output row r holds, per layer,
+  // that layer's keys then values of pooled row r
+  const int M = D * Cmax, N = 2 * kv_dim * n_layers;
   if (dt == KALM_BF16)
     kalm::launch_linear_bf16((const bf16_t*)pooled, (const bf16_t*)Wkv, M, H, N, KVc, false, false, nullptr,
                              chunk_mask, (hipStream_t)stream);
   else
     kalm::launch_linear_f32((const float*)pooled, (const float*)Wkv, M, H, N, (float*)KVc, false, chunk_mask,
                             (hipStream_t)stream);
-  return kalm::check_launch("kalm_cross_kv");
+  return kalm::check_launch(fn);
+}
+
+kalm_status kalm_cross_kv(const void* pooled, const uint8_t* chunk_mask, int32_t D, int32_t Cmax, int32_t H,
+                          const void* Wkv, int32_t kv_dim, kalm_dtype dt, void* KVc, void* stream) {
+  return cross_kv_impl("kalm_cross_kv", pooled, chunk_mask, D, Cmax, H, Wkv, kv_dim, 1, dt, KVc, stream);
+}
+
+kalm_status kalm_cross_kv_layers(const void* pooled, const uint8_t* chunk_mask, int32_t D, int32_t Cmax, int32_t H,
+                                 const void* Wkv, int32_t kv_dim, int32_t n_layers, kalm_dtype dt, void* KVc,
+                                 void* stream) {
+  return cross_kv_impl("kalm_cross_kv_layers", pooled, chunk_mask, D, Cmax, H, Wkv, kv_dim, n_layers, dt, KVc,
+                       stream);
 }
 
 static kalm_status merged_attn_impl(const char* fn, const void* Q, int64_t q_ld, int64_t q_rows, const void* Ks,

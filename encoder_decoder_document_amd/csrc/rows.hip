@@ -12,38 +12,44 @@
 namespace {
 
 // One block.  Running exclusive prefix over the query lengths, 1024 queries
-// per step; the thread owning query q writes the entries of its D pairs.
+// per step; the thread owning query q writes the entries of its D pairs.  The
+// prefix is taken in int64: a pair whose rows would end past INT32_MAX gets
+// cu_q = final_row = h0_final = -1 (and cu_q[P] = -1 when the total overflows),
+// which the attention kernels skip and the readout turns into NaN, so an
+// oversized batch can never wrap row offsets into valid-looking rows.
 __global__ __launch_bounds__(1024) void pair_layout_kernel(const int32_t* __restrict__ lq, int nQ,
                                                            int nD, int32_t* __restrict__ cu_q,
                                                            int32_t* __restrict__ doc_of_pair,
                                                            int32_t* __restrict__ final_row,
                                                            int32_t* __restrict__ h0_final,
                                                            int32_t* __restrict__ cu_u) {
-  __shared__ int32_t scan[1024];
-  __shared__ int32_t carry;
+  constexpr int64_t LIM = 0x7fffffffLL;
+  __shared__ int64_t scan[1024];
+  __shared__ int64_t carry;
   if (threadIdx.x == 0) carry = 0;
   __syncthreads();
   for (int base = 0; base < nQ; base += 1024) {
     const int q = base + threadIdx.x;
-    const int32_t len = q < nQ ? lq[q] : 0;
+    const int64_t len = q < nQ ? (int64_t)lq[q] : 0;
     scan[threadIdx.x] = len;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {  // Hillis-Steele inclusive scan
-      const int32_t v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
+      const int64_t v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
       __syncthreads();
       scan[threadIdx.x] += v;
       __syncthreads();
     }
-    const int32_t start = carry + scan[threadIdx.x] - len;  // exclusive prefix of query rows
+    const int64_t start = carry + scan[threadIdx.x] - len;  // exclusive prefix of query rows
     if (q < nQ) {
-      if (cu_u) cu_u[q] = start;
+      if (cu_u) cu_u[q] = start + len <= LIM ? (int32_t)start : -1;
       for (int dd = 0; dd < nD; ++dd) {
         const int64_t p = (int64_t)q * nD + dd;
-        const int32_t r0 = nD * start + dd * len;
-        cu_q[p] = r0;
+        const int64_t r0 = (int64_t)nD * start + (int64_t)dd * len;
+        const bool ok = r0 + len <= LIM;
+        cu_q[p] = ok ? (int32_t)r0 : -1;
         doc_of_pair[p] = dd;
-        final_row[p] = r0 + len - 1;
-        if (h0_final) h0_final[p] = start + len - 1;
+        final_row[p] = ok ? (int32_t)(r0 + len - 1) : -1;
+        if (h0_final) h0_final[p] = ok ? (int32_t)(start + len - 1) : -1;
       }
     }
     __syncthreads();
@@ -51,8 +57,9 @@ __global__ __launch_bounds__(1024) void pair_layout_kernel(const int32_t* __rest
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    cu_q[(int64_t)nQ * nD] = nD * carry;
-    if (cu_u) cu_u[nQ] = carry;
+    const int64_t total = (int64_t)nD * carry;
+    cu_q[(int64_t)nQ * nD] = total <= LIM ? (int32_t)total : -1;
+    if (cu_u) cu_u[nQ] = carry <= LIM ? (int32_t)carry : -1;
   }
 }
 

@@ -34,6 +34,7 @@ _SIGS = {
     "kalm_pair_layout": (_i32, [_c_p, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _i64, _c_p, _c_p, _c_p]),
     "kalm_chunk_pool": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p]),
     "kalm_cross_kv": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _c_p, _i32, _i32, _c_p, _c_p]),
+    "kalm_cross_kv_layers": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _c_p, _i32, _i32, _i32, _c_p, _c_p]),
     "kalm_merged_attn": (_i32, [_c_p, _i64, _c_p, _c_p, _i64, _c_p, _i32, _i64, _i32, _c_p, _c_p, _i64,
                                 _c_p, _c_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_p, _i64, _c_p, _c_p]),
     "kalm_merged_attn_rows": (_i32, [_c_p, _i64, _i64, _c_p, _c_p, _i64, _i64, _c_p, _i32, _i32, _c_p, _c_p, _i64,
@@ -176,6 +177,21 @@ def kalm_cross_kv(pooled: torch.Tensor, chunk_mask: Optional[torch.Tensor], Wkv:
         out = torch.empty(D, C, 2 * kv_dim, dtype=pooled.dtype, device=pooled.device)
     _check("kalm_cross_kv", load().kalm_cross_kv(_ptr(pooled), _ptr(chunk_mask), D, C, H, _ptr(Wkv), kv_dim,
                                                 _dt(pooled), _ptr(out), _stream(stream)))
+    return out
+
+
+def kalm_cross_kv_layers(pooled: torch.Tensor, chunk_mask: Optional[torch.Tensor], Wkv: torch.Tensor, out=None,
+                         stream=None):
+    """pooled [D,C,H], Wkv [L,2*kv_dim,H] -> KVc [D,C,L,2*kv_dim] (every layer's keys then values per row,
+    one launch)."""
+    _contig(pooled, chunk_mask, Wkv)
+    D, C, H = pooled.shape
+    L, two_kv, _ = Wkv.shape
+    kv_dim = two_kv // 2
+    if out is None:
+        out = torch.empty(D, C, L, 2 * kv_dim, dtype=pooled.dtype, device=pooled.device)
+    _check("kalm_cross_kv_layers", load().kalm_cross_kv_layers(
+        _ptr(pooled), _ptr(chunk_mask), D, C, H, _ptr(Wkv), kv_dim, L, _dt(pooled), _ptr(out), _stream(stream)))
     return out
 
 

@@ -4,8 +4,8 @@
 kernels read them) and allocates every buffer the step writes, so the step
 itself only enqueues libkalm calls on the current stream:
 
-  kalm_pair_layout -> kalm_chunk_pool -> kalm_cross_kv (one per layer, shared by
-  every query) -> kalm_gather_rows (each pair's residual stream starts from its
+  kalm_pair_layout -> kalm_chunk_pool -> kalm_cross_kv_layers (every layer's cross
+  K/V in one launch, shared by every query) -> kalm_gather_rows (each pair's residual stream starts from its
   query's first hidden state) -> per layer: kalm_linear (fused Q/K/V), kalm_merged_attn,
   kalm_linear (output projection added to the fp32 residual, bf16 copy for the
   next layer) -> kalm_yesno_score.  With ``prune`` the residual start is fused
@@ -70,7 +70,7 @@ class DeviceBatch:
     lq: torch.Tensor
     h0: torch.Tensor
     Wqkv: List[torch.Tensor]
-    Wkvc: List[torch.Tensor]
+    Wkvc: torch.Tensor          # [L, 2*kv, H]: every layer's cross K/V weights
     Wo: List[torch.Tensor]
     w_yesno: torch.Tensor
     # buffers written by the step
@@ -97,7 +97,7 @@ def upload(inputs: Dict[str, object], device="cuda", n_layers: Optional[int] = N
         return torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dtype)
 
     Wqkv = [dev(np.concatenate([W["Wq"], W["Wk"], W["Wv"]], 0)) for W in layers]
-    Wkvc = [dev(np.concatenate([W["Wkc"], W["Wvc"]], 0)) for W in layers]
+    Wkvc = dev(np.stack([np.concatenate([W["Wkc"], W["Wvc"]], 0) for W in layers]))
     Wo = [dev(W["Wo"]) for W in layers]
     buf = dict(
         cu_q=torch.empty(P + 1, dtype=torch.int32, device=device),
@@ -108,7 +108,8 @@ def upload(inputs: Dict[str, object], device="cuda", n_layers: Optional[int] = N
         pooled=torch.empty(D, Cmax, H, dtype=dt, device=device),
         chunk_mask=torch.empty(D, Cmax, dtype=torch.uint8, device=device),
         n_chunks=torch.empty(D, dtype=torch.int32, device=device),
-        kvc=torch.empty(L, D, Cmax, 2 * kv, dtype=dt, device=device),
+        # cross K/V of every layer, row-major by passage chunk: [D, Cmax, L, 2*kv]
+        kvc=torch.empty(D, Cmax, L, 2 * kv, dtype=dt, device=device),
         h=torch.empty(rows, H, dtype=torch.float32, device=device),
         qkv=torch.empty(rows, nqkv, dtype=dt, device=device),
         o=torch.empty(rows, sh.nq * sh.d, dtype=dt, device=device),
@@ -202,9 +203,15 @@ def front(b: DeviceBatch, stream=None, rec=_no_rec, h0_rows: bool = True):
     with rec("chunk_pool"):
         ops.kalm_chunk_pool(b.x, b.token_mask, b.chunk, out=(B["pooled"], B["chunk_mask"], B["n_chunks"]),
                             stream=stream)
-    for l in range(b.n_layers):
-        with rec("cross_kv"):
-            ops.kalm_cross_kv(B["pooled"], B["chunk_mask"], b.Wkvc[l], out=B["kvc"][l], stream=stream)
+    with rec("cross_kv"):
+        ops.kalm_cross_kv_layers(B["pooled"], B["chunk_mask"], b.Wkvc, out=B["kvc"], stream=stream)
+
+
+def cross_layer(b: DeviceBatch, l: int) -> torch.Tensor:
+    """Layer l's cross K/V [D*Cmax, 2*kv] (keys then values), a row-strided view of
+    the all-layer buffer."""
+    kv2 = 2 * b.nkv * b.d
+    return b.buf["kvc"].view(b.D * b.Cmax, b.n_layers * kv2)[:, l * kv2:(l + 1) * kv2]
 
 
 def pruned(b: DeviceBatch, prune: bool = True) -> bool:
@@ -240,7 +247,7 @@ def decoder(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, reuse_
     scale = 1.0 / math.sqrt(b.d)
     last_pruned = pruned(b, prune)
     for l in range(b.n_layers):
-        kvc = B["kvc"][l].view(b.D * b.Cmax, 2 * kv)
+        kvc = cross_layer(b, l)
         x_in = B["hb"] if bf else B["h"]
         if prune and l == 0:
             # the queries' own rows: one Q/K/V projection per query row, shared by its passages
@@ -370,7 +377,7 @@ def decoder_model(b: DeviceBatch, stream=None, rec=_no_rec, prune: bool = True, 
             ops.kalm_gather_rows(b.h0, B["h0_row"], dst=B["h"], stream=stream)
     qkv = B["qkv"]
     for l in range(b.n_layers):
-        kvc = B["kvc"][l].view(b.D * b.Cmax, 2 * kv)
+        kvc = cross_layer(b, l)
         cross = (kvc[:, :kv], kvc[:, kv:], B["chunk_mask"], B["doc_of_pair"], b.nq, b.nkv, b.d)
         if prune and l == 0:
             # the queries' own rows: norm, Q/K/V, RoPE once per query row

@@ -57,7 +57,7 @@ typedef enum { KALM_F32 = 0, KALM_BF16 = 1 } kalm_dtype;
 
 /* Library version, major*10000 + minor*100 + patch (0.2.0: split attention,
  * one-layer final rows, layer parts; 0.3.0: fused gate/up projection and
- * activation). */
+ * activation; 0.4.0: every layer's cross K/V in one call, 64-bit pair layout). */
 int32_t kalm_version(void);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
@@ -83,6 +83,11 @@ kalm_status kalm_device_check(void);
  *             (the query's last row in the per-query packing)
  *   cu_u      [n_queries+1] int32 out, nullable: row offsets of the per-query
  *             packing itself (cu_u[0] = 0; the layout with n_docs = 1)
+ * Row offsets are computed in 64 bits on the device (the lengths live there).
+ * A pair whose rows would extend past INT32_MAX gets cu_q = final_row =
+ * h0_final = -1, and cu_q[P] (cu_u[n_queries]) is -1 when the total does not
+ * fit: the attention entry points skip such pairs and kalm_yesno_score gives
+ * them NaN, so an oversized batch never wraps into valid-looking rows.
  */
 kalm_status kalm_pair_layout(const int32_t* lq, int32_t n_queries, int32_t n_docs,
                              int32_t* cu_q, int32_t* doc_of_pair, int32_t* final_row,
@@ -127,6 +132,29 @@ kalm_status kalm_chunk_pool(const void* x, const uint8_t* token_mask, int32_t D,
 kalm_status kalm_cross_kv(const void* pooled, const uint8_t* chunk_mask, int32_t D, int32_t Cmax,
                           int32_t H, const void* Wkv, int32_t kv_dim, kalm_dtype dt, void* KVc,
                           void* stream);
+
+/*
+ * a2 for every layer of a stack at once ([MLX] What this is: the cross K/V of
+ * the cached passage encodings; each layer has its own projection and the
+ * pooled vectors are shared by all layers): one GEMM over the layers' stacked
+ * weights, the same arithmetic as n_layers calls of kalm_cross_kv.
+ *   KVc[r, l, 0:kv_dim]        = pooled[r] . Wkv[l, 0:kv_dim]^T          (keys)
+ *   KVc[r, l, kv_dim:2*kv_dim] = pooled[r] . Wkv[l, kv_dim:2*kv_dim]^T   (values)
+ *
+ *   pooled    [D*Cmax, H] dtype dt
+ *   chunk_mask [D*Cmax] uint8, nullable: rows whose mask byte is 0 are written as
+ *             0 for every layer (whole tiles of such rows are not computed)
+ *   Wkv       [n_layers, 2*kv_dim, H] dtype dt (each layer in [out, in] layout)
+ *   KVc       [D*Cmax, n_layers, 2*kv_dim] dtype dt out: layer l's keys of row r
+ *             start at element (r*n_layers + l)*2*kv_dim, so a layer's K (or V)
+ *             is a view with row stride n_layers*2*kv_dim elements (the c_ld of
+ *             kalm_merged_attn)
+ * Requires H % 8 == 0 (bf16) or H % 4 == 0 (f32), kv_dim % 4 == 0, n_layers >= 1,
+ * 2*kv_dim*n_layers < 2^31.
+ */
+kalm_status kalm_cross_kv_layers(const void* pooled, const uint8_t* chunk_mask, int32_t D, int32_t Cmax,
+                                 int32_t H, const void* Wkv, int32_t kv_dim, int32_t n_layers, kalm_dtype dt,
+                                 void* KVc, void* stream);
 
 /*
  * a3 -- merged self+cross attention ([MLX] What this is: one scaled-dot-product

@@ -26,9 +26,61 @@ def declared_symbols():
 
 def test_header_declares_the_hot_path_calls():
     syms = declared_symbols()
-    for s in ("kalm_chunk_pool", "kalm_cross_kv", "kalm_merged_attn", "kalm_yesno_score", "kalm_linear",
-              "kalm_pair_layout", "kalm_gather_rows", "kalm_last_error", "kalm_version", "kalm_device_check"):
+    for s in ("kalm_chunk_pool", "kalm_cross_kv", "kalm_cross_kv_layers", "kalm_merged_attn", "kalm_yesno_score",
+              "kalm_linear", "kalm_pair_layout", "kalm_gather_rows", "kalm_last_error", "kalm_version",
+              "kalm_device_check"):
         assert s in syms
+
+
+def declared_params(name):
+    """Parameter names of one declaration in the header, in order."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    params = [p.strip() for p in m.group(1).split(",")]
+    return [re.findall(r"[A-Za-z_][A-Za-z0-9_]*", p)[-1] for p in params if p and p != "void"]
+
+
+# The five boundary calls: their planned parameter lists (the names the hot
+# path's steps fix), the lists as built, and every departure between them --
+# each one is listed with its reason in the design notes.  A change to a
+# signature fails here until the departure is recorded.
+PLANNED = {
+    "kalm_chunk_pool": "x token_mask D T H chunk dt pooled chunk_mask n_chunks s",
+    "kalm_cross_kv": "pooled n_chunks D Cmax H Wk Wv kv_dim dt Kc Vc s",
+    "kalm_merged_attn": "Q Ks Vs cu_q P Kc Vc chunk_mask doc_of_pair Cmax nq nkv d scale dt O lse s",
+    "kalm_yesno_score": "h final_row P H w_yesno w_dt yes no margin score s",
+    "kalm_linear": "X x_dt W M K N Y y_dt accumulate_fp32 s",
+}
+BUILT = {
+    "kalm_chunk_pool": "x token_mask D T H chunk dt pooled chunk_mask n_chunks stream",
+    "kalm_cross_kv": "pooled chunk_mask D Cmax H Wkv kv_dim dt KVc stream",
+    "kalm_merged_attn": "Q q_ld Ks Vs kv_ld cu_q P rows max_lq Kc Vc c_ld chunk_mask doc_of_pair D Cmax nq nkv d "
+                        "scale dt O o_ld lse stream",
+    "kalm_yesno_score": "h h_dt h_ld rows final_row P H w_yesno w_dt yes no margin score stream",
+    "kalm_linear": "X W M K N dt Y y_dt accumulate Y_bf16 stream",
+}
+# (planned names not kept, built names added)
+DEPARTURES = {
+    "kalm_chunk_pool": ({"s"}, {"stream"}),
+    "kalm_cross_kv": ({"n_chunks", "Wk", "Wv", "Kc", "Vc", "s"}, {"chunk_mask", "Wkv", "KVc", "stream"}),
+    "kalm_merged_attn": ({"s"}, {"q_ld", "kv_ld", "rows", "max_lq", "c_ld", "D", "o_ld", "stream"}),
+    "kalm_yesno_score": ({"s"}, {"h_dt", "h_ld", "rows", "stream"}),
+    "kalm_linear": ({"x_dt", "accumulate_fp32", "s"}, {"dt", "accumulate", "Y_bf16", "stream"}),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PLANNED))
+def test_boundary_parameter_lists(name):
+    got = declared_params(name)
+    assert got == BUILT[name].split(), f"{name}: {got}"
+    planned = set(PLANNED[name].split())
+    dropped, added = DEPARTURES[name]
+    assert planned - set(got) == dropped, f"{name}: undocumented departure {planned - set(got)}"
+    assert set(got) - planned == added, f"{name}: undocumented addition {set(got) - planned}"
+    # every kept name keeps its relative order
+    kept = [p for p in got if p in planned]
+    assert kept == [p for p in PLANNED[name].split() if p in set(got)], name
 
 
 @needs_lib
@@ -48,7 +100,7 @@ def test_binding_covers_every_declared_symbol():
 def test_invalid_arguments_rejected_before_launch():
     from encoder_decoder_document_amd import ops
     lib = ops.load()
-    assert lib.kalm_version() == 300
+    assert lib.kalm_version() == 400
     # chunk = 0
     st = lib.kalm_chunk_pool(None, None, 1, 8, 64, 0, ops.KALM_BF16, None, None, None, None)
     assert st == ops.KALM_ERR_INVALID_ARG and b"chunk" in lib.kalm_last_error()

@@ -39,6 +39,34 @@ def test_pair_layout_bit_exact(lq, D):
         assert np.array_equal(got[k].cpu().numpy(), ref[k]), k
 
 
+def test_pair_layout_overflow_marks_pairs_invalid():
+    # row offsets past INT32_MAX never wrap: such pairs get -1 offsets (the
+    # attention skips them, the readout gives NaN); the rest are exact
+    _announce("pair_layout int32 overflow")
+    lq = np.array([1 << 29, (1 << 29) - 3, 5], np.int32)
+    D = 3
+    got = ops.kalm_pair_layout(to_dev(lq, torch.int32), D, with_h0_row=False)
+    torch.cuda.synchronize()
+    lim = (1 << 31) - 1
+    start = np.concatenate([[0], np.cumsum(lq.astype(np.int64))])
+    cu, fin, h0f = [], [], []
+    for q in range(len(lq)):
+        for d in range(D):
+            r0 = D * int(start[q]) + d * int(lq[q])
+            ok = r0 + int(lq[q]) <= lim
+            cu.append(r0 if ok else -1)
+            fin.append(r0 + int(lq[q]) - 1 if ok else -1)
+            h0f.append(int(start[q]) + int(lq[q]) - 1 if ok else -1)
+    total = D * int(start[-1])
+    cu.append(total if total <= lim else -1)
+    assert -1 in cu and cu[0] == 0
+    assert got["cu_q"].cpu().tolist() == cu
+    assert got["final_row"].cpu().tolist() == fin
+    assert got["h0_final"].cpu().tolist() == h0f
+    assert got["doc_of_pair"].cpu().tolist() == [p % D for p in range(len(lq) * D)]
+    assert got["cu_u"].cpu().tolist() == [int(v) for v in start]
+
+
 # ------------------------------------------------------------------ a1 pooling
 def _pool_case(seed, D, T, H, chunk, bf16, general_mask=False, lens=None):
     x = synth.normal(seed, (D, T, H), 1.0, bf16)
@@ -117,6 +145,49 @@ def test_cross_kv_parity(D, C, H, kv, bf16):
     assert not got[cm == 0].any()
 
 
+def test_cross_kv_masked_rows_zero_on_the_big_tile_path():
+    # >= 512 tiles of 256 x 256 (D = 100 passages of 256 chunks, 2 kv = 2048):
+    # rows whose chunk mask is 0 are exactly 0 even though the pooled rows
+    # behind them hold non-zero values; the valid rows match the oracle
+    _announce("cross_kv masked, big-tile shape")
+    D, C, H, kv = 100, 256, 640, 1024
+    pooled = synth.normal(90, (D, C, H), 1.0, True)          # padded rows non-zero on purpose
+    n_valid = synth.integers(91, 0, C, D)
+    n_valid[:3] = [0, 128, 256]
+    cm = (np.arange(C)[None] < n_valid[:, None]).astype(np.uint8)
+    cm[5, ::3] = 0                                            # a general mask in one passage
+    W = synth.normal(92, (2 * kv, H), 0.02, True)
+    got = to_np(ops.kalm_cross_kv(to_dev(pooled, torch.bfloat16), to_dev(cm, torch.uint8),
+                                  to_dev(W, torch.bfloat16)))
+    torch.cuda.synchronize()
+    assert not got[cm == 0].any(), "masked chunk rows must be written as 0"
+    valid = cm != 0
+    K, V = oracle.cross_kv(pooled[valid], W[:kv], W[kv:])
+    assert_close(got[valid], np.concatenate([K, V], -1), *BF16_TOL, "KVc valid rows")
+
+
+@pytest.mark.parametrize("D,C,H,kv,L,bf16", [(7, 37, 640, 256, 3, True), (50, 256, 1152, 256, 6, True),
+                                             (8, 16, 64, 32, 2, False)])
+def test_cross_kv_layers_parity(D, C, H, kv, L, bf16):
+    # every layer's cross K/V in one launch equals each layer's projection
+    # (layer l at columns [l 2kv, (l+1) 2kv) of every output row); masked rows 0
+    _announce(f"cross_kv_layers D={D} C={C} H={H} kv={kv} L={L} bf16={bf16}")
+    pooled = synth.normal(93 + D, (D, C, H), 1.0, bf16)
+    cm = synth.bernoulli_mask(94 + D, 0.6, (D, C))
+    cm[0] = 0
+    W = synth.normal(95 + D, (L, 2 * kv, H), 0.02, bf16)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    got = to_np(ops.kalm_cross_kv_layers(to_dev(pooled, dt), to_dev(cm, torch.uint8), to_dev(W, dt)))
+    torch.cuda.synchronize()
+    assert got.shape == (D, C, L, 2 * kv)
+    assert not got[cm == 0].any()
+    valid = cm != 0
+    atol, rtol = BF16_TOL if bf16 else F32_TOL
+    for l in range(L):
+        K, V = oracle.cross_kv(pooled[valid], W[l, :kv], W[l, kv:])
+        assert_close(got[valid][:, l], np.concatenate([K, V], -1), atol, rtol, f"KVc layer {l}")
+
+
 # ------------------------------------------------------------------ a5 linear
 @pytest.mark.parametrize("M,K,N,mode", [(1000, 1152, 1536, "bf16"), (300, 1024, 1152, "acc"),
                                         (77, 200, 136, "f32out"), (513, 640, 1536, "bf16"),
@@ -124,7 +195,9 @@ def test_cross_kv_parity(D, C, H, kv, bf16):
                                         # large enough for the big-tile paths (>= 512 tiles of 256 x 256),
                                         # ragged in M, and a K that is not a multiple of 64
                                         (22093, 1152, 1536, "bf16"), (22093, 1024, 1152, "acc"), (40003, 1024, 1152, "acc"),
-                                        (88001, 1000, 1536, "bf16")])
+                                        (88001, 1000, 1536, "bf16"),
+                                        # the residual update's big-tile path with a ragged last column tile
+                                        (40003, 1024, 1160, "acc")])
 def test_linear_parity(M, K, N, mode):
     _announce(f"linear M={M} K={K} N={N} mode={mode}")
     bf = mode in ("bf16", "acc", "f32out")
@@ -154,6 +227,7 @@ def test_linear_parity(M, K, N, mode):
 
 
 @pytest.mark.parametrize("M,K,N,bf,indexed", [(300, 1024, 1152, True, True), (40003, 1024, 1152, True, True),
+                                               (40003, 1024, 1160, True, True),
                                                (22093, 1024, 1152, True, False), (33, 36, 20, False, True)])
 def test_linear_residual_parity(M, K, N, bf, indexed):
     """Y = R[r_row] + X W^T: the residual update starting from gathered rows
@@ -669,7 +743,10 @@ def test_gated_gelu_parity(M, I, bf16):
     assert_close(to_np(A), ref, *(BF16_TOL if bf16 else F32_TOL), "gated_gelu")
 
 
-@pytest.mark.parametrize("M,K,I", [(300, 200, 128), (513, 640, 384), (1, 64, 256), (1100, 1152, 768)])
+@pytest.mark.parametrize("M,K,I", [(300, 200, 128), (513, 640, 384), (1, 64, 256), (1100, 1152, 768),
+                                   # more tiles than workgroups: the persistent loop carries its copy
+                                   # ring across tiles (with a K tail)
+                                   (20000, 1000, 1536)])
 def test_linear_gated_gelu_parity(M, K, I):
     # the fused gate/up projection + activation against fp64 products of the
     # same bf16 operands: ragged M, a K tail (K % 64 != 0), several 128-unit blocks
