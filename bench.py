@@ -94,6 +94,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     ap.add_argument("--no-pool-long", action="store_true", help="skip the pooling measurement at the 1024x2560 shape")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other workloads (Nano single layer, Nano stack, Long/wide) measured after the "
+                         "headline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -322,6 +325,75 @@ def pool_long(torch, ops, reps=20):
             "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": by}
 
 
+def kernel_table(dur, work, steps, sh):
+    """Per recorded call: launches per step, average duration, and against its
+    algorithmic work the achieved rate and roofline fractions."""
+    kernels = {}
+    for k, v in dur.items():
+        n_per = len(v) / steps
+        avg_us = float(np.mean(v)) * 1e3
+        ent = {"launches_per_step": n_per, "avg_us": avg_us, "total_ms_per_step": float(np.sum(v)) / steps}
+        if k in work:
+            w = work[k]
+            if w["flops"] > 0:
+                ent["tflops"] = w["flops"] / (avg_us * 1e-6) / 1e12
+                ent["mfma_frac"] = ent["tflops"] / (PEAK_BF16_TFLOPS if sh.dtype == "bf16" else PEAK_F32_TFLOPS)
+            ent["gbs"] = w["bytes"] / (avg_us * 1e-6) / 1e9
+            ent["hbm_frac"] = ent["gbs"] / PEAK_HBM_GBS
+        kernels[k] = ent
+    return kernels
+
+
+def other_workload(torch, stack, synth, idx, steps, warmup, graph):
+    """Pairs/s of one more workload (eager steps, and replays of the step
+    captured as a HIP graph when ``graph``), with its merged attention's
+    useful-flop rate and the per-kernel split."""
+    sh = synth.SHAPES[idx]
+    print(f"[bench] other workload {sh.name}: generating", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(idx, nan_padding=False)
+    b = stack.upload(inp)
+    for _ in range(warmup):
+        stack.step(b)
+    torch.cuda.synchronize()
+    # pairs/s from plain eager steps; per-kernel times from as many more steps
+    # with HIP events around each call (recording them costs host time that
+    # would count against the microsecond steps of the small workloads)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        stack.step(b)
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / steps
+    rec = EventRec(torch)
+    for _ in range(steps):
+        stack.step(b, rec=rec)
+    single = sh.n_layers == 1
+    kernels = kernel_table(rec.durations_ms(), work_model(inp, sh, single=single), steps, sh)
+    ent = {"workload": sh.name, "queries": sh.n_queries, "docs": sh.n_docs, "pairs": sh.pairs,
+           "layers": sh.n_layers, "hidden": sh.H, "q_heads": sh.nq, "kv_heads": sh.nkv, "head_dim": sh.d,
+           "steps": steps, "warmup": warmup, "ms_per_step": el * 1e3, "value": sh.pairs / el, "unit": "pairs/s",
+           "merged_attn": attn_summary(kernels, work_model(inp, sh, single=single), sh),
+           "kernels": {k: {kk: round(vv, 6) if isinstance(vv, float) else vv for kk, vv in v.items()}
+                       for k, v in kernels.items()}}
+    if graph:
+        g = stack.StepGraph(b)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        n = max(steps, 20)
+        t0 = time.perf_counter()
+        for _ in range(n):
+            g.replay()
+        torch.cuda.synchronize()
+        gl = (time.perf_counter() - t0) / n
+        ent["graph"] = {"replays": n, "ms_per_step": gl * 1e3, "value": sh.pairs / gl, "unit": "pairs/s"}
+        del g
+    print(f"[bench] other workload {sh.name}: {el * 1e3:.3f} ms/step, {sh.pairs / el:.1f} pairs/s",
+          file=sys.stderr, flush=True)
+    del b
+    torch.cuda.empty_cache()
+    return ent
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -407,23 +479,12 @@ def main():
     work = work_model(inp, sh, single=single)
     if inp.get("model"):
         model_work(inp, sh, work, single=single)
-    kernels = {}
-    for k, v in dur.items():
-        n_per = len(v) / a.steps
-        avg_us = float(np.mean(v)) * 1e3
-        ent = {"launches_per_step": n_per, "avg_us": avg_us, "total_ms_per_step": float(np.sum(v)) / a.steps}
-        if k in work:
-            w = work[k]
-            if w["flops"] > 0:
-                ent["tflops"] = w["flops"] / (avg_us * 1e-6) / 1e12
-                ent["mfma_frac"] = ent["tflops"] / (PEAK_BF16_TFLOPS if sh.dtype == "bf16" else PEAK_F32_TFLOPS)
-            ent["gbs"] = w["bytes"] / (avg_us * 1e-6) / 1e9
-            ent["hbm_frac"] = ent["gbs"] / PEAK_HBM_GBS
+    kernels = kernel_table(dur, work, a.steps, sh)
+    for k, ent in kernels.items():
         tb = traffic_bytes(k)
         if tb is not None:
             ent["hbm_traffic_bytes"] = tb
             ent["traffic_over_algorithmic"] = tb / work[k]["bytes"] if k in work else None
-        kernels[k] = ent
     dom = max((k for k in kernels if k in work), key=lambda k: kernels[k]["total_ms_per_step"])
     w = work[dom]
     ai = w["flops"] / w["bytes"] if w["bytes"] else float("inf")
@@ -435,7 +496,11 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": kernels[dom]["gbs"] / PEAK_HBM_GBS}
     roof.update({"traffic": traffic_bytes(dom), "algorithmic_flops_per_launch": w["flops"],
-                 "algorithmic_bytes_per_launch": w["bytes"], "arith_intensity": ai, "avg_us": kernels[dom]["avg_us"]})
+                 "algorithmic_bytes_per_launch": w["bytes"], "arith_intensity": ai, "avg_us": kernels[dom]["avg_us"],
+                 # the same launch against the other roof (its flops against the MFMA peak, or its bytes
+                 # against the HBM peak)
+                 "other_roof": ({"bound": "mfma", "frac": kernels[dom].get("mfma_frac")} if roof["bound"] == "hbm"
+                                else {"bound": "hbm", "frac": kernels[dom].get("hbm_frac")})})
     out = {
         "metric": METRIC, "value": pairs_s, "unit": "pairs/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -461,6 +526,13 @@ def main():
         out["pool_long"] = pool_long(torch, ops)
     del b
     torch.cuda.empty_cache()
+    if not a.no_others and a.workload == "small_stack26_bf16" and a.chunk is None and not a.mlp_dim:
+        # the other workloads, each timed on its own after the headline: the
+        # one-layer and the Nano stack also as HIP-graph replays (their
+        # kernels run for microseconds), Long/wide with few steps (4 s each)
+        out["others"] = [other_workload(torch, stack, synth, 1, 20, 3, True),
+                         other_workload(torch, stack, synth, 2, 10, 2, True),
+                         other_workload(torch, stack, synth, 4, 2, 1, False)]
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, sh, a.cpu_seconds)
