@@ -5,8 +5,17 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "kalm_common.h"
+
+// Device scratch of kalm_merged_attn_split_noalloc: the split-KV partials
+// (o, lse of every share) live here instead of in a caller workspace.  Each
+// GPU the library runs on holds its own copy from module load until the
+// process ends; in host code `scratch` names a host-side stand-in, never
+// the device memory -- kernels get the address from hipGetSymbolAddress.
+#define KALM_NOALLOC_SCRATCH_BYTES (16u << 20)
+static __device__ __align__(256) uint8_t scratch[KALM_NOALLOC_SCRATCH_BYTES];
 
 namespace kalm {
 
@@ -36,6 +45,34 @@ kalm_status check_device() {
     return set_error(KALM_ERR_NO_DEVICE, "device %d is %s; libkalm is built for gfx950 only", dev,
                      prop.gcnArchName);
   ok.store(1, std::memory_order_relaxed);
+  return KALM_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (each GPU has its own copy at its own
+// address) and kept; KALM_ERR_NO_DEVICE / KALM_ERR_LAUNCH with a message if
+// there is no current device or the lookup fails.
+static kalm_status noalloc_scratch(void** out) {
+  constexpr int MAXDEV = 64;
+  static std::mutex mu;
+  static void* addr[MAXDEV] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAXDEV) {
+    (void)hipGetLastError();
+    return set_error(KALM_ERR_NO_DEVICE, "kalm_merged_attn_split_noalloc: no current HIP device below %d", MAXDEV);
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return set_error(KALM_ERR_LAUNCH, "kalm_merged_attn_split_noalloc: scratch address lookup failed: %s",
+                       hipGetErrorString(e));
+    }
+    addr[dev] = p;
+  }
+  *out = addr[dev];
   return KALM_OK;
 }
 
@@ -311,6 +348,30 @@ kalm_status kalm_merged_attn_split(const void* Q, int64_t q_ld, int64_t q_rows, 
                           max_lq, Kc, Vc, c_ld, chunk_mask, doc_of_pair, D, Cmax, nq, nkv, d, scale, dt, O, o_ld,
                           o_rows, lse, row_mode, stream, 3, o_self, s_ld, lse_self, n_split, workspace,
                           workspace_bytes);
+}
+
+kalm_status kalm_merged_attn_split_noalloc(const void* Q, int64_t q_ld, int64_t q_rows, const float* o_self,
+                                           int64_t s_ld, const float* lse_self, const int32_t* cu_q, int32_t P,
+                                           int32_t max_lq, const void* Kc, const void* Vc, int64_t c_ld,
+                                           const uint8_t* chunk_mask, const int32_t* doc_of_pair, int32_t D,
+                                           int32_t Cmax, int32_t nq, int32_t nkv, int32_t d, float scale,
+                                           kalm_dtype dt, void* O, int64_t o_ld, int64_t o_rows, float* lse,
+                                           int32_t row_mode, int32_t n_split, void* stream) {
+  const char* fn = "kalm_merged_attn_split_noalloc";
+  kalm::g_err[0] = 0;
+  KALM_REQUIRE(n_split >= 1 && n_split <= 64 && o_rows >= 0 && nq >= 1 && d >= 1, KALM_ERR_INVALID_ARG,
+               "%s: bad n_split / o_rows / nq / d", fn);
+  const int64_t need = (int64_t)n_split * o_rows * nq * (d + 1) * 4;
+  KALM_REQUIRE(need <= (int64_t)KALM_NOALLOC_SCRATCH_BYTES, KALM_ERR_INVALID_ARG,
+               "%s: the split partials need %lld bytes, more than the %u-byte static scratch (lower n_split or "
+               "split the batch)", fn, (long long)need, (unsigned)KALM_NOALLOC_SCRATCH_BYTES);
+  KALM_DEVICE_OR_RETURN();
+  void* ws = nullptr;
+  const kalm_status st = kalm::noalloc_scratch(&ws);
+  if (st != KALM_OK) return st;
+  return merged_attn_impl(fn, Q, q_ld, q_rows, nullptr, nullptr, 0, INT64_MAX, cu_q, P, max_lq, Kc, Vc, c_ld,
+                          chunk_mask, doc_of_pair, D, Cmax, nq, nkv, d, scale, dt, O, o_ld, o_rows, lse, row_mode,
+                          stream, 3, o_self, s_ld, lse_self, n_split, ws, (int64_t)KALM_NOALLOC_SCRATCH_BYTES);
 }
 
 kalm_status kalm_rms_norm(const void* x, kalm_dtype x_dt, int64_t x_ld, int64_t M, int32_t H, const void* w,

@@ -48,6 +48,9 @@ _SIGS = {
     "kalm_merged_attn_split": (_i32, [_c_p, _i64, _i64, _c_p, _i64, _c_p, _c_p, _i32, _i32, _c_p, _c_p, _i64, _c_p,
                                       _c_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_p, _i64, _i64, _c_p, _i32,
                                       _i32, _c_p, _i64, _c_p]),
+    "kalm_merged_attn_split_noalloc": (_i32, [_c_p, _i64, _i64, _c_p, _i64, _c_p, _c_p, _i32, _i32, _c_p, _c_p, _i64,
+                                              _c_p, _c_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_p, _i64, _i64,
+                                              _c_p, _i32, _i32, _c_p]),
     "kalm_rms_norm": (_i32, [_c_p, _i32, _i64, _i64, _i32, _c_p, _i32, _f32, _c_p, _i32, _i64, _c_p]),
     "kalm_rope": (_i32, [_c_p, _i32, _i64, _i64, _i32, _i32, _i32, _c_p, _i32, _i32, _i32, _f32, _c_p]),
     "kalm_gated_gelu": (_i32, [_c_p, _i32, _i64, _i64, _i32, _c_p, _i64, _c_p]),
@@ -320,6 +323,32 @@ def kalm_merged_attn_split(Q: torch.Tensor, o_self: torch.Tensor, lse_self: torc
         _ptr(Kc), _ptr(Vc), Kc.stride(0), _ptr(chunk_mask), _ptr(doc_of_pair), D, Cmax, nq, nkv, d, float(scale),
         _dt(Q), _ptr(out), out.stride(0), o_rows, _ptr(lse), int(row_mode), int(n_split), _ptr(workspace), ws_bytes,
         _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # the static split-KV scratch of kalm_merged_attn_split_noalloc
+
+
+def kalm_merged_attn_split_noalloc(Q: torch.Tensor, o_self: torch.Tensor, lse_self: torch.Tensor,
+                                   cu_q: torch.Tensor, max_lq: int, Kc: torch.Tensor, Vc: torch.Tensor,
+                                   chunk_mask: torch.Tensor, doc_of_pair: torch.Tensor, nq: int, nkv: int, d: int,
+                                   row_mode: int, o_rows: int, n_split: int, out: torch.Tensor,
+                                   scale: Optional[float] = None, lse: Optional[torch.Tensor] = None, stream=None):
+    """kalm_merged_attn_split with the split partials in the library's static device scratch
+    (no workspace, nothing allocated by the call; ``out`` is required).  Calls that overlap on
+    one GPU race on the scratch."""
+    for t in (Q, o_self, Kc, Vc):
+        if t.stride(-1) != 1:
+            raise ValueError("unit column stride required")
+    _contig(lse_self)
+    P = cu_q.numel() - 1
+    D, Cmax = chunk_mask.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check("kalm_merged_attn_split_noalloc", load().kalm_merged_attn_split_noalloc(
+        _ptr(Q), Q.stride(0), Q.shape[0], _ptr(o_self), o_self.stride(0), _ptr(lse_self), _ptr(cu_q), P, max_lq,
+        _ptr(Kc), _ptr(Vc), Kc.stride(0), _ptr(chunk_mask), _ptr(doc_of_pair), D, Cmax, nq, nkv, d, float(scale),
+        _dt(Q), _ptr(out), out.stride(0), o_rows, _ptr(lse), int(row_mode), int(n_split), _stream(stream)))
     return out
 
 

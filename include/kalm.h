@@ -298,6 +298,32 @@ kalm_status kalm_merged_attn_split(const void* Q, int64_t q_ld, int64_t q_rows, 
                                    int64_t workspace_bytes, void* stream);
 
 /*
+ * kalm_merged_attn_split_noalloc -- kalm_merged_attn_split for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the split partials live in a
+ * static 16 MiB device array inside the library instead of a caller
+ * workspace, and the call allocates and frees nothing.  Each GPU the library
+ * runs on holds its own copy of the array from library load until the process
+ * ends; its address is looked up once per device, on the first call made with
+ * that device current.
+ *   Limit: n_split * o_rows * nq * (d + 1) * 4 <= 16 MiB (16777216 bytes);
+ *          a larger request returns KALM_ERR_INVALID_ARG before anything is
+ *          launched.
+ *   Every scratch slot the merge reads is written by the same call first, so
+ *   the array needs no clearing; it keeps the last call's partials.
+ *   Calls that overlap in time on one GPU (different streams or host threads
+ *   without ordering between them) share the array and race: order them.
+ * Other arguments, results and errors as kalm_merged_attn_split.
+ */
+kalm_status kalm_merged_attn_split_noalloc(const void* Q, int64_t q_ld, int64_t q_rows, const float* o_self,
+                                           int64_t s_ld, const float* lse_self, const int32_t* cu_q, int32_t P,
+                                           int32_t max_lq, const void* Kc, const void* Vc, int64_t c_ld,
+                                           const uint8_t* chunk_mask, const int32_t* doc_of_pair, int32_t D,
+                                           int32_t Cmax, int32_t nq, int32_t nkv, int32_t d, float scale,
+                                           kalm_dtype dt, void* O, int64_t o_ld, int64_t o_rows, float* lse,
+                                           int32_t row_mode, int32_t n_split, void* stream);
+
+/*
  * Decoder-layer completion (a model-shaped layer around a3).  The pages say the
  * forward pass reads every dim, head count, layer count and RoPE parameter from
  * the model's config, RoPE inverse frequencies computed from it ("KaLM-Reranker

@@ -158,6 +158,10 @@ def test_invalid_arguments_rejected_before_launch():
     assert st == ops.KALM_ERR_INVALID_ARG and b"n_split" in lib.kalm_last_error()
     st = lib.kalm_merged_attn_split(*args[:20], ops.KALM_F32, *args[21:], 2, 16, need, None)
     assert st == ops.KALM_ERR_UNSUPPORTED
+    # the no-allocation split: partials larger than its static scratch are refused before any launch
+    big = args[:23] + (1 << 20,) + args[24:]
+    st = lib.kalm_merged_attn_split_noalloc(*big, 64, None)
+    assert st == ops.KALM_ERR_INVALID_ARG and b"static scratch" in lib.kalm_last_error()
     # gathered residual: no source; without an index the source needs M rows
     st = lib.kalm_linear_residual(16, 16, 10, 64, 64, ops.KALM_BF16, None, None, 10, 16, None, None)
     assert st == ops.KALM_ERR_INVALID_ARG and b"residual source" in lib.kalm_last_error()
