@@ -188,15 +188,23 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   const int r = lane & 31, g = lane >> 5;
   const int G = nq / nkv, HG = G / NH;
 
-  // Work order for L2 reuse: pair-major, the pair's head groups and row
-  // blocks consecutive (they share the pair's self K/V and the passage's cross
-  // K/V), and each XCD (block b runs on XCD b % 8) walks a contiguous range.
+  // Work order for L2 reuse: the pair's head groups and row blocks
+  // consecutive (they share the pair's self K/V and the passage's cross K/V);
+  // passage-major -- every query's pair with passage 0, then with passage 1,
+  // ... (pair p = q D + passage in the layout of kalm_pair_layout), so one
+  // passage's cross K/V stays in L2 across the queries -- and each XCD (block
+  // b runs on XCD b % 8) walks a contiguous range.
   const int64_t per_pair = (int64_t)nkv * HG * nqb;
   const int64_t total = (int64_t)P * per_pair;
   const int64_t b = blockIdx.x;
   const int64_t xper = total / 8;
   const int64_t t = (b < xper * 8) ? (b % 8) * xper + b / 8 : b;
-  const int p = (int)(t / per_pair);
+  const int64_t pi = t / per_pair;  // pair in walk order
+  int p = (int)pi;
+  if (D > 0 && P % D == 0) {
+    const int64_t nQ = P / D;
+    p = (int)((pi % nQ) * D + pi / nQ);
+  }
   const int64_t rem = t % per_pair;
   const int qb = (int)(rem % nqb);
   const int hgi = (int)(rem / nqb);
@@ -205,6 +213,7 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   const PairRows pr = pair_rows(cu_q, p, D, MODE, q_rows, kv_rows, o_rows);
   if (!pr.ok || qb * RB >= pr.nrow) return;
   const int Lq = pr.Lq, nrow = pr.nrow, pos0 = pr.pos0;
+
   const int doc = PART == 1 ? 0 : doc_of_pair[p];  // a self partial reads no passage
   const bool bad_doc = PART != 1 && (doc < 0 || doc >= D);
 
@@ -212,12 +221,46 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   // the words of tiles l and l + 64 (one ballot per 64 chunks); word t is
   // read back with a scalar readlane
   const int n_ct_all = (PART == 1 || bad_doc) ? 0 : (Cmax + BKV - 1) / BKV;
+  const int nc = min(n_ct_all * BKV, Cmax);  // chunks whose mask bytes are read
+  const uint8_t* cmd = cmask + (int64_t)(bad_doc ? 0 : doc) * Cmax;
+  // The first 256 chunks' mask bytes, loaded together from clamped in-range
+  // addresses and before the Q loads: taking them then waits for these four
+  // loads only (the vector memory counter completes in issue order), and the
+  // Q loads' latency runs on under the ballots below.
+  uint32_t pre[4] = {0, 0, 0, 0};
+  if (nc > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pre[i] = cmd[min(64 * i + lane, nc - 1)];
+  }
+  asm volatile("" ::: "memory");  // the Q loads below stay after these
+
+  const int h = kvh * G + hg * NH + wave / WPH;
+  const int qr0 = qb * RB + (wave % WPH) * 32 * RT;  // first handled query row of this wave
+  // row tile u of this wave: rows qr0 + 32u + (0..31); lane r holds one row
+  int pos[RT], tile_first[RT];
+#pragma unroll
+  for (int u = 0; u < RT; ++u) {
+    pos[u] = pos0 + min(qr0 + 32 * u + r, nrow - 1);  // its self position: sees self keys 0..pos
+    tile_first[u] = pos0 + qr0 + 32 * u;
+  }
+  const int wave_last = pos0 + min(qr0 + 32 * RT - 1, nrow - 1);
+
+  // Q fragments (MFMA B operand of S^T = K Q^T): 16 k-steps of 16 dims per
+  // row tile.
+  bf16x8_t qf[RT][HD / 16];
+#pragma unroll
+  for (int u = 0; u < RT; ++u) {
+    const bf16_t* qp = Q + (pr.q0 + min(qr0 + 32 * u + r, nrow - 1)) * q_ld + (int64_t)h * HD + 8 * g;
+#pragma unroll
+    for (int s = 0; s < HD / 16; ++s) qf[u][s] = ATTN_LD_Q((const bf16x8_t*)(qp + 16 * s));
+  }
+  // the mask bytes are taken only here, after the Q loads have gone out
+  asm volatile("" : "+v"(pre[0]), "+v"(pre[1]), "+v"(pre[2]), "+v"(pre[3])::"memory");
+
   uint32_t cmw0 = 0, cmw1 = 0;
   {
-    const uint8_t* cmd = cmask + (int64_t)(bad_doc ? 0 : doc) * Cmax;
-    for (int base = 0; base < n_ct_all * BKV; base += 64) {
-      const int c = base + lane;
-      const uint64_t bits = __ballot(c < Cmax && cmd[c] != 0);
+    // word pair of one 64-chunk ballot: tile index w = base / 32 and w + 1
+    auto put = [&](int base, uint64_t bits) {
       const int w = base >> 5;  // tile index of the low word
       if (lane == (w & 63)) {
         if (w < 64) cmw0 = (uint32_t)bits; else cmw1 = (uint32_t)bits;
@@ -225,7 +268,11 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
       if (lane == ((w + 1) & 63)) {
         if (w + 1 < 64) cmw0 = (uint32_t)(bits >> 32); else cmw1 = (uint32_t)(bits >> 32);
       }
-    }
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (64 * i < nc) put(64 * i, __ballot(64 * i + lane < nc && pre[i] != 0));
+    for (int base = 256; base < nc; base += 64) put(base, __ballot(base + lane < nc && cmd[base + lane] != 0));
   }
   auto cm_word = [&](int t) -> uint32_t {  // t is wave-uniform
     return t < 64 ? __builtin_amdgcn_readlane(cmw0, t) : __builtin_amdgcn_readlane(cmw1, t - 64);
@@ -246,26 +293,6 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
     const int tps = (n_ct_all + (int)gridDim.y - 1) / (int)gridDim.y;
     ct0 = (int)blockIdx.y * tps;
     n_ct = max(0, min(n_ct, ct0 + tps) - ct0);
-  }
-
-  const int h = kvh * G + hg * NH + wave / WPH;
-  const int qr0 = qb * RB + (wave % WPH) * 32 * RT;  // first handled query row of this wave
-  // row tile u of this wave: rows qr0 + 32u + (0..31); lane r holds one row
-  int pos[RT], tile_first[RT];
-#pragma unroll
-  for (int u = 0; u < RT; ++u) {
-    pos[u] = pos0 + min(qr0 + 32 * u + r, nrow - 1);  // its self position: sees self keys 0..pos
-    tile_first[u] = pos0 + qr0 + 32 * u;
-  }
-  const int wave_last = pos0 + min(qr0 + 32 * RT - 1, nrow - 1);
-
-  // Q fragments (MFMA B operand of S^T = K Q^T): 16 k-steps of 16 dims per row tile
-  bf16x8_t qf[RT][HD / 16];
-#pragma unroll
-  for (int u = 0; u < RT; ++u) {
-    const bf16_t* qp = Q + (pr.q0 + min(qr0 + 32 * u + r, nrow - 1)) * q_ld + (int64_t)h * HD + 8 * g;
-#pragma unroll
-    for (int s = 0; s < HD / 16; ++s) qf[u][s] = ATTN_LD_Q((const bf16x8_t*)(qp + 16 * s));
   }
 
   f32x16_t oacc[RT][HD / 32];

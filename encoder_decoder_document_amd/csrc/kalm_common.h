@@ -32,10 +32,13 @@ __device__ __forceinline__ float gated_gelu_tanh(float x, float u) {
 __device__ __forceinline__ float from_bf16(bf16_t b) { return (float)b; }
 
 // Pack two floats into one dword of two bf16 (lo = a, hi = b).
+// Two floats -> two bf16 in one word (a in the low half), round to nearest
+// even: a two-element vector conversion, which is one v_cvt_pk_bf16_f32
+// (converting the halves one by one costs two conversions, a shift and an or).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  bf16_t x = to_bf16(a), y = to_bf16(b);
-  uint16_t xs = __builtin_bit_cast(uint16_t, x), ys = __builtin_bit_cast(uint16_t, y);
-  return (uint32_t)xs | ((uint32_t)ys << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v_t{a, b}, bf16x2_t));
 }
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
