@@ -44,30 +44,38 @@ RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop/byte where the tw
 # taken -- after any change to that file the traffic is reported as null.
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 MEASURED_TRAFFIC = {
-    # profiles/hbm_traffic_small_stack26_bf16.md (the QKV figures are the mean over the
-    # 24 full-height QKV launches only; the same kernel symbol also runs the last layer's K/V)
-    "o_linear": {"src": "fa920d3086110191496affc9dbd53c74b65ac665467d78862e3bae729afcb7b2",
-                 "fetch_kib": 3108944.8, "write_kib": 6443341.3},
-    "qkv_linear": {"src": "fa920d3086110191496affc9dbd53c74b65ac665467d78862e3bae729afcb7b2",
-                   "fetch_kib": 2499455.5, "write_kib": 2688300.7},
-    "merged_attn": {"src": "d023e09b64933b7bdcf470d8636c772140c73148c65c5983dee392dacce3f01f",
-                    "fetch_kib": 1484128.2, "write_kib": 1792200.0},
+    # profiles/hbm_traffic_small_stack26_bf16.md (the QKV figures are the mean over the full-height
+    # launches only; the same kernel symbol also runs the last layer's K/V projection)
+    "qkv_linear": {"src": "e2d3b55eb3b8809eceeef7898ada9b0cb567f74202d4ba6b3979ac2026ec1d0a", "fetch_kib": 2445031.5, "write_kib": 2688309.2},
+    "o_linear": {"src": "e2d3b55eb3b8809eceeef7898ada9b0cb567f74202d4ba6b3979ac2026ec1d0a", "fetch_kib": 3124174.3, "write_kib": 6529342.6},
+    "merged_attn": {"src": "4dd2c9a07ef556bc91925ada8ccf5aac3547f94fda267b91b5b8e944e546d2c4", "fetch_kib": 1348980.6, "write_kib": 1792200.0},
 }
-KERNEL_SRC = {"o_linear": "gemm.hip", "qkv_linear": "gemm.hip", "cross_kv": "gemm.hip",
-              "merged_attn": "attn_bf16.h", "chunk_pool": "pool.hip", "gather_rows": "rows.hip"}
+# the source files each kernel is built from (headers included); their joint
+# sha256 keys the stored counter values
+KERNEL_SRC = {"o_linear": ("gemm.hip", "kalm_common.h"), "qkv_linear": ("gemm.hip", "kalm_common.h"),
+              "cross_kv": ("gemm.hip", "kalm_common.h"),
+              "merged_attn": ("attn.hip", "attn_bf16.h", "kalm_common.h"),
+              "chunk_pool": ("pool.hip", "kalm_common.h"), "gather_rows": ("rows.hip", "kalm_common.h")}
+
+
+def source_sha(kernel):
+    """sha256 over the source files a kernel is built from (None if unknown)."""
+    import hashlib
+    srcs = KERNEL_SRC.get(kernel)
+    if not srcs:
+        return None
+    h = hashlib.sha256()
+    for src in srcs:
+        with open(os.path.join(ROOT, "encoder_decoder_document_amd", "csrc", src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_bytes(kernel):
     """Counter-measured HBM bytes per launch, or None when stale or not measured."""
-    import hashlib
     m = MEASURED_TRAFFIC.get(kernel)
-    src = KERNEL_SRC.get(kernel)
-    if not m or not src:
+    if not m or m["src"] != source_sha(kernel):
         return None
-    path = os.path.join(ROOT, "encoder_decoder_document_amd", "csrc", src)
-    with open(path, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != m["src"]:
-            return None
     return m["fetch_kib"] * 1024 * FETCH_FACTOR + m["write_kib"] * 1024 * WRITE_FACTOR
 METRIC = "scored query-passage pairs/s (1 GPU) + merged-attn MFMA util % / pool HBM GB/s"
 

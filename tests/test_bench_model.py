@@ -75,18 +75,24 @@ def test_single_layer_model_counts_final_rows_only():
 
 def test_counter_traffic_goes_stale_with_the_source(monkeypatch):
     import hashlib
+    for k in bench.KERNEL_SRC:
+        h = hashlib.sha256()
+        for src in bench.KERNEL_SRC[k]:
+            h.update(open(os.path.join(ROOT, "encoder_decoder_document_amd", "csrc", src), "rb").read())
+        assert bench.source_sha(k) == h.hexdigest()
     for k, m in bench.MEASURED_TRAFFIC.items():
         t = bench.traffic_bytes(k)
-        path = os.path.join(ROOT, "encoder_decoder_document_amd", "csrc", bench.KERNEL_SRC[k])
-        current = hashlib.sha256(open(path, "rb").read()).hexdigest() == m["src"]
         # figures taken on this source, scaled by the copy calibration; none once the source changed
-        if current:
+        if bench.source_sha(k) == m["src"]:
             assert t == m["fetch_kib"] * 1024 * bench.FETCH_FACTOR + m["write_kib"] * 1024 * bench.WRITE_FACTOR
         else:
             assert t is None
-    stale = {k: dict(v, src="0" * 64) for k, v in bench.MEASURED_TRAFFIC.items()}
-    monkeypatch.setattr(bench, "MEASURED_TRAFFIC", stale)
-    assert all(bench.traffic_bytes(k) is None for k in stale)
+    # a stored figure keyed to other sources is stale: reported as null
+    fake = {"o_linear": {"src": "0" * 64, "fetch_kib": 1.0, "write_kib": 1.0},
+            "merged_attn": {"src": bench.source_sha("merged_attn"), "fetch_kib": 2.0, "write_kib": 3.0}}
+    monkeypatch.setattr(bench, "MEASURED_TRAFFIC", fake)
+    assert bench.traffic_bytes("o_linear") is None
+    assert bench.traffic_bytes("merged_attn") == 2.0 * 1024 * bench.FETCH_FACTOR + 3.0 * 1024 * bench.WRITE_FACTOR
     assert bench.traffic_bytes("no_such_kernel") is None
 
 
