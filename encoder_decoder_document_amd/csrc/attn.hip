@@ -26,11 +26,16 @@ __global__ __launch_bounds__(256) void merged_attn_f32_kernel(
   const int h = (int)((blk / nrb) % nq);
   const int p = (int)(blk / ((int64_t)nrb * nq));
   const PairRows pr = pair_rows(cu_q, p, D, mode, q_rows, kv_rows, o_rows);
-  if (!pr.ok || i >= pr.nrow) return;
+  if (!pr.ok) {
+    if (lane == 0) KALM_DBG(KALM_DBG_PAIR_ROWS);
+    return;
+  }
+  if (i >= pr.nrow) return;
   const int pos = pr.pos0 + i;  // self position of this query row
   const int kvh = h / (nq / nkv);
   const int doc = part == 1 ? 0 : doc_of_pair[p];
   const bool bad_doc = part != 1 && (doc < 0 || doc >= D);
+  if (bad_doc && lane == 0) KALM_DBG(KALM_DBG_DOC);
   constexpr int MAXJ = 4;  // d <= 256
   const int nj = (d + 63) / 64;
   float q[MAXJ], acc[MAXJ];
@@ -96,7 +101,10 @@ __global__ __launch_bounds__(256) void split_merge_kernel(
     float* __restrict__ lse) {
   const int p = blockIdx.x, h = blockIdx.y;
   const PairRows pr = pair_rows(cu_q, p, D, mode, q_rows, INT64_MAX, o_rows);
-  if (!pr.ok) return;
+  if (!pr.ok) {
+    if (threadIdx.x == 0) KALM_DBG(KALM_DBG_PAIR_ROWS);
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t dim0 = (int64_t)h * HD + 4 * lane;
   for (int i = wave; i < pr.nrow; i += 4) {
@@ -122,6 +130,8 @@ __global__ __launch_bounds__(256) void split_merge_kernel(
 }
 
 }  // namespace
+
+KALM_DBG_TAKE_DEFINE(dbg_take_attn)
 
 namespace kalm {
 

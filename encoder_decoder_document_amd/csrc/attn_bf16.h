@@ -211,11 +211,16 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   const int kvh = hgi / HG, hg = hgi % HG;
 
   const PairRows pr = pair_rows(cu_q, p, D, MODE, q_rows, kv_rows, o_rows);
-  if (!pr.ok || qb * RB >= pr.nrow) return;
+  if (!pr.ok) {
+    if (threadIdx.x == 0) KALM_DBG(KALM_DBG_PAIR_ROWS);
+    return;
+  }
+  if (qb * RB >= pr.nrow) return;
   const int Lq = pr.Lq, nrow = pr.nrow, pos0 = pr.pos0;
 
   const int doc = PART == 1 ? 0 : doc_of_pair[p];  // a self partial reads no passage
   const bool bad_doc = PART != 1 && (doc < 0 || doc >= D);
+  if (bad_doc && threadIdx.x == 0) KALM_DBG(KALM_DBG_DOC);
 
   // cross-tile validity words, kept in registers by every wave: lane l holds
   // the words of tiles l and l + 64 (one ballot per 64 chunks); word t is

@@ -216,8 +216,10 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
       return ld_out((const f32x4_t*)((const float*)Y + (int64_t)m * N + n));
     } else {
       const int64_t src = Rrow ? (int64_t)Rrow[m] : (int64_t)m;
-      if (src < 0 || src >= Rrows)
+      if (src < 0 || src >= Rrows) {
+        KALM_DBG(KALM_DBG_SRC_ROW);
         return f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      }
       return *(const f32x4_t*)(Rsrc + src * N + n);
     }
   };
@@ -325,6 +327,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
   }
 
   if (PF_Y && nk == 0) load_yold();  // a tile with no k-step (all rows masked) still adds to the stream
+  if (RES && PF_Y && sbad) KALM_DBG(KALM_DBG_SRC_ROW);
 
   // Epilogue through LDS: each wave parks 32 rows x WTN columns of its fp32
   // accumulator at a time (row stride padded by 16 bytes: conflict-free for
@@ -633,6 +636,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
     const bool row_ok = rmask ? rmask[m] != 0 : true;
     const int64_t src = Rrow ? (int64_t)Rrow[m] : (int64_t)m;
     const bool src_ok = !Rsrc || (src >= 0 && src < Rrows);
+    if (accumulate && !src_ok && tx == 0) KALM_DBG(KALM_DBG_SRC_ROW);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + tx * 4 + j;
@@ -646,6 +650,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }
 
 }  // namespace
+
+KALM_DBG_TAKE_DEFINE(dbg_take_gemm)
 
 namespace kalm {
 

@@ -76,9 +76,32 @@ static kalm_status noalloc_scratch(void** out) {
   return KALM_OK;
 }
 
-kalm_status check_launch(const char* what) {
+kalm_status check_launch(const char* what, void* stream) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(KALM_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+#ifdef KALM_DEBUG
+  const hipError_t se = hipStreamSynchronize((hipStream_t)stream);
+  if (se != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(KALM_ERR_LAUNCH, "%s: kernel failed: %s", what, hipGetErrorString(se));
+  }
+  const uint32_t w = dbg_take_rows() | dbg_take_gemm() | dbg_take_attn() | dbg_take_layer();
+  if (w) {
+    static const char* const names[] = {"pair rows outside the row counts", "passage index outside [0, D)",
+                                        "residual source row outside [0, r_rows)", "gather index outside [0, n_src)",
+                                        "final row outside [0, rows)", "RoPE row outside [0, rows)",
+                                        "pair layout past INT32_MAX"};
+    char buf[320];
+    size_t n = 0;
+    buf[0] = 0;
+    for (int b = 0; b < 7; ++b)
+      if ((w >> b) & 1u) n += snprintf(buf + n, sizeof(buf) - n, "%s%s", n ? "; " : "", names[b]);
+    if (w & 0x80000000u) snprintf(buf + n, sizeof(buf) - n, "%sguard word unreadable", n ? "; " : "");
+    return set_error(KALM_ERR_BOUNDS, "%s: bounds guard fired: %s", what, buf);
+  }
+#else
+  (void)stream;
+#endif
   return KALM_OK;
 }
 
@@ -89,6 +112,14 @@ kalm_status check_launch(const char* what) {
 extern "C" {
 
 int32_t kalm_version(void) { return 400; }
+
+int32_t kalm_debug_build(void) {
+#ifdef KALM_DEBUG
+  return 1;
+#else
+  return 0;
+#endif
+}
 
 const char* kalm_last_error(void) { return kalm::g_err; }
 
@@ -106,7 +137,7 @@ kalm_status kalm_pair_layout(const int32_t* lq, int32_t n_queries, int32_t n_doc
   KALM_DEVICE_OR_RETURN();
   kalm::launch_pair_layout(lq, n_queries, n_docs, cu_q, doc_of_pair, final_row, h0_row, rows, h0_final, cu_u,
                            (hipStream_t)stream);
-  return kalm::check_launch("kalm_pair_layout");
+  return kalm::check_launch("kalm_pair_layout", stream);
 }
 
 kalm_status kalm_chunk_pool(const void* x, const uint8_t* token_mask, int32_t D, int32_t T, int32_t H,
@@ -124,7 +155,7 @@ kalm_status kalm_chunk_pool(const void* x, const uint8_t* token_mask, int32_t D,
   if (D == 0) return KALM_OK;
   const int Cmax = (T + chunk - 1) / chunk;
   kalm::launch_chunk_pool(x, token_mask, D, T, H, chunk, Cmax, dt, pooled, chunk_mask, n_chunks, (hipStream_t)stream);
-  return kalm::check_launch("kalm_chunk_pool");
+  return kalm::check_launch("kalm_chunk_pool", stream);
 }
 
 static kalm_status linear_impl(const char* fn, const void* X, const void* W, int32_t M, int32_t K, int32_t N,
@@ -175,7 +206,7 @@ static kalm_status linear_impl(const char* fn, const void* X, const void* W, int
   else
     kalm::launch_linear_f32((const float*)X, (const float*)W, M, K, N, (float*)Y, accumulate != 0, nullptr,
                             (hipStream_t)stream, R, r_row, r_rows);
-  return kalm::check_launch(fn);
+  return kalm::check_launch(fn, stream);
 }
 
 static kalm_status cross_kv_impl(const char* fn, const void* pooled, const uint8_t* chunk_mask, int32_t D,
@@ -203,7 +234,7 @@ static kalm_status cross_kv_impl(const char* fn, const void* pooled, const uint8
   else
     kalm::launch_linear_f32((const float*)pooled, (const float*)Wkv, M, H, N, (float*)KVc, false, chunk_mask,
                             (hipStream_t)stream);
-  return kalm::check_launch(fn);
+  return kalm::check_launch(fn, stream);
 }
 
 kalm_status kalm_cross_kv(const void* pooled, const uint8_t* chunk_mask, int32_t D, int32_t Cmax, int32_t H,
@@ -292,7 +323,7 @@ static kalm_status merged_attn_impl(const char* fn, const void* Q, int64_t q_ld,
                                  kv_rows, o_rows, row_mode, max_lq, (const float*)Kc, (const float*)Vc, c_ld,
                                  chunk_mask, doc_of_pair, D, Cmax, nq, nkv, d, scale, (float*)O, o_ld, lse, part,
                                  oi, oi_ld, lsei, (hipStream_t)stream);
-  return kalm::check_launch(fn);
+  return kalm::check_launch(fn, stream);
 }
 
 kalm_status kalm_merged_attn(const void* Q, int64_t q_ld, const void* Ks, const void* Vs, int64_t kv_ld,
@@ -390,7 +421,7 @@ kalm_status kalm_rms_norm(const void* x, kalm_dtype x_dt, int64_t x_ld, int64_t 
   KALM_DEVICE_OR_RETURN();
   kalm::launch_rms_norm(x, x_dt == KALM_BF16, x_ld, M, H, w, w_dt == KALM_BF16, eps, y, y_dt == KALM_BF16, y_ld,
                         (hipStream_t)stream);
-  return kalm::check_launch("kalm_rms_norm");
+  return kalm::check_launch("kalm_rms_norm", stream);
 }
 
 kalm_status kalm_rope(void* X, kalm_dtype dt, int64_t ld, int64_t rows, int32_t col0, int32_t n_heads, int32_t d,
@@ -411,7 +442,7 @@ kalm_status kalm_rope(void* X, kalm_dtype dt, int64_t ld, int64_t rows, int32_t 
   KALM_DEVICE_OR_RETURN();
   kalm::launch_rope(X, dt == KALM_BF16, ld, rows, col0, n_heads, d, cu, n_seq, max_len, row_mode, theta,
                     (hipStream_t)stream);
-  return kalm::check_launch("kalm_rope");
+  return kalm::check_launch("kalm_rope", stream);
 }
 
 kalm_status kalm_gated_gelu(const void* Y, kalm_dtype dt, int64_t y_ld, int64_t M, int32_t I, void* A, int64_t a_ld,
@@ -425,7 +456,7 @@ kalm_status kalm_gated_gelu(const void* Y, kalm_dtype dt, int64_t y_ld, int64_t 
   KALM_REQUIRE(ALIGNED16(Y) && ALIGNED16(A), KALM_ERR_INVALID_ARG, "kalm_gated_gelu: pointers must be 16-byte aligned");
   KALM_DEVICE_OR_RETURN();
   kalm::launch_gated_gelu(Y, dt == KALM_BF16, y_ld, M, I, A, a_ld, (hipStream_t)stream);
-  return kalm::check_launch("kalm_gated_gelu");
+  return kalm::check_launch("kalm_gated_gelu", stream);
 }
 
 kalm_status kalm_linear_gated_gelu(const void* X, const void* Wg, const void* Wu, int32_t M, int32_t K, int32_t I,
@@ -442,7 +473,7 @@ kalm_status kalm_linear_gated_gelu(const void* X, const void* Wg, const void* Wu
   KALM_DEVICE_OR_RETURN();
   kalm::launch_linear_gelu_bf16((const bf16_t*)X, (const bf16_t*)Wg, (const bf16_t*)Wu, M, K, I, (bf16_t*)A,
                                 (hipStream_t)stream);
-  return kalm::check_launch("kalm_linear_gated_gelu");
+  return kalm::check_launch("kalm_linear_gated_gelu", stream);
 }
 
 kalm_status kalm_yesno_score(const void* h, kalm_dtype h_dt, int64_t h_ld, int64_t rows, const int32_t* final_row,
@@ -458,7 +489,7 @@ kalm_status kalm_yesno_score(const void* h, kalm_dtype h_dt, int64_t h_ld, int64
   if (P == 0) return KALM_OK;
   kalm::launch_yesno(h, h_dt == KALM_BF16, h_ld, rows, final_row, P, H, w_yesno, w_dt == KALM_BF16, yes, no, margin,
                      score, (hipStream_t)stream);
-  return kalm::check_launch("kalm_yesno_score");
+  return kalm::check_launch("kalm_yesno_score", stream);
 }
 
 kalm_status kalm_gather_rows(const float* src, const int32_t* idx, int64_t M, int32_t H, int64_t n_src, float* dst,
@@ -472,7 +503,7 @@ kalm_status kalm_gather_rows(const float* src, const int32_t* idx, int64_t M, in
   KALM_DEVICE_OR_RETURN();
   if (M == 0) return KALM_OK;
   kalm::launch_gather_rows(src, idx, M, H, n_src, dst, (bf16_t*)dst_bf16, (hipStream_t)stream);
-  return kalm::check_launch("kalm_gather_rows");
+  return kalm::check_launch("kalm_gather_rows", stream);
 }
 
 kalm_status kalm_rank_topn(const float* score, int32_t n_queries, int32_t n_docs, int32_t top_n,
@@ -486,7 +517,7 @@ kalm_status kalm_rank_topn(const float* score, int32_t n_queries, int32_t n_docs
   KALM_DEVICE_OR_RETURN();
   if (n_queries == 0 || top_n == 0) return KALM_OK;
   kalm::launch_rank_topn(score, n_queries, n_docs, top_n, out_index, out_score, (hipStream_t)stream);
-  return kalm::check_launch("kalm_rank_topn");
+  return kalm::check_launch("kalm_rank_topn", stream);
 }
 
 }  // extern "C"

@@ -159,12 +159,62 @@ __device__ __forceinline__ void wait_dma_ktile(int later) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// ------------------------------------------------------ debug-build guards
+// The kernels' own guards on data-dependent indexes -- a pair whose rows fall
+// outside the given row counts, a passage index outside [0, D), a residual
+// source row, gathered row or final row outside its array, a RoPE row outside
+// X, a pair layout past INT32_MAX -- keep every access in bounds in every
+// build (the work is skipped or its outputs are NaN).  Built with -DKALM_DEBUG
+// (libkalm_debug.so), a guard that fires also sets its bit in a device word of
+// its translation unit; every entry point of that build then synchronises its
+// stream and turns a set bit into KALM_ERR_BOUNDS.  Release builds compile the
+// reports out, so their kernels are unchanged.
+enum : uint32_t {
+  KALM_DBG_PAIR_ROWS = 1u,   // a pair's Q, K/V or O rows outside the row counts
+  KALM_DBG_DOC = 2u,         // doc_of_pair outside [0, D)
+  KALM_DBG_SRC_ROW = 4u,     // residual source row outside [0, r_rows)
+  KALM_DBG_GATHER = 8u,      // gather index outside [0, n_src)
+  KALM_DBG_FINAL_ROW = 16u,  // final row outside [0, rows)
+  KALM_DBG_ROPE_ROW = 32u,   // RoPE row outside [0, rows)
+  KALM_DBG_LAYOUT = 64u,     // pair layout offset past INT32_MAX
+};
+#ifdef KALM_DEBUG
+static __device__ uint32_t kalm_dbg_word;
+#define KALM_DBG(bit) atomicOr(&kalm_dbg_word, (uint32_t)(bit))
+// Host: this translation unit's guard word on the current device, read and
+// cleared (the caller has synchronised the stream that ran the kernels).
+#define KALM_DBG_TAKE_DEFINE(name)                                                        \
+  namespace kalm {                                                                        \
+  uint32_t name() {                                                                       \
+    uint32_t v = 0, z = 0;                                                                \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(kalm_dbg_word), sizeof(v)) != hipSuccess ||   \
+        hipMemcpyToSymbol(HIP_SYMBOL(kalm_dbg_word), &z, sizeof(z)) != hipSuccess) {      \
+      (void)hipGetLastError();                                                            \
+      return 0x80000000u;                                                                 \
+    }                                                                                     \
+    return v;                                                                             \
+  }                                                                                       \
+  }
+namespace kalm {
+uint32_t dbg_take_rows();
+uint32_t dbg_take_gemm();
+uint32_t dbg_take_attn();
+uint32_t dbg_take_layer();
+}  // namespace kalm
+#else
+#define KALM_DBG(bit) ((void)0)
+#define KALM_DBG_TAKE_DEFINE(name)
+#endif
+
 // ---------------------------------------------------------------- host side
 namespace kalm {
 
 kalm_status set_error(kalm_status st, const char* fmt, ...);
 kalm_status check_device();
-kalm_status check_launch(const char* what);
+// After the launches of entry point `what` on `stream`: a launch error is
+// KALM_ERR_LAUNCH; in the debug build the stream is also synchronised (a
+// kernel fault is reported against `what`) and a fired guard is KALM_ERR_BOUNDS.
+kalm_status check_launch(const char* what, void* stream);
 
 }  // namespace kalm
 

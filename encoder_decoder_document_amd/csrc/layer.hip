@@ -86,7 +86,10 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ X, int64_t ld
     row = s;
     pos = len - 1;
   }
-  if (row < 0 || row >= rows) return;
+  if (row < 0 || row >= rows) {
+    KALM_DBG(KALM_DBG_ROPE_ROW);
+    return;
+  }
   T* base = X + row * ld + col0 + (int64_t)head * d;
   const f32x4_t a = ld4(base + i0), b = ld4(base + i0 + d / 2);
   f32x4_t oa, ob;
@@ -122,6 +125,8 @@ __global__ __launch_bounds__(256) void gated_gelu_kernel(const T* __restrict__ Y
 }
 
 }  // namespace
+
+KALM_DBG_TAKE_DEFINE(dbg_take_layer)
 
 namespace kalm {
 

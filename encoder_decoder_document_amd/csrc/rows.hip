@@ -46,6 +46,7 @@ __global__ __launch_bounds__(1024) void pair_layout_kernel(const int32_t* __rest
         const int64_t p = (int64_t)q * nD + dd;
         const int64_t r0 = (int64_t)nD * start + (int64_t)dd * len;
         const bool ok = r0 + len <= LIM;
+        if (!ok) KALM_DBG(KALM_DBG_LAYOUT);
         cu_q[p] = ok ? (int32_t)r0 : -1;
         doc_of_pair[p] = dd;
         final_row[p] = ok ? (int32_t)(r0 + len - 1) : -1;
@@ -99,6 +100,7 @@ __global__ __launch_bounds__(256) void yesno_kernel(const void* __restrict__ h, 
   sy = wave_sum(sy);
   sn = wave_sum(sn);
   if (!ok) sy = sn = __builtin_nanf("");
+  if (!ok && lane == 0) KALM_DBG(KALM_DBG_FINAL_ROW);
   if (lane == 0) {
     const float m = sy - sn;
     const float e = expf(-fabsf(m));  // never overflows
@@ -120,6 +122,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const float* __restric
   if (m >= M) return;
   const int64_t s = idx[m];
   const bool ok = s >= 0 && s < n_src;
+  if (!ok && lane == 0) KALM_DBG(KALM_DBG_GATHER);
   const float qnan = __builtin_nanf("");
   for (int h = lane * 4; h < H; h += 256) {
     f32x4_t v = ok ? *(const f32x4_t*)(src + s * H + h) : f32x4_t{qnan, qnan, qnan, qnan};
@@ -168,6 +171,8 @@ __global__ __launch_bounds__(256) void rank_topn_kernel(const float* __restrict_
 }
 
 }  // namespace
+
+KALM_DBG_TAKE_DEFINE(dbg_take_rows)
 
 namespace kalm {
 

@@ -4,11 +4,14 @@ Every function has the name of the C entry point it wraps, takes torch tensors
 that already live on the GPU, passes their device pointers and the current
 HIP stream, and raises ``KalmError`` on a non-OK status.  No computation of
 the hot path happens here; PyTorch only supplies device memory and streams.
-The library is loaded from the package directory; when it is missing (or no
-GPU is usable) the calls fail loudly -- there is no CPU fallback.
+The library is loaded from the package directory (libkalm.so, or the debug
+build libkalm_debug.so when the environment variable KALM_LIBRARY is "debug";
+any other value is taken as a path); when it is missing (or no GPU is usable)
+the calls fail loudly -- there is no CPU fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -16,10 +19,14 @@ from typing import Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkalm.so")
+_PKG = os.path.dirname(os.path.abspath(__file__))
+RELEASE_LIB_PATH = os.path.join(_PKG, "libkalm.so")
+DEBUG_LIB_PATH = os.path.join(_PKG, "libkalm_debug.so")
+_env_lib = os.environ.get("KALM_LIBRARY", "")
+_LIB_PATH = DEBUG_LIB_PATH if _env_lib == "debug" else (_env_lib or RELEASE_LIB_PATH)
 _lib = None
 
-KALM_OK, KALM_ERR_INVALID_ARG, KALM_ERR_UNSUPPORTED, KALM_ERR_NO_DEVICE, KALM_ERR_LAUNCH = range(5)
+KALM_OK, KALM_ERR_INVALID_ARG, KALM_ERR_UNSUPPORTED, KALM_ERR_NO_DEVICE, KALM_ERR_LAUNCH, KALM_ERR_BOUNDS = range(6)
 KALM_F32, KALM_BF16 = 0, 1
 
 _c_p = ctypes.c_void_p
@@ -30,6 +37,7 @@ _f32 = ctypes.c_float
 _SIGS = {
     "kalm_version": (_i32, []),
     "kalm_last_error": (ctypes.c_char_p, []),
+    "kalm_debug_build": (_i32, []),
     "kalm_device_check": (_i32, []),
     "kalm_pair_layout": (_i32, [_c_p, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _i64, _c_p, _c_p, _c_p]),
     "kalm_chunk_pool": (_i32, [_c_p, _c_p, _i32, _i32, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p]),
@@ -82,7 +90,7 @@ def load(path: Optional[str] = None):
         return _lib
     p = path or _LIB_PATH
     if not os.path.exists(p):
-        raise FileNotFoundError(f"libkalm.so not built at {p}; run __graft_entry__.build() first")
+        raise FileNotFoundError(f"{os.path.basename(p)} not built at {p}; run __graft_entry__.build() first")
     lib = ctypes.CDLL(p)
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)
@@ -91,6 +99,23 @@ def load(path: Optional[str] = None):
     if path is None:
         _lib = lib
     return lib
+
+
+@contextlib.contextmanager
+def using(path: str):
+    """Route every call made inside the block through the library at `path`
+    (for example DEBUG_LIB_PATH), then restore the previous one."""
+    global _lib, _LIB_PATH
+    prev, prev_path = load(), _LIB_PATH
+    _lib, _LIB_PATH = load(path), path
+    try:
+        yield _lib
+    finally:
+        _lib, _LIB_PATH = prev, prev_path
+
+
+def debug_build() -> bool:
+    return bool(load().kalm_debug_build())
 
 
 def _check(fn: str, status: int):

@@ -50,7 +50,8 @@ typedef enum {
   KALM_ERR_INVALID_ARG = 1,
   KALM_ERR_UNSUPPORTED = 2,
   KALM_ERR_NO_DEVICE = 3,
-  KALM_ERR_LAUNCH = 4
+  KALM_ERR_LAUNCH = 4,
+  KALM_ERR_BOUNDS = 5 /* debug build only: a kernel's index guard fired (see kalm_debug_build) */
 } kalm_status;
 
 typedef enum { KALM_F32 = 0, KALM_BF16 = 1 } kalm_dtype;
@@ -62,6 +63,21 @@ int32_t kalm_version(void);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* kalm_last_error(void);
+
+/* 1 in the debug build of the library (libkalm_debug.so, compiled with
+ * -DKALM_DEBUG), 0 in the release build (libkalm.so).  Both export the same
+ * entry points and run the same kernels.  Every kernel guards its
+ * data-dependent indexes in both builds: a pair whose rows fall outside the
+ * given row counts is skipped, a passage index outside [0, D), a residual
+ * source row, gathered row or final row outside its array gives NaN outputs, a
+ * RoPE row outside X is left alone, and a pair layout past INT32_MAX gives -1
+ * offsets.  In the debug build each guard that fires is also recorded, and
+ * every entry point synchronises its stream after its launches and returns
+ * KALM_ERR_BOUNDS (with kalm_last_error naming the guard) instead of KALM_OK;
+ * a kernel fault is reported as KALM_ERR_LAUNCH against the call that ran it.
+ * Because it synchronises, the debug build cannot be captured into a HIP graph,
+ * and concurrent calls on one device share its guard record. */
+int32_t kalm_debug_build(void);
 
 /* KALM_OK when a gfx950 device is visible, KALM_ERR_NO_DEVICE otherwise. */
 kalm_status kalm_device_check(void);

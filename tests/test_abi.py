@@ -14,6 +14,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kalm.h")
 LIB = os.path.join(ROOT, "encoder_decoder_document_amd", "libkalm.so")
+DEBUG_LIB = os.path.join(ROOT, "encoder_decoder_document_amd", "libkalm_debug.so")
+BOTH = [pytest.param(LIB, id="release"), pytest.param(DEBUG_LIB, id="debug")]
 
 needs_lib = pytest.mark.skipif(not os.path.exists(LIB), reason="libkalm.so not built (run __graft_entry__.build())")
 
@@ -84,10 +86,22 @@ def test_boundary_parameter_lists(name):
 
 
 @needs_lib
-def test_library_exports_every_declared_symbol():
-    lib = ctypes.CDLL(LIB)
+@pytest.mark.parametrize("path", BOTH)
+def test_library_exports_every_declared_symbol(path):
+    lib = ctypes.CDLL(path)
     missing = [s for s in declared_symbols() if not hasattr(lib, s)]
     assert not missing, f"not exported: {missing}"
+
+
+@needs_lib
+@pytest.mark.parametrize("path,flag", [(LIB, 0), (DEBUG_LIB, 1)])
+def test_debug_build_reports_itself(path, flag):
+    # the two builds share every entry point; only the debug one records guards
+    lib = ctypes.CDLL(path)
+    lib.kalm_debug_build.restype = ctypes.c_int32
+    lib.kalm_version.restype = ctypes.c_int32
+    assert lib.kalm_debug_build() == flag
+    assert lib.kalm_version() == 400
 
 
 @needs_lib
@@ -97,9 +111,10 @@ def test_binding_covers_every_declared_symbol():
 
 
 @needs_lib
-def test_invalid_arguments_rejected_before_launch():
+@pytest.mark.parametrize("path", BOTH)
+def test_invalid_arguments_rejected_before_launch(path):
     from encoder_decoder_document_amd import ops
-    lib = ops.load()
+    lib = ops.load(path)
     assert lib.kalm_version() == 400
     # chunk = 0
     st = lib.kalm_chunk_pool(None, None, 1, 8, 64, 0, ops.KALM_BF16, None, None, None, None)
@@ -182,7 +197,8 @@ def test_invalid_arguments_rejected_before_launch():
 
 
 @needs_lib
-def test_no_device_means_error_not_cpu_fallback():
+@pytest.mark.parametrize("path", BOTH)
+def test_no_device_means_error_not_cpu_fallback(path):
     import subprocess
     import sys
     code = (
@@ -191,7 +207,7 @@ def test_no_device_means_error_not_cpu_fallback():
         "s=lib.kalm_device_check(); print(s, lib.kalm_last_error().decode())"
     )
     env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1")
-    out = subprocess.run([sys.executable, "-c", code, LIB], capture_output=True, text=True, env=env, timeout=120)
+    out = subprocess.run([sys.executable, "-c", code, path], capture_output=True, text=True, env=env, timeout=120)
     status = int(out.stdout.split()[0])
     assert status == 3, out.stdout + out.stderr   # KALM_ERR_NO_DEVICE
     assert "no HIP device" in out.stdout or "gfx950" in out.stdout
