@@ -48,6 +48,9 @@ enum Epi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_ACC = 2 };
 #ifndef GEMM_PERSIST
 #define GEMM_PERSIST 1
 #endif
+#ifndef GEMM_PKREV
+#define GEMM_PKREV 1
+#endif
 #ifndef GEMM_KREV
 #define GEMM_KREV 1
 #endif
@@ -463,7 +466,12 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_persistent(
   if (vb >= total) return;
   int gk = 0;  // k-tiles consumed by this workgroup (ring position)
   for (int kt = 0; kt < STAGES - 1 && kt < nk; ++kt) issue(tile_of(vb), kt, kt % STAGES);
-  for (; vb < total; vb += grid) {
+  // k order: odd rounds walk k downwards, so a round starts on the weight
+  // k-tiles the previous round used last (still in its XCD's L2)
+  for (int rnd = 0; vb < total; vb += grid, ++rnd) {
+    const bool rev = GEMM_PKREV && (rnd & 1);
+    const bool rev_next = GEMM_PKREV && !(rnd & 1);
+    auto kix = [&](int kt) { return rev ? nk - 1 - kt : kt; };
     const int t = tile_of(vb);
     const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
     const int vb_next = vb + grid;
@@ -481,13 +489,13 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_persistent(
       wait_dma_ktile<CPS>(0);
       __syncthreads();  // k-tile visible to all waves; the other slot is free
       bf16_t* cur = smem + (gk % STAGES) * STAGE_ELEMS;
-      if (k_tail && kt == nk - 1) {
-        zero_k_tail<BM, BK>(cur, kt * BK, K, tid, NT);
-        zero_k_tail<BN, BK>(cur + BM * BK, kt * BK, K, tid, NT);
+      if (k_tail && kix(kt) == nk - 1) {
+        zero_k_tail<BM, BK>(cur, kix(kt) * BK, K, tid, NT);
+        zero_k_tail<BN, BK>(cur + BM * BK, kix(kt) * BK, K, tid, NT);
         __syncthreads();
       }
-      if (kt + 1 < nk) issue(t, kt + 1, (gk + 1) % STAGES);
-      else if (has_next) issue(tile_of(vb_next), 0, (gk + 1) % STAGES);
+      if (kt + 1 < nk) issue(t, kix(kt + 1), (gk + 1) % STAGES);
+      else if (has_next) issue(tile_of(vb_next), rev_next ? nk - 1 : 0, (gk + 1) % STAGES);
       const bf16_t* a = cur;
       const bf16_t* bb = cur + BM * BK;
       // fragments of k-step s + 1 are read from LDS while the MFMAs of k-step s run
