@@ -194,20 +194,25 @@ __global__ __launch_bounds__(NW * 64, RT == 1 ? 2 : 1) void merged_attn_bf16_ker
   // ... (pair p = q D + passage in the layout of kalm_pair_layout), so one
   // passage's cross K/V stays in L2 across the queries -- and each XCD (block
   // b runs on XCD b % 8) walks a contiguous range.
-  const int64_t per_pair = (int64_t)nkv * HG * nqb;
-  const int64_t total = (int64_t)P * per_pair;
-  const int64_t b = blockIdx.x;
-  const int64_t xper = total / 8;
-  const int64_t t = (b < xper * 8) ? (b % 8) * xper + b / 8 : b;
-  const int64_t pi = t / per_pair;  // pair in walk order
+  // (32-bit unsigned arithmetic: the host keeps the number of work items
+  // below 2^31, and 64-bit divisions by run-time values cost the scalar unit
+  // hundreds of instructions)
+  const uint32_t per_pair = (uint32_t)nkv * (uint32_t)HG * (uint32_t)nqb;
+  const uint32_t total = (uint32_t)P * per_pair;
+  const uint32_t b = blockIdx.x;
+  const uint32_t xper = total / 8;
+  const uint32_t t = (b < xper * 8) ? (b % 8) * xper + b / 8 : b;
+  const uint32_t pi = t / per_pair;  // pair in walk order
   int p = (int)pi;
   if (D > 0 && P % D == 0) {
-    const int64_t nQ = P / D;
-    p = (int)((pi % nQ) * D + pi / nQ);
+    const uint32_t nQ = (uint32_t)P / (uint32_t)D;
+    const uint32_t q = pi % nQ;
+    p = (int)(q * (uint32_t)D + (pi - q) / nQ);
   }
-  const int64_t rem = t % per_pair;
-  const int qb = (int)(rem % nqb);
-  const int hgi = (int)(rem / nqb);
+  const uint32_t rem = t - pi * per_pair;
+  const uint32_t hgu = rem / (uint32_t)nqb;
+  const int qb = (int)(rem - hgu * (uint32_t)nqb);
+  const int hgi = (int)hgu;
   const int kvh = hgi / HG, hg = hgi % HG;
 
   const PairRows pr = pair_rows(cu_q, p, D, MODE, q_rows, kv_rows, o_rows);

@@ -295,6 +295,11 @@ static kalm_status merged_attn_impl(const char* fn, const void* Q, int64_t q_ld,
     KALM_REQUIRE(G == 1 || G == 2 || G % 4 == 0, KALM_ERR_UNSUPPORTED,
                  "%s: query heads per KV head must be 1, 2 or a multiple of 4 (got %d)", fn, G);
     KALM_REQUIRE(Cmax <= 4096, KALM_ERR_UNSUPPORTED, "%s: bf16 path supports Cmax <= 4096 (got %d)", fn, Cmax);
+    // one workgroup per (pair, KV head, head group, block of >= 32 rows): at
+    // most P * nq * ceil(rows / 32) of them, which must stay below 2^31
+    const int64_t rows_per_pair = (row_mode == 1 || row_mode == 3) ? 1 : max_lq;
+    KALM_REQUIRE((int64_t)P * nq * ((rows_per_pair + 31) / 32) < (1LL << 31), KALM_ERR_UNSUPPORTED,
+                 "%s: too many attention work items (P=%d, nq=%d, max_lq=%d)", fn, P, nq, max_lq);
     KALM_REQUIRE((part == 2 || (int64_t)max_lq * kv_ld * 2 < (1LL << 31)) &&
                      (part == 1 || (int64_t)Cmax * c_ld * 2 < (1LL << 31)),
                  KALM_ERR_UNSUPPORTED, "%s: per-pair K block exceeds 2 GiB", fn);
