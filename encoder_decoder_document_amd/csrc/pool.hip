@@ -7,7 +7,8 @@
 // ballot over the token mask, each lane streams 16-byte vectors of the chunk's
 // valid token rows (masked tokens are never loaded, so NaN padding cannot
 // leak), sums them in fp32, divides once by the valid count (IEEE division) and
-// rounds once to the storage type.  The chunk-0 wave of each doc also counts
+// rounds once to the storage type.  Non-temporal loads and stores: every token
+// row is read once and every pooled row written once.  The chunk-0 wave of each doc also counts
 // the doc's valid chunks, so no atomics and no second pass are needed.
 #include "kalm_common.h"
 
@@ -99,31 +100,54 @@ __global__ __launch_bounds__(256) void chunk_pool_kernel(const uint8_t* __restri
   const uint8_t* xrow = x + ((int64_t)d * T + t0) * row_bytes;
   uint8_t* orow = pooled + id * row_bytes;
   const float fcnt = (float)cnt;
-  for (int h = lane * V::N; h < H; h += 64 * V::N) {
-    float acc[V::N];
+  // The token rows are read once: non-temporal loads and stores keep them
+  // from displacing reused lines in L2 (about 15% faster at 100 x 1024 x 2560).
+  if constexpr (CH > 0) {
+    // U 16-byte vectors of the row per lane per step, and every token load of
+    // a step issued before any is summed (U = 5 covers a 2560-wide row)
+    constexpr int U = 5;
+    for (int h0 = lane * V::N; h0 < H; h0 += U * 64 * V::N) {
+      u32x4_t r[U][CH];
 #pragma unroll
-    for (int i = 0; i < V::N; ++i) acc[i] = 0.f;
-    if (CH > 0) {
-      u32x4_t r[CH > 0 ? CH : 1];
+      for (int u = 0; u < U; ++u) {
+        const int h = h0 + u * 64 * V::N;
 #pragma unroll
-      for (int j = 0; j < (CH > 0 ? CH : 1); ++j)
-        if ((bits >> j) & 1) r[j] = *(const u32x4_t*)(xrow + j * row_bytes + (int64_t)h * ESZ);
+        for (int j = 0; j < CH; ++j)
+          if (h < H && ((bits >> j) & 1))
+            r[u][j] = __builtin_nontemporal_load((const u32x4_t*)(xrow + j * row_bytes + (int64_t)h * ESZ));
+      }
 #pragma unroll
-      for (int j = 0; j < (CH > 0 ? CH : 1); ++j)
-        if ((bits >> j) & 1) V::add(acc, r[j]);
-    } else {
+      for (int u = 0; u < U; ++u) {
+        const int h = h0 + u * 64 * V::N;
+        if (h >= H) continue;
+        float acc[V::N];
+#pragma unroll
+        for (int i = 0; i < V::N; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+          if ((bits >> j) & 1) V::add(acc, r[u][j]);
+        float out[V::N];
+#pragma unroll
+        for (int i = 0; i < V::N; ++i) out[i] = cnt > 0 ? acc[i] / fcnt : 0.f;
+        __builtin_nontemporal_store(V::pack(out), (u32x4_t*)(orow + (int64_t)h * ESZ));
+      }
+    }
+  } else {
+    for (int h = lane * V::N; h < H; h += 64 * V::N) {
+      float acc[V::N];
+#pragma unroll
+      for (int i = 0; i < V::N; ++i) acc[i] = 0.f;
       uint64_t b = bits;
       while (b) {
         const int j = __builtin_ctzll(b);
         b &= b - 1;
-        const u32x4_t r = *(const u32x4_t*)(xrow + j * row_bytes + (int64_t)h * ESZ);
-        V::add(acc, r);
+        V::add(acc, __builtin_nontemporal_load((const u32x4_t*)(xrow + j * row_bytes + (int64_t)h * ESZ)));
       }
-    }
-    float out[V::N];
+      float out[V::N];
 #pragma unroll
-    for (int i = 0; i < V::N; ++i) out[i] = cnt > 0 ? acc[i] / fcnt : 0.f;
-    *(u32x4_t*)(orow + (int64_t)h * ESZ) = V::pack(out);
+      for (int i = 0; i < V::N; ++i) out[i] = cnt > 0 ? acc[i] / fcnt : 0.f;
+      __builtin_nontemporal_store(V::pack(out), (u32x4_t*)(orow + (int64_t)h * ESZ));
+    }
   }
 }
 
