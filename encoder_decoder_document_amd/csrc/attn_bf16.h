@@ -40,16 +40,23 @@ namespace {
 constexpr int HD = 256;          // head dim of the bf16 path
 constexpr int BKV = 32;          // keys per tile
 constexpr float LAZY = 8.0f;     // lazy-rescale threshold, log2 units
-// Streaming (non-temporal) hints for the Q loads and O stores: measured
-// slower here (2.50 vs 2.20 ms at the Small shape), so off by default.
-#ifndef ATTN_STREAM
-#define ATTN_STREAM 0
+// Streaming (non-temporal) hints for the Q loads and for the O stores, off by
+// default: at the Small shape the hinted Q loads took the kernel from 1.66 to
+// 1.98 ms, and the hinted O stores changed nothing measurable.
+#ifndef ATTN_STREAM_Q
+#define ATTN_STREAM_Q 0
 #endif
-#if ATTN_STREAM
+#ifndef ATTN_STREAM_O
+#define ATTN_STREAM_O 0
+#endif
+#if ATTN_STREAM_Q
 #define ATTN_LD_Q(p) __builtin_nontemporal_load(p)
-#define ATTN_ST_O(v, p) __builtin_nontemporal_store(v, p)
 #else
 #define ATTN_LD_Q(p) (*(p))
+#endif
+#if ATTN_STREAM_O
+#define ATTN_ST_O(v, p) __builtin_nontemporal_store(v, p)
+#else
 #define ATTN_ST_O(v, p) (*(p) = (v))
 #endif
 #ifndef ATTN_WAVES
