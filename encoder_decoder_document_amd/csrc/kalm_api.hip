@@ -151,6 +151,8 @@ kalm_status kalm_chunk_pool(const void* x, const uint8_t* token_mask, int32_t D,
   KALM_REQUIRE(D == 0 || (x && token_mask && pooled && chunk_mask && n_chunks), KALM_ERR_INVALID_ARG,
                "kalm_chunk_pool: null pointer");
   KALM_REQUIRE(ALIGNED16(x) && ALIGNED16(pooled), KALM_ERR_INVALID_ARG, "kalm_chunk_pool: x/pooled not 16-byte aligned");
+  KALM_REQUIRE((int64_t)D * ((T + chunk - 1) / chunk) < (1LL << 26), KALM_ERR_UNSUPPORTED,
+               "kalm_chunk_pool: D * ceil(T / chunk) must stay below 2^26 pooled rows");
   KALM_DEVICE_OR_RETURN();
   if (D == 0) return KALM_OK;
   const int Cmax = (T + chunk - 1) / chunk;

@@ -65,9 +65,11 @@ __global__ __launch_bounds__(256) void chunk_pool_kernel(const uint8_t* __restri
   using V = PoolVec<BF16>;
   constexpr int ESZ = BF16 ? 2 : 4;
   const int lane = threadIdx.x & 63;
-  const int64_t id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (id >= (int64_t)D * Cmax) return;
-  const int d = (int)(id / Cmax), c = (int)(id % Cmax);
+  // 32-bit row index (the host keeps D * Cmax below 2^26): a 64-bit division
+  // by the run-time Cmax costs the scalar unit hundreds of instructions
+  const uint32_t id = blockIdx.x * 4u + (threadIdx.x >> 6);
+  if (id >= (uint32_t)D * (uint32_t)Cmax) return;
+  const int d = (int)(id / (uint32_t)Cmax), c = (int)(id - (uint32_t)d * (uint32_t)Cmax);
   const int csz = CH > 0 ? CH : chunk;
   const uint8_t* m = mask + (int64_t)d * T;
   const int t0 = c * csz;
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(256) void chunk_pool_kernel(const uint8_t* __restri
 
   const int64_t row_bytes = (int64_t)H * ESZ;
   const uint8_t* xrow = x + ((int64_t)d * T + t0) * row_bytes;
-  uint8_t* orow = pooled + id * row_bytes;
+  uint8_t* orow = pooled + (int64_t)id * row_bytes;
   const float fcnt = (float)cnt;
   // The token rows are read once: non-temporal loads and stores keep them
   // from displacing reused lines in L2 (about 15% faster at 100 x 1024 x 2560).
