@@ -194,6 +194,13 @@ def test_invalid_arguments_rejected_before_launch(path):
     assert st == ops.KALM_ERR_UNSUPPORTED
     st = lib.kalm_linear_gated_gelu(16, 16, None, 10, 64, 128, 16, None)
     assert st == ops.KALM_ERR_INVALID_ARG and b"null" in lib.kalm_last_error()
+    # launch-size limits (fake, never dereferenced pointers): 2^26 or more pooled rows;
+    # 2^31 or more attention work items
+    st = lib.kalm_chunk_pool(16, 32, 1 << 20, 1024, 64, 4, ops.KALM_BF16, 48, 64, 80, None)
+    assert st == ops.KALM_ERR_UNSUPPORTED and b"2^26" in lib.kalm_last_error()
+    st = lib.kalm_merged_attn(16, 1024, 32, 48, 256, 64, 1 << 28, 1 << 30, 512, 80, 96, 256, 112, 128, 1, 4,
+                              4, 1, 256, 0.0625, ops.KALM_BF16, 144, 1024, None, None)
+    assert st == ops.KALM_ERR_UNSUPPORTED and b"work items" in lib.kalm_last_error()
 
 
 @needs_lib
