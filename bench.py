@@ -46,9 +46,9 @@ FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 MEASURED_TRAFFIC = {
     # profiles/hbm_traffic_small_stack26_bf16.md (the QKV figures are the mean over the full-height
     # launches only; the same kernel symbol also runs the last layer's K/V projection)
-    "qkv_linear": {"src": "804f6ba3f35f191f3e4cdcd80bcfcc696014d095d185e3d564896cc13e9d18f4", "fetch_kib": 1892805.4, "write_kib": 2688304.8},
-    "o_linear": {"src": "804f6ba3f35f191f3e4cdcd80bcfcc696014d095d185e3d564896cc13e9d18f4", "fetch_kib": 3124805.8, "write_kib": 6529430.8},
-    "merged_attn": {"src": "ab1f02d79fefe8d059345050f2ac75701a7ebfcde0658b4aa202d55dfd40e86a", "fetch_kib": 1348975.0, "write_kib": 1792200.0},
+    "qkv_linear": {"src": "804f6ba3f35f191f3e4cdcd80bcfcc696014d095d185e3d564896cc13e9d18f4", "fetch_kib": 1883966.6, "write_kib": 2688330.1},
+    "o_linear": {"src": "804f6ba3f35f191f3e4cdcd80bcfcc696014d095d185e3d564896cc13e9d18f4", "fetch_kib": 3123938.4, "write_kib": 6529536.5},
+    "merged_attn": {"src": "7789502f81c8b83a4def65d09a3941259f87406efa97af929c8fe8edf79695fd", "fetch_kib": 1348961.0, "write_kib": 1792200.0},
 }
 # the source files each kernel is built from (headers included); their joint
 # sha256 keys the stored counter values
