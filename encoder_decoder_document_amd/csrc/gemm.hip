@@ -45,6 +45,14 @@ enum Epi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_ACC = 2 };
 #ifndef GEMM_PF_Y
 #define GEMM_PF_Y true
 #endif
+// Activation slots of the residual update's ring (beside 2 weight slots):
+// 3 puts each activation k-tile in flight one k-tile earlier than its weight
+// k-tile -- the activations come from HBM, the weights from L2 -- and the
+// ring (80 KB) still lets two workgroups share a CU.  Measured at the Small
+// shape (A/B on one box): 3.11-3.13 ms against 3.20 ms per launch with 2.
+#ifndef GEMM_RES_ASTG
+#define GEMM_RES_ASTG 3
+#endif
 #ifndef GEMM_PERSIST
 #define GEMM_PERSIST 1
 #endif
@@ -135,11 +143,13 @@ __device__ __forceinline__ void zero_k_tail(bf16_t* tile, int k0, int K, int tid
 // WM x WN waves split the block tile BM x BN; k advances BK per stage and
 // STAGES k-tiles live in the LDS ring (STAGES - 1 in flight while one feeds
 // the MFMAs); OCC = waves per SIMD it is built for (bounds the registers).
+// ASTG = 3 (with STAGES = 2) gives the activation operand a third slot of its
+// own: its copies are issued one k-tile ahead of the weights' copies.
 // PF_Y (residual update only): the fp32 values the epilogue adds to are loaded
 // into registers while the last k-tile is copied and multiplied, so their
 // memory latency is hidden instead of being paid after the k-loop.
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int OCC, bool PF_Y = false,
-          bool STREAM_X = GEMM_STREAM_X, bool RES = false>
+          bool STREAM_X = GEMM_STREAM_X, bool RES = false, int ASTG = STAGES>
 __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, int M, int K, int N,
     void* __restrict__ Y, int epi, bf16_t* __restrict__ Ybf, const uint8_t* __restrict__ rmask,
@@ -151,8 +161,14 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int STAGE_ELEMS = (BM + BN) * BK;
+  // SPLIT: ASTG activation slots beside STAGES weight slots; the activation
+  // copies run one k-tile further ahead than the weight copies
+  constexpr bool SPLIT = ASTG != STAGES;
+  static_assert(!SPLIT || (STAGES == 2 && ASTG == 3), "split ring: 3 activation and 2 weight slots");
+  constexpr int RING_ELEMS = SPLIT ? ASTG * BM * BK + STAGES * BN * BK : STAGES * STAGE_ELEMS;
+  constexpr int PA = DmaPlan<BM, NW, BK, true>::PER;  // activation copies per thread per k-tile
 
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGES * STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[RING_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
@@ -171,10 +187,16 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
   // skip tiles whose rows are all masked out (padded chunks of the cross projection)
   bool tile_live = true;
   if (rmask) {
-    int any = 0;
+    // block-wide OR through the (not yet used) ring, so the kernel needs no
+    // LDS beyond the ring
+    int* flag = (int*)smem;
+    if (tid == 0) *flag = 0;
+    __syncthreads();
     for (int rr = tid; rr < BM; rr += NT)
-      if (m0 + rr < M && rmask[m0 + rr]) any = 1;
-    tile_live = __syncthreads_or(any) != 0;
+      if (m0 + rr < M && rmask[m0 + rr]) *flag = 1;
+    __syncthreads();
+    tile_live = *flag != 0;
+    __syncthreads();  // read before the first copies overwrite it
   }
 
   f32x16_t acc[FN][FM];
@@ -201,6 +223,14 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
     const uint32_t b = lds_base + (uint32_t)((i % STAGES) * STAGE_ELEMS * 2);
     planA.issue(b, kidx(i) * BK, K);
     planB.issue(b + BM * BK * 2, kidx(i) * BK, K);
+  };
+  auto a_slot = [&](int i) { return SPLIT ? smem + (i % ASTG) * (BM * BK) : smem + (i % STAGES) * STAGE_ELEMS; };
+  auto b_slot = [&](int i) {
+    return SPLIT ? smem + ASTG * (BM * BK) + (i % STAGES) * (BN * BK) : smem + (i % STAGES) * STAGE_ELEMS + BM * BK;
+  };
+  auto issue_a = [&](int i) { planA.issue(lds_base + (uint32_t)((i % ASTG) * BM * BK * 2), kidx(i) * BK, K); };
+  auto issue_b = [&](int i) {
+    planB.issue(lds_base + (uint32_t)((ASTG * BM * BK + (i % STAGES) * BN * BK) * 2), kidx(i) * BK, K);
   };
 
   const int r = lane & 31, g = lane >> 5;
@@ -265,19 +295,32 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
       }
     }
   };
-  for (int kt = 0; kt < STAGES - 1 && kt < nk; ++kt) issue(kt);
+  if constexpr (SPLIT) {
+    // copy order: A0 B0 A1, then per k-tile kt: B(kt+1) A(kt+2) -- so when
+    // k-tile kt starts, only A(kt+1) (issued last) may still be in flight
+    if (nk > 0) {
+      issue_a(0);
+      issue_b(0);
+    }
+    if (nk > 1) issue_a(1);
+  } else {
+    for (int kt = 0; kt < STAGES - 1 && kt < nk; ++kt) issue(kt);
+  }
   for (int kt = 0; kt < nk; ++kt) {
     // this thread's copies of k-tile kt are done once at most those of the
     // (up to two) later k-tiles already issued are outstanding -- and, at the
     // last k-tile with PF_Y, the NY loads of the fp32 stream issued after them
     if (PF_Y && kt == nk - GEMM_PF_DIST && kt >= 1 && STAGES == 2)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NY) : "memory");  // the copy is older than the NY loads
-    else wait_dma_ktile<CPS>(min(nk - 1 - kt, STAGES - 2));
+    else if (SPLIT && kt + 1 < nk)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PA) : "memory");  // A(kt + 1) may stay in flight
+    else wait_dma_ktile<CPS>(SPLIT ? 0 : min(nk - 1 - kt, STAGES - 2));
     __syncthreads();  // k-tile kt visible to all waves; slot of k-tile kt-1 free
-    bf16_t* cur = smem + (kt % STAGES) * STAGE_ELEMS;
+    bf16_t* cur = a_slot(kt);
+    bf16_t* curb = b_slot(kt);
     if (k_tail && kidx(kt) == nk - 1) {
       zero_k_tail<BM, BK>(cur, kidx(kt) * BK, K, tid, NT);
-      zero_k_tail<BN, BK>(cur + BM * BK, kidx(kt) * BK, K, tid, NT);
+      zero_k_tail<BN, BK>(curb, kidx(kt) * BK, K, tid, NT);
       __syncthreads();
     }
     if constexpr (PF_Y && RES) {
@@ -288,10 +331,15 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
         for (int i = 0; i < NY; ++i) asm volatile("" ::"v"(srow[i]));
       }
     }
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    if constexpr (SPLIT) {
+      if (kt + 1 < nk) issue_b(kt + 1);
+      if (kt + 2 < nk) issue_a(kt + 2);
+    } else {
+      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    }
     if (PF_Y && kt == max(nk - 1 - GEMM_PF_DIST, 0)) load_yold();
     const bf16_t* a = cur;
-    const bf16_t* bb = cur + BM * BK;
+    const bf16_t* bb = curb;
     // fragments of k-step s + 1 are read from LDS while the MFMAs of k-step s run
     constexpr int KS = BK / 16;
     bf16x8_t xf[KS][FM], wf[KS][FN];
@@ -340,7 +388,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_bf16_kernel(
   // pieces per instruction.
   constexpr int EP_LD = WTN + 4;  // fp32 per parked row
   // waves take turns when all of their parking areas do not fit the ring at once
-  constexpr int EP_ROUNDS = (NW * 32 * EP_LD * 4 + STAGES * STAGE_ELEMS * 2 - 1) / (STAGES * STAGE_ELEMS * 2);
+  constexpr int EP_ROUNDS = (NW * 32 * EP_LD * 4 + RING_ELEMS * 2 - 1) / (RING_ELEMS * 2);
   static_assert(EP_ROUNDS <= 2 && NW % EP_ROUNDS == 0, "epilogue staging fits the ring in two rounds");
   __syncthreads();  // every wave is done reading the ring
   float* park = (float*)smem + (wave / EP_ROUNDS) * (32 * EP_LD);
@@ -673,10 +721,10 @@ void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, v
     // two workgroups per CU, so one's epilogue traffic overlaps the other's k-loop
     const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
     if (Rsrc)
-      hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 64, 2, 4, GEMM_PF_Y, GEMM_STREAM_X, true>), dim3(tiles),
+      hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 64, 2, 4, GEMM_PF_Y, GEMM_STREAM_X, true, GEMM_RES_ASTG>), dim3(tiles),
                          dim3(512), 0, s, X, W, M, K, N, Y, epi, Y_bf16, rmask, Rsrc, Rrow, Rrows);
     else
-      hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 64, 2, 4, GEMM_PF_Y>), dim3(tiles), dim3(512), 0, s, X, W,
+      hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 64, 2, 4, GEMM_PF_Y, GEMM_STREAM_X, false, GEMM_RES_ASTG>), dim3(tiles), dim3(512), 0, s, X, W,
                          M, K, N, Y, epi, Y_bf16, rmask, Rsrc, Rrow, Rrows);
   } else if (big_tiles >= 512 && rmask) {
     // rows with a zero mask byte (padded chunks of the cross projection) are
