@@ -197,7 +197,10 @@ def test_cross_kv_layers_parity(D, C, H, kv, L, bf16):
                                         (22093, 1152, 1536, "bf16"), (22093, 1024, 1152, "acc"), (40003, 1024, 1152, "acc"),
                                         (88001, 1000, 1536, "bf16"),
                                         # the residual update's big-tile path with a ragged last column tile
-                                        (40003, 1024, 1160, "acc")])
+                                        (40003, 1024, 1160, "acc"),
+                                        # its split ring (activation copies a k-tile ahead): a K tail, and
+                                        # k-loops of one and of two k-tiles
+                                        (22093, 1000, 1536, "acc"), (22093, 64, 1536, "acc"), (22093, 128, 1536, "acc")])
 def test_linear_parity(M, K, N, mode):
     _announce(f"linear M={M} K={K} N={N} mode={mode}")
     bf = mode in ("bf16", "acc", "f32out")
@@ -228,7 +231,9 @@ def test_linear_parity(M, K, N, mode):
 
 @pytest.mark.parametrize("M,K,N,bf,indexed", [(300, 1024, 1152, True, True), (40003, 1024, 1152, True, True),
                                                (40003, 1024, 1160, True, True),
-                                               (22093, 1024, 1152, True, False), (33, 36, 20, False, True)])
+                                               (22093, 1024, 1152, True, False), (33, 36, 20, False, True),
+                                               # the gathered big-tile path with a K tail
+                                               (22093, 1000, 1536, True, True)])
 def test_linear_residual_parity(M, K, N, bf, indexed):
     """Y = R[r_row] + X W^T: the residual update starting from gathered rows
     (big and small tile paths, fp32 path); out-of-range indices give NaN rows."""
