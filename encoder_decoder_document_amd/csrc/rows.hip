@@ -12,7 +12,9 @@
 namespace {
 
 // One block.  Running exclusive prefix over the query lengths, 1024 queries
-// per step; the thread owning query q writes the entries of its D pairs.  The
+// per step; the step's starts and lengths go to LDS and all threads then write
+// the entries of its queries' pairs (pair-major, so consecutive threads write
+// consecutive entries).  The
 // prefix is taken in int64: a pair whose rows would end past INT32_MAX gets
 // cu_q = final_row = h0_final = -1 (and cu_q[P] = -1 when the total overflows),
 // which the attention kernels skip and the readout turns into NaN, so an
@@ -25,6 +27,7 @@ __global__ __launch_bounds__(1024) void pair_layout_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ cu_u) {
   constexpr int64_t LIM = 0x7fffffffLL;
   __shared__ int64_t scan[1024];
+  __shared__ int64_t qstart[1024], qlen[1024];
   __shared__ int64_t carry;
   if (threadIdx.x == 0) carry = 0;
   __syncthreads();
@@ -40,18 +43,25 @@ __global__ __launch_bounds__(1024) void pair_layout_kernel(const int32_t* __rest
       __syncthreads();
     }
     const int64_t start = carry + scan[threadIdx.x] - len;  // exclusive prefix of query rows
-    if (q < nQ) {
-      if (cu_u) cu_u[q] = start + len <= LIM ? (int32_t)start : -1;
-      for (int dd = 0; dd < nD; ++dd) {
-        const int64_t p = (int64_t)q * nD + dd;
-        const int64_t r0 = (int64_t)nD * start + (int64_t)dd * len;
-        const bool ok = r0 + len <= LIM;
-        if (!ok) KALM_DBG(KALM_DBG_LAYOUT);
-        cu_q[p] = ok ? (int32_t)r0 : -1;
-        doc_of_pair[p] = dd;
-        final_row[p] = ok ? (int32_t)(r0 + len - 1) : -1;
-        if (h0_final) h0_final[p] = ok ? (int32_t)(start + len - 1) : -1;
-      }
+    qstart[threadIdx.x] = start;
+    qlen[threadIdx.x] = len;
+    if (q < nQ && cu_u) cu_u[q] = start + len <= LIM ? (int32_t)start : -1;
+    __syncthreads();
+    // the entries of this step's pairs: pair p = q nD + dd, in pair order
+    // (32-bit: the host keeps nQ nD below 2^31)
+    const int nq_step = min(1024, nQ - base);
+    const uint32_t n_ent = (uint32_t)nq_step * (uint32_t)nD;
+    for (uint32_t e = threadIdx.x; e < n_ent; e += 1024) {
+      const int ql = (int)(e / (uint32_t)nD), dd = (int)(e - (uint32_t)ql * (uint32_t)nD);
+      const int64_t st = qstart[ql], ln = qlen[ql];
+      const int64_t p = (int64_t)base * nD + e;
+      const int64_t r0 = (int64_t)nD * st + (int64_t)dd * ln;
+      const bool ok = r0 + ln <= LIM;
+      if (!ok) KALM_DBG(KALM_DBG_LAYOUT);
+      cu_q[p] = ok ? (int32_t)r0 : -1;
+      doc_of_pair[p] = dd;
+      final_row[p] = ok ? (int32_t)(r0 + ln - 1) : -1;
+      if (h0_final) h0_final[p] = ok ? (int32_t)(st + ln - 1) : -1;
     }
     __syncthreads();
     if (threadIdx.x == 1023) carry += scan[1023];
