@@ -27,9 +27,12 @@ def _announce(msg):
 
 
 # ------------------------------------------------------------------ a0 layout
-@pytest.mark.parametrize("lq,D", [([16], 8), ([3, 1, 4, 1, 5], 7), ([64] * 3 + [512, 1, 77], 100)])
+@pytest.mark.parametrize("lq,D", [([16], 8), ([3, 1, 4, 1, 5], 7), ([64] * 3 + [512, 1, 77], 100),
+                                  # more than one 1024-query scan step, and one query with many passages
+                                  pytest.param([int(x) for x in synth.integers(17, 1, 600, 2500)], 3, id="q2500-d3"),
+                                  pytest.param([300], 5000, id="q1-d5000")])
 def test_pair_layout_bit_exact(lq, D):
-    _announce(f"pair_layout lq={lq} D={D}")
+    _announce(f"pair_layout queries={len(lq)} D={D}")
     lq = np.asarray(lq, np.int32)
     rows = int(D * lq.sum())
     got = ops.kalm_pair_layout(to_dev(lq, torch.int32), D, rows=rows)
