@@ -46,9 +46,9 @@ FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 MEASURED_TRAFFIC = {
     # profiles/hbm_traffic_small_stack26_bf16.md (the QKV figures are the mean over the full-height
     # launches only; the same kernel symbol also runs the last layer's K/V projection)
-    "qkv_linear": {"src": "f0eb885edaf442864741495d539ac49e3c7b6ef74f451d78a485952dabb18429", "fetch_kib": 1820361.1, "write_kib": 2688301.7},
-    "o_linear": {"src": "f0eb885edaf442864741495d539ac49e3c7b6ef74f451d78a485952dabb18429", "fetch_kib": 3114758.9, "write_kib": 6544806.7},
-    "merged_attn": {"src": "7789502f81c8b83a4def65d09a3941259f87406efa97af929c8fe8edf79695fd", "fetch_kib": 1348967.2, "write_kib": 1792200.0},
+    "qkv_linear": {"src": "25b4c172737f9f7a78d46b8f8ebd2509231b9bbf8b505cdbf3421072b3dd7c7b", "fetch_kib": 1880075.5, "write_kib": 2688306.2},
+    "o_linear": {"src": "25b4c172737f9f7a78d46b8f8ebd2509231b9bbf8b505cdbf3421072b3dd7c7b", "fetch_kib": 3114048.0, "write_kib": 6544855.2},
+    "merged_attn": {"src": "7789502f81c8b83a4def65d09a3941259f87406efa97af929c8fe8edf79695fd", "fetch_kib": 1348960.8, "write_kib": 1792200.0},
 }
 # the source files each kernel is built from (headers included); their joint
 # sha256 keys the stored counter values

@@ -56,6 +56,10 @@ enum Epi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_ACC = 2 };
 #ifndef GEMM_PERSIST
 #define GEMM_PERSIST 1
 #endif
+// shortest k-loop at which a plain residual update takes the persistent kernel
+#ifndef GEMM_RES_PERSIST_MINK
+#define GEMM_RES_PERSIST_MINK 2048
+#endif
 #ifndef GEMM_PKREV
 #define GEMM_PKREV 1
 #endif
@@ -719,7 +723,13 @@ void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, v
                         const int32_t* Rrow, int64_t Rrows) {
   const int epi = !y_f32 ? EPI_BF16 : (accumulate ? EPI_F32_ACC : EPI_F32);
   const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles >= 512 && epi == EPI_F32_ACC) {
+  // A plain residual update (no gathered rows) with a long k-loop goes to the
+  // persistent 256 x 256 kernel: its tiles need half the operand bytes per
+  // output of the 128 x 128 ones, which outweighs an epilogue it cannot hide
+  // behind a second workgroup.  Measured: at K = 2048, H = 2560 (the Long/wide
+  // stack) 39.7 against 45.6 ms per launch; at K = 1024 (Small) 3.78 against 3.12.
+  const bool res_persist = GEMM_PERSIST && !Rsrc && !rmask && K >= GEMM_RES_PERSIST_MINK;
+  if (big_tiles >= 512 && epi == EPI_F32_ACC && !res_persist) {
     // residual update (reads and writes the fp32 stream): 128 x 128 tiles,
     // two workgroups per CU, so one's epilogue traffic overlaps the other's k-loop
     const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
@@ -736,7 +746,7 @@ void launch_linear_bf16(const bf16_t* X, const bf16_t* W, int M, int K, int N, v
     const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 4, 64, 2, 4>), dim3(tiles), dim3(512), 0, s, X, W, M, K, N, Y,
                        epi, Y_bf16, rmask, Rsrc, Rrow, Rrows);
-  } else if (big_tiles >= 512 && GEMM_PERSIST) {  // never EPI_F32_ACC, never masked rows
+  } else if (big_tiles >= 512 && GEMM_PERSIST) {  // never masked or gathered rows
     // persistent 256 x 256 tiles, one workgroup per CU
     const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
     const int grid = tiles < 256 ? ((tiles + 7) / 8) * 8 : 256;

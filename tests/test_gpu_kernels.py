@@ -203,7 +203,10 @@ def test_cross_kv_layers_parity(D, C, H, kv, L, bf16):
                                         (40003, 1024, 1160, "acc"),
                                         # its split ring (activation copies a k-tile ahead): a K tail, and
                                         # k-loops of one and of two k-tiles
-                                        (22093, 1000, 1536, "acc"), (22093, 64, 1536, "acc"), (22093, 128, 1536, "acc")])
+                                        (22093, 1000, 1536, "acc"), (22093, 64, 1536, "acc"), (22093, 128, 1536, "acc"),
+                                        # a long k-loop: the residual update on the persistent 256 x 256 tiles,
+                                        # ragged in M, and in N
+                                        (22093, 2048, 1536, "acc"), (26200, 2048, 1160, "acc")])
 def test_linear_parity(M, K, N, mode):
     _announce(f"linear M={M} K={K} N={N} mode={mode}")
     bf = mode in ("bf16", "acc", "f32out")
